@@ -1,0 +1,99 @@
+"""Planted mistakes in the oracle must be caught by its pins.
+
+Each case patches one oracle function (on the CPU, inside this process only)
+with a plausible error and checks that the pin written for that step fails.
+"""
+import numpy as np
+import pytest
+
+import oracle
+import oracle.moe_oracle as mo
+import test_oracle_pins as pins
+
+
+def patch(monkeypatch, name, fn):
+    """Replace one oracle function everywhere it can be reached from."""
+    monkeypatch.setattr(mo, name, fn)
+    monkeypatch.setattr(oracle, name, fn)
+
+
+def expect_failure(fn):
+    with pytest.raises(AssertionError):
+        fn()
+
+
+def test_unrenormalised_gates_are_caught(monkeypatch):
+    def bad(logits, idx):
+        l = np.asarray(logits, np.float64)
+        s = np.exp(l - l.max(1, keepdims=True)); s /= s.sum(1, keepdims=True)
+        return np.take_along_axis(s, idx.astype(np.int64), 1)      # missing renormalisation
+    patch(monkeypatch, "renormalised_gates", bad)
+    expect_failure(lambda: pins.test_gates_equal_ratio_form_and_masked_resoftmax_form("tiny_fp32"))
+
+
+def test_wrong_tie_rule_is_caught(monkeypatch):
+    def bad(logits, K):
+        l = np.asarray(logits, np.float32)[:, ::-1]
+        o = np.argsort(-l, axis=1, kind="stable")[:, :K]
+        return (l.shape[1] - 1 - o).astype(np.int32)               # ties to the higher id
+    patch(monkeypatch, "select_top_k", bad)
+    expect_failure(pins.test_top_k_all_ties_take_lowest_ids_and_equal_gates)
+
+
+def test_ascending_selection_is_caught(monkeypatch):
+    def bad(logits, K):
+        return np.argsort(np.asarray(logits, np.float32), axis=1, kind="stable")[:, :K].astype(np.int32)
+    patch(monkeypatch, "select_top_k", bad)
+    expect_failure(pins.test_top_k_is_the_unique_dominating_subset_by_brute_force)
+
+
+def test_dropping_the_first_tokens_instead_of_the_last_is_caught(monkeypatch):
+    orig = mo.dispatch
+
+    def bad(idx, N, C):
+        if C is None:
+            return orig(idx, N, C)
+        rev = orig(np.asarray(idx)[::-1], N, C)                   # keeps the last C tokens
+        T = idx.shape[0]
+        out = dict(rev)
+        out["slot_row"] = rev["slot_row"][::-1].copy()
+        out["row_token"] = (T - 1 - rev["row_token"]).astype(np.int32)
+        return out
+    patch(monkeypatch, "dispatch", bad)
+    expect_failure(lambda: pins.test_dispatch_matches_sort_definition_and_invariants(3))
+
+
+def test_sign_error_in_silu_is_caught(monkeypatch):
+    patch(monkeypatch, "silu", lambda z: z / (1.0 + np.exp(z)))
+    expect_failure(pins.test_expert_ffn_matches_torch_modules)
+
+
+def test_transposed_second_linear_is_caught(monkeypatch):
+    orig = mo.expert_ffn
+
+    def bad(z, w1, b1, w2, b2, return_hidden=False):
+        w2 = np.asarray(w2)
+        if w2.shape[0] == w2.shape[1]:
+            w2 = w2.T
+        return orig(z, w1, b1, w2, b2, return_hidden)
+    patch(monkeypatch, "expert_ffn", bad)
+    wl = pins.W.custom_workload("sq", T=6, d_model=8, n_routed=3, top_k=2, n_shared=0, d_ff=8,
+                                dtype="f32", expert_bias=True)
+    routed, _ = pins.providers(wl)
+    x = wl.x().numpy()
+    import torch
+    w1, b1, w2, b2 = (torch.from_numpy(np.asarray(t, np.float64)) for t in routed(0))
+    ref = torch.nn.functional.linear(torch.nn.functional.silu(
+        torch.nn.functional.linear(torch.from_numpy(x).double(), w1, b1)), w2, b2).numpy()
+    got = mo.expert_ffn(x, *routed(0))
+    assert not np.allclose(got, ref)
+
+
+def test_dropped_shared_experts_are_caught(monkeypatch):
+    orig = mo.layer_forward
+
+    def bad(*a, **k):
+        k["n_shared"] = 0
+        return orig(*a, **k)
+    patch(monkeypatch, "layer_forward", bad)
+    expect_failure(lambda: pins.test_layer_equals_dense_masked_brute_force(pins.SMALL[1]))
