@@ -1,0 +1,221 @@
+/*
+ * moe_mi355x.h — C interface of the sparse top-K routed MoE FFN forward
+ * (renormalised gates, optional always-on shared experts) for MI355X (gfx950).
+ *
+ * Sources, cited by page title and section:
+ *   [TopK]  "Sparse MoE Top-Kルーティング" glossary page (jisaku.com):
+ *           section ルーティングの仕組み (router scores for every expert, keep
+ *           the K best, masked re-softmax gives the gates, gate-weighted sum);
+ *           section 解決策2: エキスパートキャパシティファクター (per-expert token
+ *           limit, overflow tokens dropped / left to the residual).
+ *   [DSMoE] "論文解説: DeepSeekMoE — 細粒度エキスパート分割と共有エキスパートによる
+ *           MoE効率化" (0h-n0.github.io): section 共有エキスパート機構 (output
+ *           equation: sum of shared experts plus gate-weighted routed experts);
+ *           section ルーティングとバランス損失 (gate equation
+ *           g_j = s_j / sum_{k in TopK} s_k, s = softmax(W_r x)); section
+ *           アルゴリズム (layer arguments d_model, n_routed, n_shared, top_k,
+ *           d_ff; router Linear without bias; expert Linear-SiLU-Linear).
+ *   [EP]    "エキスパート並列（Expert Parallelism）" glossary page (jisaku.com):
+ *           section 推論フロー (gate selects experts, tokens are sent to their
+ *           experts, results are sent back); on one GPU that exchange is the
+ *           on-device permutation below.
+ *
+ * Conventions shared by every entry point
+ *   - Every pointer argument of type void*, float*, int32_t* that names a
+ *     tensor is a DEVICE pointer owned by the caller; the library allocates
+ *     nothing and keeps no state between calls.  `cfg` and `w` (the structs)
+ *     are HOST pointers read during the call only.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the default stream).
+ *     Calls only enqueue work on it; none synchronises with the host and none
+ *     copies device data to the host.  Results are ready when the stream is.
+ *   - Tensors are dense and row-major in the shapes given; "act" denotes the
+ *     activation / expert-weight type chosen by cfg->dtype (MOE_F32: float,
+ *     MOE_BF16: bfloat16 bits).  Router weights, router bias, logits and
+ *     gates are always float32.  Every device pointer must be 16-byte aligned.
+ *   - Return value: MOE_OK, or a negative moe_status.  Argument errors are
+ *     detected on the host before anything is enqueued.  Launch failures
+ *     return MOE_ERR_HIP.  Device-side contents (for example an expert index
+ *     outside [0, N) handed to moe_permute) are not validated; behaviour is
+ *     then undefined.  No C++ exception crosses this interface.
+ *   - T == 0 is a successful no-op.
+ *   - Supported sizes: 1 <= top_k <= n_routed <= 1024; n_shared <= 64;
+ *     d_model, d_ff multiples of 64 for MOE_BF16 and of 16 for MOE_F32;
+ *     T * top_k < 2^31.  Others return MOE_ERR_UNSUPPORTED.
+ *
+ * Numerical contract
+ *   - Logits: float32, per (t, e) one fused multiply-add chain over k
+ *     ascending starting at +0, then + router_bias[e] with one rounding.
+ *   - Selection: the K largest logits, key (logit desc, expert id asc); slot
+ *     k of a token holds its k-th best expert.
+ *   - Gates: softmax over the K kept logits (float32), which equals
+ *     s_j / sum_{k in TopK} s_k of [DSMoE] gate equation.
+ *   - Capacity: C = cfg->capacity when >= 0, else ceil(cf * T * K / N)
+ *     evaluated in double as ((cf * T) * K) / N when cf > 0, else no limit.
+ *     An expert keeps its first C tokens in token order; a dropped
+ *     (token, slot) contributes nothing; gates are not renormalised again.
+ *   - Output: y_t = sum_i S_i(x_t) + sum_{k kept} g[t,k] * E_{idx[t,k]}(x_t),
+ *     accumulated in float32, shared experts first, then k ascending; no
+ *     residual term (that add belongs to the caller).
+ *   - Expert E(z) = W2 SiLU(W1 z + b1) + b2; bf16 configurations round the
+ *     hidden activations and the expert outputs to bf16, accumulate in fp32.
+ */
+#ifndef MOE_MI355X_H
+#define MOE_MI355X_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    MOE_OK = 0,
+    MOE_ERR_INVALID_ARG = -1,   /* NULL where required, negative size, K > N ... */
+    MOE_ERR_UNSUPPORTED = -2,   /* sizes outside the supported ranges above      */
+    MOE_ERR_WORKSPACE = -3,     /* workspace missing or smaller than required    */
+    MOE_ERR_HIP = -4            /* a HIP runtime call or kernel launch failed    */
+} moe_status;
+
+typedef enum { MOE_F32 = 0, MOE_BF16 = 1 } moe_dtype;
+
+/* Layer shape ([DSMoE] アルゴリズム: d_model, n_routed, n_shared, top_k, d_ff). */
+typedef struct {
+    int64_t T;                /* tokens (batch * seq_len, flattened)              */
+    int32_t d_model;          /* d                                                 */
+    int32_t n_routed;         /* N routed experts                                  */
+    int32_t top_k;            /* K experts kept per token                          */
+    int32_t n_shared;         /* K_s always-active shared experts (may be 0)       */
+    int32_t d_ff;             /* f, hidden width of every expert                   */
+    int32_t dtype;            /* moe_dtype of x, expert weights/biases, hidden, y  */
+    float capacity_factor;    /* <= 0: no factor-derived limit                     */
+    int32_t capacity;         /* >= 0: explicit per-expert limit; -1: use factor   */
+} moe_config;
+
+/* Expert and router weights, nn.Linear layout (out_features, in_features). */
+typedef struct {
+    const float *w_router;    /* [N][d] float32                                   */
+    const float *router_bias; /* [N] float32 or NULL                              */
+    const void *w1;           /* [N][f][d] act                                    */
+    const void *b1;           /* [N][f] act or NULL                               */
+    const void *w2;           /* [N][d][f] act                                    */
+    const void *b2;           /* [N][d] act or NULL                               */
+    const void *ws1;          /* [K_s][f][d] act (NULL when K_s == 0)             */
+    const void *bs1;          /* [K_s][f] act or NULL                             */
+    const void *ws2;          /* [K_s][d][f] act (NULL when K_s == 0)             */
+    const void *bs2;          /* [K_s][d] act or NULL                             */
+} moe_weights;
+
+/*
+ * moe_route — router scores, top-K selection and renormalised gates
+ * ([TopK] ルーティングの仕組み; [DSMoE] gate equation).
+ *   x           [T][d] act
+ *   w_router    [N][d] float32;  router_bias [N] float32 or NULL (part of the
+ *               logit for both selection and gates)
+ *   logits      [T][N] float32 output (required; also the gates' input)
+ *   topk_idx    [T][K] int32 output, expert ids in slot order
+ *   topk_gate   [T][K] float32 output, sums to 1 per token
+ */
+int moe_route(const moe_config *cfg, const void *x, const float *w_router,
+              const float *router_bias, float *logits, int32_t *topk_idx,
+              float *topk_gate, void *stream);
+
+/*
+ * moe_permute — dispatch as an on-device permutation: per-expert histogram,
+ * capacity clip, exclusive scan, stable scatter ([EP] 推論フロー steps 2-3 on
+ * one GPU; [TopK] capacity section).
+ *   topk_idx    [T][K] int32 input, values in [0, N)
+ *   x           [T][d] act input, read only when x_perm != NULL
+ *   counts      [N] int32 output: kept rows per expert
+ *   offsets     [N+1] int32 output: exclusive scan of counts
+ *   row_token   [T*K] int32 output: rows 0..offsets[N]-1 hold the token of
+ *               each row, experts in order, tokens ascending within one
+ *   slot_row    [T*K] int32 output: row of (t, k), or -1 when dropped
+ *   n_dropped   [1] int32 output
+ *   x_perm      [T*K][d] act output (rows 0..offsets[N]-1) or NULL to skip
+ *   ws          device workspace of moe_permute_workspace_size(cfg) bytes
+ */
+int moe_permute(const moe_config *cfg, const int32_t *topk_idx, const void *x,
+                int32_t *counts, int32_t *offsets, int32_t *row_token, int32_t *slot_row,
+                int32_t *n_dropped, void *x_perm, void *ws, size_t ws_bytes, void *stream);
+size_t moe_permute_workspace_size(const moe_config *cfg);
+
+/*
+ * moe_grouped_ffn — every group's expert FFN over its contiguous rows:
+ * rows offsets[g] .. offsets[g+1]-1 get E_g(x_rows[r]) ([DSMoE] アルゴリズム,
+ * expert Linear(d, f) - SiLU - Linear(f, d)).
+ *   n_groups    number of experts in w1/w2 (>= 1)
+ *   x_rows      [max_rows][d] act input
+ *   offsets     [n_groups+1] int32 DEVICE array, non-decreasing, offsets[0]=0
+ *   max_rows    host-side upper bound on offsets[n_groups] (sizes the launch)
+ *   w1 [G][f][d], b1 [G][f] or NULL, w2 [G][d][f], b2 [G][d] or NULL (act)
+ *   h           [max_rows][f] act output (hidden activations)
+ *   y_rows      [max_rows][d] act output
+ * Only cfg->d_model, cfg->d_ff and cfg->dtype are read.
+ */
+int moe_grouped_ffn(const moe_config *cfg, int32_t n_groups, const void *x_rows,
+                    const int32_t *offsets, int64_t max_rows, const void *w1, const void *b1,
+                    const void *w2, const void *b2, void *h, void *y_rows, void *stream);
+
+/*
+ * moe_combine — y_t = sum_i S_i[t] + sum_{k: slot_row[t,k] >= 0}
+ * g[t,k] * y_rows[slot_row[t,k]] ([DSMoE] 共有エキスパート機構 equation).
+ *   y_rows      [*][d] act, indexed by slot_row
+ *   slot_row    [T][K] int32, topk_gate [T][K] float32
+ *   shared_out  [K_s][T][d] act or NULL (K_s from cfg->n_shared)
+ *   y           [T][d] act output
+ */
+int moe_combine(const moe_config *cfg, const void *y_rows, const int32_t *slot_row,
+                const float *topk_gate, const void *shared_out, void *y, void *stream);
+
+/*
+ * moe_layer_forward — the whole layer: route, permute (the gather is fused
+ * into the first expert GEMM), routed and shared expert FFNs, combine.
+ *   x [T][d] act input, y [T][d] act output.
+ *   topk_idx, topk_gate ([T][K]) and counts ([N]) are optional copies of the
+ *   routing outputs (NULL to skip).
+ *   ws          device workspace of moe_layer_workspace_size(cfg) bytes.
+ */
+int moe_layer_forward(const moe_config *cfg, const moe_weights *w, const void *x, void *y,
+                      int32_t *topk_idx, float *topk_gate, int32_t *counts,
+                      void *ws, size_t ws_bytes, void *stream);
+size_t moe_layer_workspace_size(const moe_config *cfg);
+
+/* Stages of moe_layer_forward, in launch order. */
+enum {
+    MOE_STAGE_ROUTER = 0,   /* router logits                                   */
+    MOE_STAGE_TOPK = 1,     /* top-K selection and gates                       */
+    MOE_STAGE_DISPATCH = 2, /* histogram, scan, scatter                        */
+    MOE_STAGE_UP = 3,       /* first Linear + SiLU, routed and shared experts  */
+    MOE_STAGE_DOWN = 4,     /* second Linear, routed and shared experts        */
+    MOE_STAGE_COMBINE = 5,  /* gate-weighted sum + shared outputs              */
+    MOE_STAGE_COUNT = 6
+};
+
+/*
+ * moe_layer_forward_events — moe_layer_forward that also records caller-owned
+ * HIP events on `stream` at every stage boundary, for timing the stages on the
+ * stream they run on.  stage_events points to MOE_STAGE_COUNT + 1 hipEvent_t
+ * handles (as void*): event i is recorded just before stage i is launched and
+ * event MOE_STAGE_COUNT after the last one.  NULL behaves like
+ * moe_layer_forward.  The events are only recorded, never waited on.
+ */
+int moe_layer_forward_events(const moe_config *cfg, const moe_weights *w, const void *x,
+                             void *y, int32_t *topk_idx, float *topk_gate, int32_t *counts,
+                             void *ws, size_t ws_bytes, void *const *stage_events,
+                             void *stream);
+
+/* Per-expert capacity the library applies for cfg (-1 = unlimited). */
+int64_t moe_capacity(const moe_config *cfg);
+
+/* Static text for a moe_status value. */
+const char *moe_status_string(int status);
+
+/* Interface version: 0x00MMmmpp. */
+int moe_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_MI355X_H */

@@ -1,0 +1,517 @@
+// Grouped expert GEMM: every group (expert) multiplies its own contiguous
+// slice of rows by its own weight matrix, with the bias and, for the first
+// Linear, the SiLU fused into the epilogue (DeepSeekMoE explainer page,
+// section アルゴリズム: expert = Linear(d, d_ff) - SiLU - Linear(d_ff, d)).
+//
+//   out[r, n] = epi( sum_k A[r, k] * W_g[n, k] + bias_g[n] ),  r in group g
+//
+// Both operands keep the reduction dimension contiguous (activations row-major
+// [rows][K], weights in nn.Linear layout [Nout][K]), so both tiles are loaded
+// the same way.
+//
+// Groups: routed groups take their row ranges from the device-resident
+// offsets written by the dispatch (no host round trip); shared-expert groups
+// cover all T_sh rows.  Every workgroup rebuilds the prefix sum of m-tiles
+// per group in LDS from those offsets, so the launch is sized from a host
+// upper bound and the work list lives entirely on the device.
+//
+// Scheduling: persistent workgroups; the tile range is split into eight equal
+// contiguous parts, one per XCD (workgroups are dealt to the eight XCDs
+// round-robin by id), and within a part tiles are visited in bands of GM
+// m-tiles so that the workgroups running together on one XCD share weight
+// tiles and activation tiles in that XCD's L2.
+//
+// bf16 path: MFMA v_mfma_f32_32x32x16_bf16, fp32 accumulate.  Tiles go from
+// HBM to registers (16-byte loads, prefetched one K-step ahead) to LDS, double
+// buffered, with an XOR swizzle of the 16-byte chunks so the fragment reads
+// of 32 rows hit distinct banks.  The weight tile is the MFMA's first operand,
+// so each lane ends up holding four consecutive output features of one row
+// and the epilogue writes 8-byte packed bf16 stores.
+//
+// fp32 path: a plain LDS-tiled VALU kernel (4x4 register tile per thread).
+#include "moe_common.h"
+
+namespace moe {
+namespace {
+
+constexpr int kMaxGroups = kMaxRouted + kMaxShared;
+constexpr int kXcds = 8;
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));   // 16 bytes, register-friendly
+
+struct GemmArgs {
+  const int32_t *offsets;
+  const void *A;
+  const int32_t *a_index;
+  const void *A_sh;
+  const void *W;
+  const void *bias;
+  const void *W_sh;
+  const void *bias_sh;
+  void *C;
+  void *C_sh;
+  int64_t T_sh;
+  int64_t a_sh_stride;
+  int n_routed;
+  int n_shared;
+  int Nout;
+  int K;
+};
+
+// Block-wide exclusive scan of one int per thread (NT threads, NT % 64 == 0).
+template <int NT>
+__device__ __forceinline__ int block_excl_scan(int v, int *s_tmp, int *total) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  int incl = v;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int o = __shfl_up(incl, off);
+    if (lane >= off) incl += o;
+  }
+  if (lane == 63) s_tmp[wave] = incl;
+  __syncthreads();
+  int base = 0, tot = 0;
+#pragma unroll
+  for (int w = 0; w < NT / 64; ++w) {
+    const int s = s_tmp[w];
+    base += (w < wave) ? s : 0;
+    tot += s;
+  }
+  *total = tot;
+  return base + incl - v;
+}
+
+// m-tile prefix over groups, built in LDS by every workgroup.
+template <int NT, int BM>
+__device__ int build_tile_prefix(const GemmArgs &a, int *s_pref, int *s_tmp) {
+  const int n_groups = a.n_routed + a.n_shared;
+  const int per = (n_groups + NT - 1) / NT;
+  const int g0 = threadIdx.x * per;
+  const int g1 = min(g0 + per, n_groups);
+  int local = 0;
+  for (int g = g0; g < g1; ++g) {
+    const int64_t rows = g < a.n_routed ? (a.offsets[g + 1] - a.offsets[g]) : a.T_sh;
+    local += static_cast<int>((rows + BM - 1) / BM);
+  }
+  int total;
+  int run = block_excl_scan<NT>(local, s_tmp, &total);
+  for (int g = g0; g < g1; ++g) {
+    s_pref[g] = run;
+    const int64_t rows = g < a.n_routed ? (a.offsets[g + 1] - a.offsets[g]) : a.T_sh;
+    run += static_cast<int>((rows + BM - 1) / BM);
+  }
+  if (threadIdx.x == 0) s_pref[n_groups] = total;
+  __syncthreads();
+  return total;
+}
+
+// Group of m-tile mt: largest g with s_pref[g] <= mt (never an empty group).
+__device__ __forceinline__ int find_group(const int *s_pref, int n_groups, int mt) {
+  int lo = 0, hi = n_groups;   // invariant: s_pref[lo] <= mt < s_pref[hi]
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if (s_pref[mid] <= mt) lo = mid; else hi = mid;
+  }
+  return lo;
+}
+
+template <typename T>
+struct TileView {
+  const T *W;              // group's weights [Nout][K]
+  const T *bias;           // group's bias [Nout] or null
+  int64_t rows;            // rows of the group
+  int64_t row0;            // first row of this tile within the group
+  int64_t out_base;        // output row index of the group's row 0
+  T *C;                    // output base
+  int g;
+};
+
+template <typename T>
+__device__ __forceinline__ TileView<T> tile_view(const GemmArgs &a, int g, int lm, int BM) {
+  TileView<T> v;
+  v.g = g;
+  v.row0 = static_cast<int64_t>(lm) * BM;
+  if (g < a.n_routed) {
+    const int64_t o0 = a.offsets[g];
+    v.rows = a.offsets[g + 1] - o0;
+    v.out_base = o0;
+    v.W = static_cast<const T *>(a.W) + static_cast<int64_t>(g) * a.Nout * a.K;
+    v.bias = a.bias ? static_cast<const T *>(a.bias) + static_cast<int64_t>(g) * a.Nout : nullptr;
+    v.C = static_cast<T *>(a.C);
+  } else {
+    const int gs = g - a.n_routed;
+    v.rows = a.T_sh;
+    v.out_base = static_cast<int64_t>(gs) * a.T_sh;
+    v.W = static_cast<const T *>(a.W_sh) + static_cast<int64_t>(gs) * a.Nout * a.K;
+    v.bias = a.bias_sh ? static_cast<const T *>(a.bias_sh) + static_cast<int64_t>(gs) * a.Nout
+                       : nullptr;
+    v.C = static_cast<T *>(a.C_sh);
+  }
+  return v;
+}
+
+// Source row pointer of local row r (clamped into the group).
+template <typename T>
+__device__ __forceinline__ const T *a_row_ptr(const GemmArgs &a, const TileView<T> &v,
+                                              int64_t r) {
+  if (r >= v.rows) r = v.rows - 1;
+  if (v.g < a.n_routed) {
+    const int64_t gr = v.out_base + r;
+    const int64_t src = a.a_index ? static_cast<int64_t>(a.a_index[gr]) : gr;
+    return static_cast<const T *>(a.A) + src * a.K;
+  }
+  const int gs = v.g - a.n_routed;
+  return static_cast<const T *>(a.A_sh) + static_cast<int64_t>(gs) * a.a_sh_stride + r * a.K;
+}
+
+// Decode a linear tile index into (m-tile, n-tile), banded by GM m-tiles.
+template <int GM>
+__device__ __forceinline__ void decode_tile(int L, int total_m, int n_nt, int *mt, int *nt) {
+  const int band = L / (GM * n_nt);
+  const int first = band * GM;
+  const int gm = min(GM, total_m - first);
+  const int r = L - band * GM * n_nt;
+  *mt = first + r % gm;
+  *nt = r / gm;
+}
+
+// ---------------------------------------------------------------------------
+// bf16 MFMA kernel
+// ---------------------------------------------------------------------------
+template <int A_CH, int B_CH, int BK>
+__device__ __forceinline__ void gload_tiles(u32x4_t (&ra)[A_CH], u32x4_t (&rb)[B_CH],
+                                            const uint16_t *const (&a_src)[A_CH],
+                                            const uint16_t *const (&b_src)[B_CH], int kb) {
+#pragma unroll
+  for (int i = 0; i < A_CH; ++i) ra[i] = *reinterpret_cast<const u32x4_t *>(a_src[i] + kb * BK);
+#pragma unroll
+  for (int i = 0; i < B_CH; ++i) rb[i] = *reinterpret_cast<const u32x4_t *>(b_src[i] + kb * BK);
+}
+
+// 16-byte chunk kc of tile row `row` lives at chunk position kc ^ (row & 7).
+template <int A_CH, int B_CH, int BM, int BK, int NT>
+__device__ __forceinline__ void lstore_tiles(uint16_t *stage, const u32x4_t (&ra)[A_CH],
+                                             const u32x4_t (&rb)[B_CH], int tid, int kc) {
+  uint16_t *sb = stage + BM * BK;
+#pragma unroll
+  for (int i = 0; i < A_CH; ++i) {
+    const int row = (tid >> 3) + i * (NT / 8);
+    *reinterpret_cast<u32x4_t *>(stage + row * BK + ((kc ^ (row & 7)) << 3)) = ra[i];
+  }
+#pragma unroll
+  for (int i = 0; i < B_CH; ++i) {
+    const int row = (tid >> 3) + i * (NT / 8);
+    *reinterpret_cast<u32x4_t *>(sb + row * BK + ((kc ^ (row & 7)) << 3)) = rb[i];
+  }
+}
+
+template <int BM, int BN, int WAVES_M, int WAVES_N, int EPI, int GM>
+__global__ __launch_bounds__(WAVES_M *WAVES_N * 64) void grouped_gemm_bf16_kernel(GemmArgs a) {
+  constexpr int NT = WAVES_M * WAVES_N * 64;
+  constexpr int BK = 64;                 // 8 chunks of 16 B per row
+  constexpr int WTM = BM / WAVES_M;      // rows (tokens) per wave
+  constexpr int WTN = BN / WAVES_N;      // output features per wave
+  constexpr int TM = WTM / 32;
+  constexpr int TN = WTN / 32;
+  constexpr int A_CH = BM * 8 / NT;      // 16-byte chunks per thread per stage
+  constexpr int B_CH = BN * 8 / NT;
+  constexpr int STAGE = (BM + BN) * BK;  // bf16 elements per stage
+  static_assert(WTM % 32 == 0 && WTN % 32 == 0, "wave tile must be MFMA-aligned");
+  static_assert((BM * 8) % NT == 0 && (BN * 8) % NT == 0, "chunks must divide evenly");
+
+  __shared__ __attribute__((aligned(16))) uint16_t s_tile[2 * STAGE];
+  __shared__ int s_pref[kMaxGroups + 1];
+  __shared__ int s_tmp[NT / 64];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = uniform(tid >> 6);
+  const int wm = wave % WAVES_M, wn = wave / WAVES_M;
+  const int n_groups = a.n_routed + a.n_shared;
+
+  const int total_m = build_tile_prefix<NT, BM>(a, s_pref, s_tmp);
+  const int n_nt = (a.Nout + BN - 1) / BN;
+  const int total = total_m * n_nt;
+  const int xcd = blockIdx.x % kXcds;
+  const int slot = blockIdx.x / kXcds;
+  const int nslots = gridDim.x / kXcds;
+  const int part = (total + kXcds - 1) / kXcds;
+  const int begin = xcd * part;
+  const int end = min(total, begin + part);
+  const int nk = a.K / BK;
+  const int kc = tid & 7;                 // this thread's 16-byte chunk column
+
+  for (int L = begin + slot; L < end; L += nslots) {
+    int mt, nt;
+    decode_tile<GM>(L, total_m, n_nt, &mt, &nt);
+    const int g = find_group(s_pref, n_groups, mt);
+    const TileView<uint16_t> v = tile_view<uint16_t>(a, g, mt - s_pref[g], BM);
+    const int n0 = nt * BN;
+
+    const uint16_t *a_src[A_CH];
+    const uint16_t *b_src[B_CH];
+#pragma unroll
+    for (int i = 0; i < A_CH; ++i) {
+      const int row = (tid >> 3) + i * (NT / 8);
+      a_src[i] = a_row_ptr(a, v, v.row0 + row) + kc * 8;
+    }
+#pragma unroll
+    for (int i = 0; i < B_CH; ++i) {
+      int n = n0 + (tid >> 3) + i * (NT / 8);
+      if (n >= a.Nout) n = a.Nout - 1;
+      b_src[i] = v.W + static_cast<int64_t>(n) * a.K + kc * 8;
+    }
+
+    u32x4_t ra[A_CH], rb[B_CH];
+    f32x16_t acc[TN][TM];
+#pragma unroll
+    for (int i = 0; i < TN; ++i)
+#pragma unroll
+      for (int j = 0; j < TM; ++j)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+
+    gload_tiles<A_CH, B_CH, BK>(ra, rb, a_src, b_src, 0);
+    lstore_tiles<A_CH, B_CH, BM, BK, NT>(s_tile, ra, rb, tid, kc);
+    __syncthreads();
+    for (int kb = 0; kb < nk; ++kb) {
+      const int cur = kb & 1;
+      if (kb + 1 < nk) gload_tiles<A_CH, B_CH, BK>(ra, rb, a_src, b_src, kb + 1);
+      const uint16_t *sa = s_tile + cur * STAGE;
+      const uint16_t *sb = sa + BM * BK;
+#pragma unroll
+      for (int ks = 0; ks < BK / 16; ++ks) {
+        const int c = ks * 2 + (lane >> 5);
+        bf16x8_t fa[TM], fb[TN];
+#pragma unroll
+        for (int mi = 0; mi < TM; ++mi) {
+          const int row = wm * WTM + mi * 32 + (lane & 31);
+          fa[mi] = *reinterpret_cast<const bf16x8_t *>(sa + row * BK + ((c ^ (row & 7)) << 3));
+        }
+#pragma unroll
+        for (int ni = 0; ni < TN; ++ni) {
+          const int row = wn * WTN + ni * 32 + (lane & 31);
+          fb[ni] = *reinterpret_cast<const bf16x8_t *>(sb + row * BK + ((c ^ (row & 7)) << 3));
+        }
+#pragma unroll
+        for (int ni = 0; ni < TN; ++ni)
+#pragma unroll
+          for (int mi = 0; mi < TM; ++mi)
+            acc[ni][mi] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[ni], fa[mi], acc[ni][mi], 0, 0, 0);
+      }
+      if (kb + 1 < nk) lstore_tiles<A_CH, B_CH, BM, BK, NT>(s_tile + (cur ^ 1) * STAGE, ra, rb, tid, kc);
+      __syncthreads();
+    }
+
+    // epilogue: acc[ni][mi][q*4 + j] holds feature n = base + q*8 + (lane>>5)*4 + j
+    // of row m = wm*WTM + mi*32 + (lane & 31)
+#pragma unroll
+    for (int mi = 0; mi < TM; ++mi) {
+      const int64_t r = v.row0 + wm * WTM + mi * 32 + (lane & 31);
+      if (r >= v.rows) continue;
+      uint16_t *out_row = v.C + (v.out_base + r) * a.Nout;
+#pragma unroll
+      for (int ni = 0; ni < TN; ++ni) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int n = n0 + wn * WTN + ni * 32 + q * 8 + (lane >> 5) * 4;
+          if (n >= a.Nout) continue;
+          float o[4];
+#pragma unroll
+          for (int j = 0; j < 4; ++j) o[j] = acc[ni][mi][q * 4 + j];
+          if (v.bias) {
+            const uint2 bq = *reinterpret_cast<const uint2 *>(v.bias + n);
+            o[0] += __uint_as_float(bq.x << 16);
+            o[1] += __uint_as_float(bq.x & 0xFFFF0000u);
+            o[2] += __uint_as_float(bq.y << 16);
+            o[3] += __uint_as_float(bq.y & 0xFFFF0000u);
+          }
+          if (EPI == kEpiBiasSilu) {
+#pragma unroll
+            for (int j = 0; j < 4; ++j) o[j] = silu(o[j]);
+          }
+          uint2 packed;
+          packed.x = f32_to_bf16(o[0]) | (static_cast<uint32_t>(f32_to_bf16(o[1])) << 16);
+          packed.y = f32_to_bf16(o[2]) | (static_cast<uint32_t>(f32_to_bf16(o[3])) << 16);
+          *reinterpret_cast<uint2 *>(out_row + n) = packed;
+        }
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// fp32 VALU kernel (also accepts bf16 operands): 64x64 tiles, 256 threads
+// ---------------------------------------------------------------------------
+template <typename TA, int EPI>
+__global__ __launch_bounds__(256) void grouped_gemm_valu_kernel(GemmArgs a) {
+  constexpr int BM = 64, BN = 64, BK = 16, NT = 256, GM = 8;
+  __shared__ float s_a[BK][BM + 4];
+  __shared__ float s_b[BK][BN + 4];
+  __shared__ int s_pref[kMaxGroups + 1];
+  __shared__ int s_tmp[NT / 64];
+  const int tid = threadIdx.x;
+  const int n_groups = a.n_routed + a.n_shared;
+  const int total_m = build_tile_prefix<NT, BM>(a, s_pref, s_tmp);
+  const int n_nt = (a.Nout + BN - 1) / BN;
+  const int total = total_m * n_nt;
+  const int xcd = blockIdx.x % kXcds, slot = blockIdx.x / kXcds, nslots = gridDim.x / kXcds;
+  const int part = (total + kXcds - 1) / kXcds;
+  const int begin = xcd * part, end = min(total, begin + part);
+  const int tm = tid & 15, tn = tid >> 4;
+  const int lrow = tid >> 2, lk = (tid & 3) * 4;   // loader: 64 rows x 4 chunks of 4
+
+  for (int L = begin + slot; L < end; L += nslots) {
+    int mt, nt;
+    decode_tile<GM>(L, total_m, n_nt, &mt, &nt);
+    const int g = find_group(s_pref, n_groups, mt);
+    const TileView<TA> v = tile_view<TA>(a, g, mt - s_pref[g], BM);
+    const int n0 = nt * BN;
+    const TA *arow = a_row_ptr<TA>(a, v, v.row0 + lrow);
+    int nb = n0 + lrow;
+    if (nb >= a.Nout) nb = a.Nout - 1;
+    const TA *brow = v.W + static_cast<int64_t>(nb) * a.K;
+
+    float acc[4][4] = {};
+    for (int k0 = 0; k0 < a.K; k0 += BK) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        s_a[lk + j][lrow] = Act<TA>::to_f32(arow[k0 + lk + j]);
+        s_b[lk + j][lrow] = Act<TA>::to_f32(brow[k0 + lk + j]);
+      }
+      __syncthreads();
+#pragma unroll
+      for (int k = 0; k < BK; ++k) {
+        float av[4], bv[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) { av[i] = s_a[k][tm * 4 + i]; bv[i] = s_b[k][tn * 4 + i]; }
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+          for (int j = 0; j < 4; ++j) acc[i][j] = __builtin_fmaf(av[i], bv[j], acc[i][j]);
+      }
+      __syncthreads();
+    }
+    TA *C = v.C;
+    const TA *bias = v.bias;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int64_t rr = v.row0 + tm * 4 + i;
+      if (rr >= v.rows) continue;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int n = n0 + tn * 4 + j;
+        if (n >= a.Nout) continue;
+        float o = acc[i][j];
+        if (bias) o += Act<TA>::to_f32(bias[n]);
+        if (EPI == kEpiBiasSilu) o = silu(o);
+        C[(v.out_base + rr) * a.Nout + n] = Act<TA>::from_f32(o);
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// host side
+// ---------------------------------------------------------------------------
+struct DevInfo {
+  int cus = 0;
+};
+
+DevInfo &dev_info() {
+  static DevInfo info[64];
+  int dev = 0;
+  (void)hipGetDevice(&dev);
+  DevInfo &d = info[dev & 63];
+  if (d.cus == 0) {
+    int v = 0;
+    if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || v <= 0)
+      v = 256;
+    d.cus = v;
+  }
+  return d;
+}
+
+GemmArgs make_args(const GemmGroups &g) {
+  GemmArgs a;
+  a.offsets = g.offsets;
+  a.A = g.A;
+  a.a_index = g.a_index;
+  a.A_sh = g.A_sh;
+  a.W = g.W;
+  a.bias = g.bias;
+  a.W_sh = g.W_sh;
+  a.bias_sh = g.bias_sh;
+  a.C = g.C;
+  a.C_sh = g.C_sh;
+  a.T_sh = g.T_sh;
+  a.a_sh_stride = g.a_sh_stride;
+  a.n_routed = g.n_routed;
+  a.n_shared = g.n_shared;
+  a.Nout = g.Nout;
+  a.K = g.K;
+  return a;
+}
+
+int64_t tiles_upper_bound(const GemmGroups &g, int BM, int BN) {
+  const int64_t m = g.max_routed_rows / BM + g.n_routed +
+                    static_cast<int64_t>(g.n_shared) * ((g.T_sh + BM - 1) / BM);
+  return m * ((g.Nout + BN - 1) / BN);
+}
+
+// Persistent grid: enough workgroups to fill the chip (per_cu resident per
+// CU), never more than tiles exist, always a multiple of the XCD count.
+unsigned persistent_grid(int64_t tiles_ub, int per_cu) {
+  const int64_t full = static_cast<int64_t>(dev_info().cus) * per_cu;
+  int64_t g = tiles_ub < full ? tiles_ub : full;
+  g = ((g + kXcds - 1) / kXcds) * kXcds;
+  if (g < kXcds) g = kXcds;
+  return static_cast<unsigned>(g);
+}
+
+template <int BM, int BN, int WM, int WN, int GM>
+hipError_t launch_bf16(const GemmArgs &a, const GemmGroups &g, Epilogue epi, int per_cu,
+                       hipStream_t s) {
+  const unsigned grid = persistent_grid(tiles_upper_bound(g, BM, BN), per_cu);
+  const dim3 block(WM * WN * 64);
+  if (epi == kEpiBiasSilu)
+    hipLaunchKernelGGL((grouped_gemm_bf16_kernel<BM, BN, WM, WN, kEpiBiasSilu, GM>), dim3(grid),
+                       block, 0, s, a);
+  else
+    hipLaunchKernelGGL((grouped_gemm_bf16_kernel<BM, BN, WM, WN, kEpiBias, GM>), dim3(grid),
+                       block, 0, s, a);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_grouped_gemm(bool bf16, const GemmGroups &g, Epilogue epi, hipStream_t s) {
+  const GemmArgs a = make_args(g);
+  if (g.n_routed + g.n_shared <= 0 || g.Nout <= 0) return hipSuccess;
+  if (bf16 && g.K % 64 == 0 && g.Nout % 4 == 0) {
+    // rows per routed group decide the tile: few rows -> stream weights with a
+    // short M tile; many rows -> square tiles for operand reuse
+    const int64_t groups = g.n_routed > 0 ? g.n_routed : 1;
+    const int64_t mean_rows = g.max_routed_rows / groups;
+    if (mean_rows <= 48 && g.T_sh <= 256)
+      return launch_bf16<32, 128, 1, 4, 8>(a, g, epi, 2, s);
+    return launch_bf16<128, 128, 2, 2, 8>(a, g, epi, 2, s);
+  }
+  const unsigned grid = persistent_grid(tiles_upper_bound(g, 64, 64), 4);
+  if (bf16) {
+    if (epi == kEpiBiasSilu)
+      hipLaunchKernelGGL((grouped_gemm_valu_kernel<uint16_t, kEpiBiasSilu>), dim3(grid), dim3(256), 0, s, a);
+    else
+      hipLaunchKernelGGL((grouped_gemm_valu_kernel<uint16_t, kEpiBias>), dim3(grid), dim3(256), 0, s, a);
+  } else {
+    if (epi == kEpiBiasSilu)
+      hipLaunchKernelGGL((grouped_gemm_valu_kernel<float, kEpiBiasSilu>), dim3(grid), dim3(256), 0, s, a);
+    else
+      hipLaunchKernelGGL((grouped_gemm_valu_kernel<float, kEpiBias>), dim3(grid), dim3(256), 0, s, a);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace moe

@@ -1,0 +1,317 @@
+// Host side of the C interface declared in include/moe_mi355x.h: argument
+// validation, workspace layout and kernel launches on the caller's stream.
+// No call allocates device memory, synchronises, or copies device data back.
+#include <math.h>
+#include <string.h>
+
+#include "moe_common.h"
+#include "moe_mi355x.h"
+
+namespace {
+
+using moe::GemmGroups;
+
+constexpr size_t kAlign = 256;
+inline size_t align_up(size_t b) { return (b + kAlign - 1) & ~(kAlign - 1); }
+
+bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+size_t act_bytes(const moe_config *c) { return c->dtype == MOE_BF16 ? 2 : 4; }
+
+// Shape checks shared by every entry point.  `need_route` adds the routing
+// limits (N, K); `need_ffn` adds the expert widths.
+int check_config(const moe_config *c, bool need_route, bool need_ffn) {
+  if (!c) return MOE_ERR_INVALID_ARG;
+  if (c->T < 0 || c->d_model <= 0) return MOE_ERR_INVALID_ARG;
+  if (c->dtype != MOE_F32 && c->dtype != MOE_BF16) return MOE_ERR_INVALID_ARG;
+  const int mult = c->dtype == MOE_BF16 ? 64 : 16;
+  if (c->d_model % mult != 0) return MOE_ERR_UNSUPPORTED;
+  if (need_route) {
+    if (c->n_routed <= 0 || c->top_k <= 0 || c->top_k > c->n_routed) return MOE_ERR_INVALID_ARG;
+    if (c->n_routed > moe::kMaxRouted || c->top_k > 64) return MOE_ERR_UNSUPPORTED;
+    if (c->T * static_cast<int64_t>(c->top_k) >= (int64_t(1) << 31)) return MOE_ERR_UNSUPPORTED;
+    if (c->capacity < -1) return MOE_ERR_INVALID_ARG;
+  }
+  if (need_ffn) {
+    if (c->d_ff <= 0) return MOE_ERR_INVALID_ARG;
+    if (c->d_ff % mult != 0) return MOE_ERR_UNSUPPORTED;
+    if (c->n_shared < 0) return MOE_ERR_INVALID_ARG;
+    if (c->n_shared > moe::kMaxShared) return MOE_ERR_UNSUPPORTED;
+  }
+  return MOE_OK;
+}
+
+int hip_status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_HIP; }
+
+int64_t capacity_of(const moe_config *c) {
+  if (c->capacity >= 0) return c->capacity;
+  if (!(c->capacity_factor > 0.0f)) return -1;
+  const double v = static_cast<double>(c->capacity_factor) * static_cast<double>(c->T) *
+                   static_cast<double>(c->top_k) / static_cast<double>(c->n_routed);
+  return static_cast<int64_t>(ceil(v));
+}
+
+// Workspace of the whole layer, carved in this order (each piece 256-aligned).
+struct LayerWs {
+  float *logits;
+  int32_t *idx;
+  float *gates;
+  int32_t *counts;
+  int32_t *offsets;
+  int32_t *n_dropped;
+  int32_t *row_token;
+  int32_t *slot_row;
+  void *dispatch_ws;
+  void *h;       // routed hidden [T*K][f]
+  void *h_sh;    // shared hidden [Ks][T][f]
+  void *y_rows;  // routed outputs [T*K][d]
+  void *s_out;   // shared outputs [Ks][T][d]
+  size_t bytes;
+};
+
+LayerWs layer_ws(const moe_config *c, void *base) {
+  LayerWs w;
+  char *p = static_cast<char *>(base);
+  size_t off = 0;
+  auto take = [&](size_t b) {
+    char *q = p ? p + off : nullptr;
+    off += align_up(b);
+    return static_cast<void *>(q);
+  };
+  const int64_t T = c->T, K = c->top_k, N = c->n_routed, Ks = c->n_shared;
+  const size_t ab = act_bytes(c);
+  w.logits = static_cast<float *>(take(sizeof(float) * T * N));
+  w.idx = static_cast<int32_t *>(take(sizeof(int32_t) * T * K));
+  w.gates = static_cast<float *>(take(sizeof(float) * T * K));
+  w.counts = static_cast<int32_t *>(take(sizeof(int32_t) * N));
+  w.offsets = static_cast<int32_t *>(take(sizeof(int32_t) * (N + 1)));
+  w.n_dropped = static_cast<int32_t *>(take(sizeof(int32_t)));
+  w.row_token = static_cast<int32_t *>(take(sizeof(int32_t) * T * K));
+  w.slot_row = static_cast<int32_t *>(take(sizeof(int32_t) * T * K));
+  w.dispatch_ws = take(moe::dispatch_workspace_bytes(T, static_cast<int>(K), static_cast<int>(N)));
+  w.h = take(ab * T * K * c->d_ff);
+  w.h_sh = take(ab * Ks * T * c->d_ff);
+  w.y_rows = take(ab * T * K * c->d_model);
+  w.s_out = take(ab * Ks * T * c->d_model);
+  w.bytes = off;
+  return w;
+}
+
+}  // namespace
+
+extern "C" {
+
+int moe_version(void) { return 0x000100; }
+
+const char *moe_status_string(int status) {
+  switch (status) {
+    case MOE_OK: return "ok";
+    case MOE_ERR_INVALID_ARG: return "invalid argument";
+    case MOE_ERR_UNSUPPORTED: return "unsupported size";
+    case MOE_ERR_WORKSPACE: return "workspace missing or too small";
+    case MOE_ERR_HIP: return "HIP runtime error";
+    default: return "unknown status";
+  }
+}
+
+int64_t moe_capacity(const moe_config *cfg) {
+  if (!cfg || cfg->n_routed <= 0) return -1;
+  return capacity_of(cfg);
+}
+
+int moe_route(const moe_config *cfg, const void *x, const float *w_router,
+              const float *router_bias, float *logits, int32_t *topk_idx, float *topk_gate,
+              void *stream) {
+  int st = check_config(cfg, true, false);
+  if (st != MOE_OK) return st;
+  if (cfg->T == 0) return MOE_OK;
+  if (!x || !w_router || !logits || !topk_idx || !topk_gate) return MOE_ERR_INVALID_ARG;
+  if (!aligned16(x) || !aligned16(w_router)) return MOE_ERR_INVALID_ARG;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const bool bf16 = cfg->dtype == MOE_BF16;
+  st = hip_status(moe::launch_router_logits(bf16, x, w_router, router_bias, logits, cfg->T,
+                                            cfg->d_model, cfg->n_routed, s));
+  if (st != MOE_OK) return st;
+  return hip_status(moe::launch_topk_gates(logits, cfg->T, cfg->n_routed, cfg->top_k, topk_idx,
+                                           topk_gate, s));
+}
+
+size_t moe_permute_workspace_size(const moe_config *cfg) {
+  if (check_config(cfg, true, false) != MOE_OK) return 0;
+  return moe::dispatch_workspace_bytes(cfg->T, cfg->top_k, cfg->n_routed);
+}
+
+int moe_permute(const moe_config *cfg, const int32_t *topk_idx, const void *x, int32_t *counts,
+                int32_t *offsets, int32_t *row_token, int32_t *slot_row, int32_t *n_dropped,
+                void *x_perm, void *ws, size_t ws_bytes, void *stream) {
+  int st = check_config(cfg, true, false);
+  if (st != MOE_OK) return st;
+  if (cfg->T == 0) return MOE_OK;
+  if (!topk_idx || !counts || !offsets || !row_token || !slot_row || !n_dropped)
+    return MOE_ERR_INVALID_ARG;
+  if (x_perm && (!x || !aligned16(x) || !aligned16(x_perm))) return MOE_ERR_INVALID_ARG;
+  const size_t need = moe::dispatch_workspace_bytes(cfg->T, cfg->top_k, cfg->n_routed);
+  if (!ws || ws_bytes < need) return MOE_ERR_WORKSPACE;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  st = hip_status(moe::launch_dispatch(topk_idx, cfg->T, cfg->top_k, cfg->n_routed,
+                                       capacity_of(cfg), counts, offsets, row_token, slot_row,
+                                       n_dropped, ws, s));
+  if (st != MOE_OK || !x_perm) return st;
+  return hip_status(moe::launch_gather_rows(cfg->dtype == MOE_BF16, x, row_token,
+                                            offsets + cfg->n_routed, cfg->T * cfg->top_k,
+                                            cfg->d_model, x_perm, s));
+}
+
+int moe_grouped_ffn(const moe_config *cfg, int32_t n_groups, const void *x_rows,
+                    const int32_t *offsets, int64_t max_rows, const void *w1, const void *b1,
+                    const void *w2, const void *b2, void *h, void *y_rows, void *stream) {
+  int st = check_config(cfg, false, true);
+  if (st != MOE_OK) return st;
+  if (n_groups <= 0 || max_rows < 0) return MOE_ERR_INVALID_ARG;
+  if (n_groups > moe::kMaxRouted + moe::kMaxShared) return MOE_ERR_UNSUPPORTED;
+  if (max_rows == 0) return MOE_OK;
+  if (max_rows >= (int64_t(1) << 31)) return MOE_ERR_UNSUPPORTED;
+  if (!x_rows || !offsets || !w1 || !w2 || !h || !y_rows) return MOE_ERR_INVALID_ARG;
+  if (!aligned16(x_rows) || !aligned16(w1) || !aligned16(w2) || !aligned16(h) ||
+      !aligned16(y_rows))
+    return MOE_ERR_INVALID_ARG;
+  const bool bf16 = cfg->dtype == MOE_BF16;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  GemmGroups g{};
+  g.offsets = offsets;
+  g.n_routed = n_groups;
+  g.A = x_rows;
+  g.W = w1;
+  g.bias = b1;
+  g.C = h;
+  g.Nout = cfg->d_ff;
+  g.K = cfg->d_model;
+  g.max_routed_rows = max_rows;
+  st = hip_status(moe::launch_grouped_gemm(bf16, g, moe::kEpiBiasSilu, s));
+  if (st != MOE_OK) return st;
+  g.A = h;
+  g.W = w2;
+  g.bias = b2;
+  g.C = y_rows;
+  g.Nout = cfg->d_model;
+  g.K = cfg->d_ff;
+  return hip_status(moe::launch_grouped_gemm(bf16, g, moe::kEpiBias, s));
+}
+
+int moe_combine(const moe_config *cfg, const void *y_rows, const int32_t *slot_row,
+                const float *topk_gate, const void *shared_out, void *y, void *stream) {
+  int st = check_config(cfg, true, false);
+  if (st != MOE_OK) return st;
+  if (cfg->n_shared < 0) return MOE_ERR_INVALID_ARG;
+  if (cfg->n_shared > moe::kMaxShared) return MOE_ERR_UNSUPPORTED;
+  if (cfg->T == 0) return MOE_OK;
+  if (!y_rows || !slot_row || !topk_gate || !y) return MOE_ERR_INVALID_ARG;
+  if (cfg->n_shared > 0 && !shared_out) return MOE_ERR_INVALID_ARG;
+  if (!aligned16(y_rows) || !aligned16(y) || (shared_out && !aligned16(shared_out)))
+    return MOE_ERR_INVALID_ARG;
+  return hip_status(moe::launch_combine(cfg->dtype == MOE_BF16, y_rows, slot_row, topk_gate,
+                                        cfg->n_shared > 0 ? shared_out : nullptr, cfg->n_shared,
+                                        cfg->T, cfg->top_k, cfg->d_model, y,
+                                        static_cast<hipStream_t>(stream)));
+}
+
+size_t moe_layer_workspace_size(const moe_config *cfg) {
+  if (check_config(cfg, true, true) != MOE_OK) return 0;
+  return layer_ws(cfg, nullptr).bytes;
+}
+
+int moe_layer_forward(const moe_config *cfg, const moe_weights *w, const void *x, void *y,
+                      int32_t *topk_idx, float *topk_gate, int32_t *counts, void *ws,
+                      size_t ws_bytes, void *stream) {
+  return moe_layer_forward_events(cfg, w, x, y, topk_idx, topk_gate, counts, ws, ws_bytes,
+                                  nullptr, stream);
+}
+
+int moe_layer_forward_events(const moe_config *cfg, const moe_weights *w, const void *x,
+                             void *y, int32_t *topk_idx, float *topk_gate, int32_t *counts,
+                             void *ws, size_t ws_bytes, void *const *stage_events,
+                             void *stream) {
+  int st = check_config(cfg, true, true);
+  if (st != MOE_OK) return st;
+  if (!w) return MOE_ERR_INVALID_ARG;
+  if (cfg->T == 0) return MOE_OK;
+  if (!x || !y || !w->w_router || !w->w1 || !w->w2) return MOE_ERR_INVALID_ARG;
+  if (cfg->n_shared > 0 && (!w->ws1 || !w->ws2)) return MOE_ERR_INVALID_ARG;
+  if (!aligned16(x) || !aligned16(y) || !aligned16(w->w_router) || !aligned16(w->w1) ||
+      !aligned16(w->w2))
+    return MOE_ERR_INVALID_ARG;
+  const LayerWs L = layer_ws(cfg, ws);
+  if (!ws || ws_bytes < L.bytes) return MOE_ERR_WORKSPACE;
+
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const bool bf16 = cfg->dtype == MOE_BF16;
+  const int64_t T = cfg->T;
+  const int K = cfg->top_k, N = cfg->n_routed, Ks = cfg->n_shared;
+  int32_t *idx = topk_idx ? topk_idx : L.idx;
+  float *gates = topk_gate ? topk_gate : L.gates;
+  int32_t *cnt = counts ? counts : L.counts;
+  auto mark = [&](int i) -> int {
+    if (!stage_events) return MOE_OK;
+    return hip_status(hipEventRecord(static_cast<hipEvent_t>(stage_events[i]), s));
+  };
+
+  if ((st = mark(MOE_STAGE_ROUTER)) != MOE_OK) return st;
+  st = hip_status(moe::launch_router_logits(bf16, x, w->w_router, w->router_bias, L.logits, T,
+                                            cfg->d_model, N, s));
+  if (st != MOE_OK) return st;
+  if ((st = mark(MOE_STAGE_TOPK)) != MOE_OK) return st;
+  st = hip_status(moe::launch_topk_gates(L.logits, T, N, K, idx, gates, s));
+  if (st != MOE_OK) return st;
+  if ((st = mark(MOE_STAGE_DISPATCH)) != MOE_OK) return st;
+  st = hip_status(moe::launch_dispatch(idx, T, K, N, capacity_of(cfg), cnt, L.offsets,
+                                       L.row_token, L.slot_row, L.n_dropped, L.dispatch_ws, s));
+  if (st != MOE_OK) return st;
+
+  // First Linear + SiLU: routed rows gather their token's x directly.
+  GemmGroups g{};
+  g.offsets = L.offsets;
+  g.n_routed = N;
+  g.A = x;
+  g.a_index = L.row_token;
+  g.n_shared = Ks;
+  g.T_sh = T;
+  g.A_sh = x;
+  g.a_sh_stride = 0;
+  g.W = w->w1;
+  g.bias = w->b1;
+  g.W_sh = w->ws1;
+  g.bias_sh = w->bs1;
+  g.C = L.h;
+  g.C_sh = L.h_sh;
+  g.Nout = cfg->d_ff;
+  g.K = cfg->d_model;
+  g.max_routed_rows = T * K;
+  if ((st = mark(MOE_STAGE_UP)) != MOE_OK) return st;
+  st = hip_status(moe::launch_grouped_gemm(bf16, g, moe::kEpiBiasSilu, s));
+  if (st != MOE_OK) return st;
+
+  // Second Linear.
+  g.A = L.h;
+  g.a_index = nullptr;
+  g.A_sh = L.h_sh;
+  g.a_sh_stride = T * cfg->d_ff;
+  g.W = w->w2;
+  g.bias = w->b2;
+  g.W_sh = w->ws2;
+  g.bias_sh = w->bs2;
+  g.C = L.y_rows;
+  g.C_sh = L.s_out;
+  g.Nout = cfg->d_model;
+  g.K = cfg->d_ff;
+  if ((st = mark(MOE_STAGE_DOWN)) != MOE_OK) return st;
+  st = hip_status(moe::launch_grouped_gemm(bf16, g, moe::kEpiBias, s));
+  if (st != MOE_OK) return st;
+
+  if ((st = mark(MOE_STAGE_COMBINE)) != MOE_OK) return st;
+  st = hip_status(moe::launch_combine(bf16, L.y_rows, L.slot_row, gates,
+                                      Ks > 0 ? L.s_out : nullptr, Ks, T, K, cfg->d_model, y, s));
+  if (st != MOE_OK) return st;
+  return mark(MOE_STAGE_COUNT);
+}
+
+}  // extern "C"

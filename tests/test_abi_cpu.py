@@ -1,0 +1,113 @@
+"""The C library loads, exports every declared entry point, and rejects bad
+arguments on the host (no GPU needed: validation happens before any launch)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "moe_mi355x.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(moe_\w+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def B():
+    from sparse_mixture_experts_renormalised_amd import binding
+    if not os.path.exists(binding.LIB_PATH):
+        import __graft_entry__
+        __graft_entry__.build()
+    binding.lib()
+    return binding
+
+
+def test_every_declared_symbol_is_exported(B):
+    names = declared_functions()
+    assert "moe_layer_forward" in names and "moe_route" in names
+    for n in names:
+        assert hasattr(B.lib(), n), n
+    assert set(names) == set(B.EXPORTS)
+
+
+def test_version_and_status_strings(B):
+    assert B.lib().moe_version() == 0x000100
+    assert B.lib().moe_status_string(0) == b"ok"
+    assert B.lib().moe_status_string(-3).startswith(b"workspace")
+
+
+def test_capacity_rule(B):
+    assert B.capacity(B.config(128, 7168, 256, 8, 1, 2048, "bf16", 1.25)) == 5
+    assert B.capacity(B.config(10, 64, 3, 2, 0, 64, "bf16", 1.0)) == 7
+    assert B.capacity(B.config(10, 64, 3, 2, 0, 64, "bf16", 0.0)) == -1
+    assert B.capacity(B.config(10, 64, 3, 2, 0, 64, "bf16", 1.0, 0)) == 0
+
+
+def call_status(fn, *args):
+    try:
+        fn(*args)
+    except Exception as e:     # MoeError carries the status
+        return getattr(e, "status", None)
+    return 0
+
+
+def test_invalid_arguments_are_rejected_before_launch(B):
+    L = B.lib()
+    P = ctypes.c_void_p
+    good = B.config(64, 128, 8, 2, 0, 256, "bf16")
+    # K > N, K = 0, N too large, bad dtype, unaligned widths
+    for cfg, want in [(B.config(64, 128, 4, 5, 0, 256, "bf16"), -1),
+                      (B.config(64, 128, 4, 0, 0, 256, "bf16"), -1),
+                      (B.config(64, 128, 2048, 2, 0, 256, "bf16"), -2),
+                      (B.config(64, 100, 8, 2, 0, 256, "bf16"), -2),
+                      (B.config(64, 128, 8, 2, 0, 96, "bf16"), -2),
+                      (B.config(64, 128, 8, 2, 65, 256, "bf16"), -2),
+                      (B.config(-1, 128, 8, 2, 0, 256, "bf16"), -1)]:
+        assert L.moe_layer_forward(ctypes.byref(cfg), None, None, None, None, None, None, None,
+                                   0, None) == want
+    bad = B.config(64, 128, 8, 2, 0, 256, "bf16")
+    bad.dtype = 7
+    assert L.moe_route(ctypes.byref(bad), None, None, None, None, None, None, None) == -1
+    # NULL pointers and missing workspace
+    assert L.moe_route(ctypes.byref(good), None, None, None, None, None, None, None) == -1
+    assert L.moe_permute(ctypes.byref(good), P(16), None, P(16), P(16), P(16), P(16), P(16),
+                         None, None, 0, None) == -3
+    w = B.Weights()
+    assert L.moe_layer_forward(ctypes.byref(good), ctypes.byref(w), P(16), P(16), None, None,
+                               None, None, 0, None) == -1
+    w.w_router = w.w1 = w.w2 = 4096
+    assert L.moe_layer_forward(ctypes.byref(good), ctypes.byref(w), P(4096), P(4096), None, None,
+                               None, None, 0, None) == -3
+    # misaligned device pointer
+    assert L.moe_layer_forward(ctypes.byref(good), ctypes.byref(w), P(4100), P(4096), None, None,
+                               None, None, 1 << 30, P(4096)) == -1
+    # grouped FFN argument checks
+    assert L.moe_grouped_ffn(ctypes.byref(good), 0, None, None, 10, None, None, None, None, None,
+                             None, None) == -1
+    assert L.moe_grouped_ffn(ctypes.byref(good), 3, None, None, 10, None, None, None, None, None,
+                             None, None) == -1
+    # combine needs shared outputs when shared experts exist
+    sh = B.config(64, 128, 8, 2, 2, 256, "bf16")
+    assert L.moe_combine(ctypes.byref(sh), P(16), P(16), P(16), None, P(16), None) == -1
+
+
+def test_empty_batch_is_a_no_op(B):
+    L = B.lib()
+    cfg = B.config(0, 128, 8, 2, 0, 256, "bf16")
+    w = B.Weights()
+    assert L.moe_layer_forward(ctypes.byref(cfg), ctypes.byref(w), None, None, None, None, None,
+                               None, 0, None) == 0
+    assert L.moe_route(ctypes.byref(cfg), None, None, None, None, None, None, None) == 0
+
+
+def test_workspace_sizes_grow_with_the_layer(B):
+    small = B.layer_workspace_size(B.config(64, 128, 8, 2, 0, 256, "f32"))
+    big = B.layer_workspace_size(B.config(4096, 7168, 256, 8, 1, 2048, "bf16"))
+    assert 0 < small < big
+    # hidden + expert outputs of every assignment dominate: T*K*(d+f) act elements
+    assert big >= 4096 * 8 * (7168 + 2048) * 2
+    assert B.layer_workspace_size(B.config(64, 128, 8, 9, 0, 256, "f32")) == 0

@@ -1,0 +1,391 @@
+"""Parity of the HIP library (through its C interface) with the CPU oracle.
+
+Bar: integer outputs (expert ids, counts, offsets, permutation, drops) bit
+exact; logits bit exact (same fixed fused-multiply-add order); gates within
+1e-6; outputs within relative L2 error 1e-5 (fp32 layers) or 1e-2 (bf16
+layers, fp32 accumulate, bf16 hidden and expert outputs).  Every input comes
+from the seeded generator; every expected value from the oracle.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads as W
+import workloads.device  # noqa: F401  (device-resident instances)
+
+pytestmark = pytest.mark.gpu
+
+TOL = {"f32": 1e-5, "bf16": 1e-2}
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from sparse_mixture_experts_renormalised_amd import binding
+    binding.lib()     # fails loudly when the library is missing
+    yield
+
+
+def B():
+    from sparse_mixture_experts_renormalised_amd import binding
+    return binding
+
+
+def rel_l2(got, ref):
+    got = np.asarray(got, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    den = np.linalg.norm(ref)
+    return float(np.linalg.norm(got - ref) / (den if den > 0 else 1.0))
+
+
+def host(t):
+    return t.float().cpu().numpy() if t.dtype in (torch.bfloat16, torch.float32) else t.cpu().numpy()
+
+
+def act_dtype(wl):
+    return torch.bfloat16 if wl.dtype == "bf16" else torch.float32
+
+
+def bias_np(wl):
+    b = wl.router_bias_values()
+    return None if b is None else b.numpy()
+
+
+def providers_host(wl):
+    cache = {}
+
+    def routed(e):
+        if ("r", e) not in cache:
+            cache[("r", e)] = tuple(None if t is None else t.float().numpy() for t in wl.routed_expert(e))
+        return cache[("r", e)]
+
+    def shared(i):
+        if ("s", i) not in cache:
+            cache[("s", i)] = tuple(None if t is None else t.float().numpy() for t in wl.shared_expert(i))
+        return cache[("s", i)]
+    return routed, shared
+
+
+def cfg_of(wl, capacity=-1):
+    return B().config(wl.T, wl.d_model, wl.n_routed, wl.top_k, wl.n_shared, wl.d_ff, wl.dtype,
+                      wl.capacity_factor, capacity)
+
+
+# ---------------------------------------------------------------------------
+# the generator gives the same bits on the device as on the host
+# ---------------------------------------------------------------------------
+
+def test_device_generator_matches_host():
+    for dtype in ("f32", "bf16"):
+        h = W.fill_normal((333, 517), 0.3, dtype, 7, 4, 9)
+        d = W.fill_normal((333, 517), 0.3, dtype, 7, 4, 9, device="cuda")
+        assert torch.equal(h, d.cpu())
+    wl = W.get_workload("dsv3_prefill")
+    for e in (0, 255):
+        dh = wl.routed_expert(e)[0]
+        dd = wl.routed_expert(e, "cuda")[0]
+        assert torch.equal(dh, dd.cpu())
+
+
+# ---------------------------------------------------------------------------
+# moe_route
+# ---------------------------------------------------------------------------
+
+ROUTE_CASES = [W.get_workload(n) for n in W.WORKLOADS] + [
+    W.custom_workload("ragged_T", T=131, d_model=64, n_routed=24, top_k=5, n_shared=0, d_ff=64,
+                      dtype="bf16", router_bias="gauss", router_bias_var=0.5),
+    W.custom_workload("wide_N", T=70, d_model=32, n_routed=1000, top_k=64, n_shared=0, d_ff=16,
+                      dtype="f32"),
+    W.custom_workload("T1_K1", T=1, d_model=16, n_routed=3, top_k=1, n_shared=0, d_ff=16,
+                      dtype="f32"),
+]
+
+
+@pytest.mark.parametrize("wl", ROUTE_CASES, ids=lambda w: w.name)
+def test_route_bit_exact(wl):
+    b = B()
+    cfg = cfg_of(wl)
+    x = wl.x("cuda")
+    wr = wl.w_router("cuda")
+    rb = wl.router_bias_values("cuda")
+    T, N, K = wl.T, wl.n_routed, wl.top_k
+    logits = torch.empty((T, N), dtype=torch.float32, device="cuda")
+    idx = torch.empty((T, K), dtype=torch.int32, device="cuda")
+    gates = torch.empty((T, K), dtype=torch.float32, device="cuda")
+    b.route(cfg, x, wr, rb, logits, idx, gates)
+    torch.cuda.synchronize()
+    ref_l, ref_i, ref_g = oracle.route(host(x), host(wr), bias_np(wl), K)
+    assert np.array_equal(logits.cpu().numpy().view(np.uint32), ref_l.view(np.uint32))
+    assert np.array_equal(idx.cpu().numpy(), ref_i)
+    assert np.abs(gates.cpu().numpy() - ref_g).max() <= 1e-6
+
+
+def test_route_all_ties_pick_lowest_ids():
+    b = B()
+    wl = W.custom_workload("ties", T=67, d_model=64, n_routed=40, top_k=7, n_shared=0, d_ff=64,
+                           dtype="bf16")
+    cfg = cfg_of(wl)
+    x = wl.x("cuda")
+    wr = torch.zeros((40, 64), dtype=torch.float32, device="cuda")
+    logits = torch.empty((67, 40), dtype=torch.float32, device="cuda")
+    idx = torch.empty((67, 7), dtype=torch.int32, device="cuda")
+    gates = torch.empty((67, 7), dtype=torch.float32, device="cuda")
+    b.route(cfg, x, wr, None, logits, idx, gates)
+    torch.cuda.synchronize()
+    assert np.array_equal(idx.cpu().numpy(), np.tile(np.arange(7, dtype=np.int32), (67, 1)))
+    assert np.abs(gates.cpu().numpy() - 1.0 / 7).max() <= 1e-7
+
+
+# ---------------------------------------------------------------------------
+# moe_permute (fed the oracle's routing)
+# ---------------------------------------------------------------------------
+
+def random_idx(T, N, K, seed):
+    rng = np.random.default_rng(seed)
+    return np.stack([rng.permutation(N)[:K] for _ in range(T)]).astype(np.int32)
+
+
+PERMUTE_CASES = [
+    (1, 4, 1, -1), (63, 8, 2, -1), (64, 8, 2, -1), (65, 8, 2, 3), (200, 33, 5, -1),
+    (200, 33, 5, 0), (200, 33, 5, 7), (777, 256, 8, 5), (4097, 64, 8, -1), (300, 1000, 16, 2),
+]
+
+
+@pytest.mark.parametrize("T,N,K,C", PERMUTE_CASES)
+def test_permute_bit_exact(T, N, K, C):
+    b = B()
+    d = 64
+    wl = W.custom_workload("perm", T=T, d_model=d, n_routed=N, top_k=K, n_shared=0, d_ff=64,
+                           dtype="bf16")
+    cfg = cfg_of(wl, capacity=C)
+    idx_h = random_idx(T, N, K, T * 31 + N)
+    idx = torch.from_numpy(idx_h).cuda()
+    x = wl.x("cuda")
+    st = W.device.stage_tensors(wl)
+    ws = torch.empty((b.permute_workspace_size(cfg),), dtype=torch.uint8, device="cuda")
+    b.permute(cfg, idx, x, st["counts"], st["offsets"], st["row_token"], st["slot_row"],
+              st["n_dropped"], st["x_perm"], ws)
+    torch.cuda.synchronize()
+    ref = oracle.dispatch(idx_h, N, None if C < 0 else C)
+    R = int(ref["offsets"][-1])
+    assert np.array_equal(st["counts"].cpu().numpy(), ref["counts"])
+    assert np.array_equal(st["offsets"].cpu().numpy(), ref["offsets"])
+    assert np.array_equal(st["row_token"][:R].cpu().numpy(), ref["row_token"])
+    assert np.array_equal(st["slot_row"].cpu().numpy().reshape(T, K), ref["slot_row"])
+    assert int(st["n_dropped"].item()) == ref["n_dropped"]
+    # gathered rows are exact copies
+    xp = st["x_perm"][:R].cpu()
+    assert torch.equal(xp, x.cpu()[torch.from_numpy(ref["row_token"]).long()])
+
+
+@pytest.mark.parametrize("name", list(W.WORKLOADS))
+def test_permute_on_workload_routing(name):
+    b = B()
+    wl = W.get_workload(name)
+    _, idx_h, _ = oracle.route(host(wl.x()), wl.w_router().numpy(), bias_np(wl), wl.top_k)
+    cfg = cfg_of(wl)
+    idx = torch.from_numpy(idx_h).cuda()
+    st = {k: v for k, v in W.device.stage_tensors(wl).items() if k in
+          ("counts", "offsets", "row_token", "slot_row", "n_dropped")}
+    ws = torch.empty((b.permute_workspace_size(cfg),), dtype=torch.uint8, device="cuda")
+    b.permute(cfg, idx, None, st["counts"], st["offsets"], st["row_token"], st["slot_row"],
+              st["n_dropped"], None, ws)
+    torch.cuda.synchronize()
+    C = oracle.capacity_limit(wl.capacity_factor, wl.T, wl.top_k, wl.n_routed)
+    assert b.capacity(cfg) == (-1 if C is None else C)
+    ref = oracle.dispatch(idx_h, wl.n_routed, C)
+    R = int(ref["offsets"][-1])
+    assert np.array_equal(st["counts"].cpu().numpy(), ref["counts"])
+    assert np.array_equal(st["offsets"].cpu().numpy(), ref["offsets"])
+    assert np.array_equal(st["row_token"][:R].cpu().numpy(), ref["row_token"])
+    assert np.array_equal(st["slot_row"].cpu().numpy().reshape(wl.T, wl.top_k), ref["slot_row"])
+    assert int(st["n_dropped"].item()) == ref["n_dropped"]
+
+
+# ---------------------------------------------------------------------------
+# moe_grouped_ffn (fed oracle-permuted rows)
+# ---------------------------------------------------------------------------
+
+FFN_CASES = [
+    # (name, rows per group, d, f, dtype, expert_bias)
+    ("f32_ragged", [0, 5, 64, 65, 130, 1], 64, 48, "f32", True),
+    ("bf16_ragged", [0, 1, 127, 128, 129, 300, 0, 77], 128, 192, "bf16", False),
+    ("bf16_bias", [3, 200, 64], 64, 128, "bf16", True),
+    ("bf16_decode_tile", [1, 5, 0, 3, 5, 2, 4, 5, 5, 1], 256, 320, "bf16", False),
+    ("bf16_ntail", [40, 90], 320, 704, "bf16", False),
+]
+
+
+@pytest.mark.parametrize("case", FFN_CASES, ids=lambda c: c[0])
+def test_grouped_ffn_matches_oracle(case):
+    b = B()
+    name, rows, d, f, dtype, eb = case
+    G = len(rows)
+    R = int(sum(rows))
+    wl = W.custom_workload(name, T=max(R, 1), d_model=d, n_routed=G, top_k=1, n_shared=0, d_ff=f,
+                           dtype=dtype, expert_bias=eb)
+    cfg = cfg_of(wl)
+    x_rows = W.fill_normal((max(R, 1), d), 1.0, dtype, 3, 1, 0, "cuda")
+    w1, b1, w2, b2 = wl.stacked(False, "cuda")
+    offs = np.concatenate([[0], np.cumsum(rows)]).astype(np.int32)
+    offsets = torch.from_numpy(offs).cuda()
+    act = act_dtype(wl)
+    h = torch.zeros((max(R, 1), f), dtype=act, device="cuda")
+    y = torch.zeros((max(R, 1), d), dtype=act, device="cuda")
+    b.grouped_ffn(cfg, G, x_rows, offsets, R, w1, b1, w2, b2, h, y)
+    torch.cuda.synchronize()
+    routed, _ = providers_host(wl)
+    H, Y = oracle.grouped_ffn(host(x_rows), offs, routed, G)
+    assert rel_l2(host(h)[:R], H) <= TOL[dtype]
+    assert rel_l2(host(y)[:R], Y) <= TOL[dtype]
+
+
+# ---------------------------------------------------------------------------
+# moe_combine (fed oracle expert outputs and gates)
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("dtype,Ks,C", [("f32", 0, -1), ("bf16", 2, -1), ("bf16", 1, 2)])
+def test_combine_matches_oracle(dtype, Ks, C):
+    b = B()
+    T, N, K, d = 97, 12, 3, 128
+    wl = W.custom_workload("comb", T=T, d_model=d, n_routed=N, top_k=K, n_shared=Ks, d_ff=64,
+                           dtype=dtype)
+    idx_h = random_idx(T, N, K, 5)
+    disp = oracle.dispatch(idx_h, N, None if C < 0 else C)
+    R = int(disp["offsets"][-1])
+    rng = np.random.default_rng(9)
+    g = rng.random((T, K)) + 0.1
+    g = (g / g.sum(1, keepdims=True)).astype(np.float32)
+    act = act_dtype(wl)
+    y_rows = W.fill_normal((max(R, 1), d), 1.0, dtype, 1, 20, 0, "cuda")
+    shared = W.fill_normal((max(Ks, 1), T, d), 1.0, dtype, 1, 21, 0, "cuda") if Ks else None
+    y = torch.zeros((T, d), dtype=act, device="cuda")
+    cfg = cfg_of(wl, capacity=C)
+    b.combine(cfg, y_rows, torch.from_numpy(disp["slot_row"]).cuda(), torch.from_numpy(g).cuda(),
+              shared, y)
+    torch.cuda.synchronize()
+    ref = oracle.combine(host(y_rows)[:R], disp["slot_row"], g, None if shared is None else host(shared))
+    assert rel_l2(host(y), ref) <= TOL[dtype]
+
+
+# ---------------------------------------------------------------------------
+# moe_layer_forward: small layers compared in full
+# ---------------------------------------------------------------------------
+
+SMALL_LAYERS = [
+    W.get_workload("tiny_fp32"),
+    W.custom_workload("f32_shared_cap", T=150, d_model=64, n_routed=6, top_k=2, n_shared=2,
+                      d_ff=96, dtype="f32", expert_bias=True, capacity_factor=1.0),
+    W.custom_workload("bf16_small", T=333, d_model=128, n_routed=16, top_k=4, n_shared=1,
+                      d_ff=256, dtype="bf16", router_bias="gauss", router_bias_var=0.5),
+    W.custom_workload("bf16_decode_like", T=64, d_model=256, n_routed=64, top_k=6, n_shared=1,
+                      d_ff=192, dtype="bf16", router_bias="zipf", zipf_s=1.1,
+                      capacity_factor=1.25),
+    W.custom_workload("bf16_K_eq_N", T=100, d_model=64, n_routed=4, top_k=4, n_shared=0,
+                      d_ff=128, dtype="bf16", expert_bias=True),
+    W.custom_workload("N1_K1", T=77, d_model=64, n_routed=1, top_k=1, n_shared=0, d_ff=64,
+                      dtype="f32", expert_bias=True),
+    W.custom_workload("T1", T=1, d_model=128, n_routed=8, top_k=2, n_shared=1, d_ff=128,
+                      dtype="bf16"),
+]
+
+
+def run_layer(wl):
+    dl = W.device.DeviceLayer(wl)
+    dl.forward()
+    torch.cuda.synchronize()
+    return dl
+
+
+@pytest.mark.parametrize("wl", SMALL_LAYERS, ids=lambda w: w.name)
+def test_layer_forward_matches_oracle(wl):
+    dl = run_layer(wl)
+    routed, shared = providers_host(wl)
+    ref = oracle.layer_forward(host(dl.x), wl.w_router().numpy(), bias_np(wl), routed, shared,
+                               top_k=wl.top_k, n_shared=wl.n_shared,
+                               capacity_factor=wl.capacity_factor)
+    assert np.array_equal(dl.topk_idx.cpu().numpy(), ref["topk_idx"])
+    assert np.array_equal(dl.counts.cpu().numpy(), ref["counts"])
+    assert np.abs(dl.topk_gate.cpu().numpy() - ref["gates"]).max() <= 1e-6
+    assert rel_l2(host(dl.y), ref["y"]) <= TOL[wl.dtype]
+
+
+def test_layer_forward_is_deterministic():
+    wl = SMALL_LAYERS[2]
+    dl = run_layer(wl)
+    y1 = dl.y.clone()
+    dl.y.zero_()
+    dl.forward()
+    torch.cuda.synchronize()
+    assert torch.equal(y1, dl.y)
+
+
+def test_layer_zero_capacity_gives_shared_only():
+    wl = SMALL_LAYERS[2]
+    b = B()
+    dl = W.device.DeviceLayer(wl)
+    dl.cfg = b.config(wl.T, wl.d_model, wl.n_routed, wl.top_k, wl.n_shared, wl.d_ff, wl.dtype,
+                      0.0, 0)
+    dl.forward()
+    torch.cuda.synchronize()
+    assert int(dl.counts.sum().item()) == 0
+    _, shared = providers_host(wl)
+    ref = sum(oracle.expert_ffn(host(dl.x), *shared(i)) for i in range(wl.n_shared))
+    assert rel_l2(host(dl.y), ref) <= TOL[wl.dtype]
+
+
+def test_layer_identical_experts():
+    wl = W.custom_workload("ident", T=130, d_model=128, n_routed=8, top_k=3, n_shared=0, d_ff=128,
+                           dtype="bf16")
+    dl = W.device.DeviceLayer(wl)
+    for t in (dl.w1, dl.w2):
+        t[1:].copy_(t[0:1].expand_as(t[1:]))
+    dl.forward()
+    torch.cuda.synchronize()
+    e0 = dl.expert_host(0)
+    ref = oracle.expert_ffn(host(dl.x), *e0)
+    assert rel_l2(host(dl.y), ref) <= TOL["bf16"]
+
+
+# ---------------------------------------------------------------------------
+# full-size workloads, in the launch configuration the benchmark times:
+# routing compared on every token, outputs on sampled tokens
+# ---------------------------------------------------------------------------
+
+SAMPLES = {"tiny_fp32": None, "mixtral_shape": 12, "deepseekmoe_fine": 24, "dsv3_prefill": 8,
+           "dsv3_decode": 16}
+
+
+@pytest.mark.parametrize("name", list(W.WORKLOADS))
+def test_full_size_workload(name):
+    wl = W.get_workload(name)
+    print(f"[full-size] {name}: T={wl.T} d={wl.d_model} N={wl.n_routed} K={wl.top_k} "
+          f"Ks={wl.n_shared} f={wl.d_ff}", flush=True)
+    dl = run_layer(wl)
+    n = SAMPLES[name]
+    rng = np.random.default_rng(123)
+    toks = None if n is None else np.sort(rng.choice(wl.T, size=n, replace=False))
+    cache = {}
+
+    def routed(e):
+        if ("r", e) not in cache:
+            cache[("r", e)] = dl.expert_host(e)
+        return cache[("r", e)]
+
+    def shared(i):
+        return dl.expert_host(i, shared=True)
+
+    ref = oracle.layer_forward(host(dl.x), host(dl.w_router),
+                               None if dl.router_bias is None else host(dl.router_bias),
+                               routed, shared, top_k=wl.top_k, n_shared=wl.n_shared,
+                               capacity_factor=wl.capacity_factor, tokens=toks)
+    assert np.array_equal(dl.topk_idx.cpu().numpy(), ref["topk_idx"])
+    assert np.array_equal(dl.counts.cpu().numpy(), ref["counts"])
+    assert np.abs(dl.topk_gate.cpu().numpy() - ref["gates"]).max() <= 1e-6
+    y = host(dl.y) if toks is None else host(dl.y[torch.from_numpy(toks).long().cuda()])
+    err = rel_l2(y, ref["y"])
+    print(f"[full-size] {name}: rel_l2={err:.3e} kept={int(ref['offsets'][-1])} "
+          f"dropped={ref['n_dropped']}", flush=True)
+    assert err <= TOL[wl.dtype]
