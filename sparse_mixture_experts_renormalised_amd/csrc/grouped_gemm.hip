@@ -22,9 +22,9 @@
 // tiles and activation tiles in that XCD's L2.
 //
 // bf16 path: MFMA v_mfma_f32_32x32x16_bf16, fp32 accumulate.  Tiles go from
-// HBM to registers (16-byte loads, prefetched one K-step ahead) to LDS, double
-// buffered, with an XOR swizzle of the 16-byte chunks so the fragment reads
-// of 32 rows hit distinct banks.  The weight tile is the MFMA's first operand,
+// HBM straight into LDS (global_load_lds, 16 bytes per lane, no staging
+// registers), double buffered, with an XOR swizzle of the 16-byte chunks so
+// the fragment reads of 32 rows hit distinct banks.  The weight tile is the MFMA's first operand,
 // so each lane ends up holding four consecutive output features of one row
 // and the epilogue writes 8-byte packed bf16 stores.
 //
@@ -180,30 +180,66 @@ __device__ __forceinline__ void decode_tile(int L, int total_m, int n_nt, int *m
 // ---------------------------------------------------------------------------
 // bf16 MFMA kernel
 // ---------------------------------------------------------------------------
-template <int A_CH, int B_CH, int BK>
-__device__ __forceinline__ void gload_tiles(u32x4_t (&ra)[A_CH], u32x4_t (&rb)[B_CH],
-                                            const uint16_t *const (&a_src)[A_CH],
-                                            const uint16_t *const (&b_src)[B_CH], int kb) {
-#pragma unroll
-  for (int i = 0; i < A_CH; ++i) ra[i] = *reinterpret_cast<const u32x4_t *>(a_src[i] + kb * BK);
-#pragma unroll
-  for (int i = 0; i < B_CH; ++i) rb[i] = *reinterpret_cast<const u32x4_t *>(b_src[i] + kb * BK);
+// One wave instruction moves 8 tile rows x 128 bytes straight from global
+// memory into LDS: lane L lands at byte 16*L of the 1 KB block, i.e. row L/8,
+// chunk position L%8.  Position p of row r must hold logical chunk p ^ (r%8)
+// (the XOR swizzle the fragment reads expect), so lane L fetches chunk
+// (L%8) ^ (L/8) of its row; the 128-byte row segment stays fully used.
+__device__ __forceinline__ void load_rows_to_lds(const uint16_t *src, uint16_t *lds_block) {
+  __builtin_amdgcn_global_load_lds(src, lds_block, 16, 0, 0);
 }
 
-// 16-byte chunk kc of tile row `row` lives at chunk position kc ^ (row & 7).
-template <int A_CH, int B_CH, int BM, int BK, int NT>
-__device__ __forceinline__ void lstore_tiles(uint16_t *stage, const u32x4_t (&ra)[A_CH],
-                                             const u32x4_t (&rb)[B_CH], int tid, int kc) {
-  uint16_t *sb = stage + BM * BK;
+// Issue the global->LDS loads of K-step kb into one stage.
+template <int A_INS, int B_INS, int NW, int BM, int BK>
+__device__ __forceinline__ void issue_stage(uint16_t *sa, const uint16_t *const (&a_src)[A_INS],
+                                            const uint16_t *const (&b_src)[B_INS], int kb,
+                                            int wave) {
+  uint16_t *sb = sa + BM * BK;
 #pragma unroll
-  for (int i = 0; i < A_CH; ++i) {
-    const int row = (tid >> 3) + i * (NT / 8);
-    *reinterpret_cast<u32x4_t *>(stage + row * BK + ((kc ^ (row & 7)) << 3)) = ra[i];
+  for (int j = 0; j < A_INS; ++j) load_rows_to_lds(a_src[j] + kb * BK, sa + (j * NW + wave) * 8 * BK);
+#pragma unroll
+  for (int j = 0; j < B_INS; ++j) load_rows_to_lds(b_src[j] + kb * BK, sb + (j * NW + wave) * 8 * BK);
+}
+
+// Fragments of one 16-wide K slice: lane l holds 8 consecutive k of row l%32
+// (k offset 8*(l/32)) for each 32-row block of the wave's rows.
+template <int TM, int TN, int BM, int BK, int WTM, int WTN>
+__device__ __forceinline__ void load_frags(const uint16_t *sa, bf16x8_t (&fa)[TM],
+                                           bf16x8_t (&fb)[TN], int ks, int wm, int wn,
+                                           int lane) {
+  const uint16_t *sb = sa + BM * BK;
+  const int c = ks * 2 + (lane >> 5);
+#pragma unroll
+  for (int mi = 0; mi < TM; ++mi) {
+    const int row = wm * WTM + mi * 32 + (lane & 31);
+    fa[mi] = *reinterpret_cast<const bf16x8_t *>(sa + row * BK + ((c ^ (row & 7)) << 3));
   }
 #pragma unroll
-  for (int i = 0; i < B_CH; ++i) {
-    const int row = (tid >> 3) + i * (NT / 8);
-    *reinterpret_cast<u32x4_t *>(sb + row * BK + ((kc ^ (row & 7)) << 3)) = rb[i];
+  for (int ni = 0; ni < TN; ++ni) {
+    const int row = wn * WTN + ni * 32 + (lane & 31);
+    fb[ni] = *reinterpret_cast<const bf16x8_t *>(sb + row * BK + ((c ^ (row & 7)) << 3));
+  }
+}
+
+// Multiply one staged K-step into the wave's accumulators.  The fragments of
+// slice ks+1 are read while the MFMAs of slice ks run (two register sets).
+template <int TM, int TN, int BM, int BK, int WTM, int WTN>
+__device__ __forceinline__ void mma_stage(const uint16_t *sa, f32x16_t (&acc)[TN][TM], int wm,
+                                          int wn, int lane) {
+  constexpr int NS = BK / 16;
+  bf16x8_t fa[2][TM], fb[2][TN];
+  load_frags<TM, TN, BM, BK, WTM, WTN>(sa, fa[0], fb[0], 0, wm, wn, lane);
+#pragma unroll
+  for (int ks = 0; ks < NS; ++ks) {
+    if (ks + 1 < NS)
+      load_frags<TM, TN, BM, BK, WTM, WTN>(sa, fa[(ks + 1) & 1], fb[(ks + 1) & 1], ks + 1, wm, wn,
+                                           lane);
+#pragma unroll
+    for (int ni = 0; ni < TN; ++ni)
+#pragma unroll
+      for (int mi = 0; mi < TM; ++mi)
+        acc[ni][mi] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[ks & 1][ni], fa[ks & 1][mi],
+                                                              acc[ni][mi], 0, 0, 0);
   }
 }
 
@@ -215,13 +251,17 @@ __global__ __launch_bounds__(WAVES_M *WAVES_N * 64) void grouped_gemm_bf16_kerne
   constexpr int WTN = BN / WAVES_N;      // output features per wave
   constexpr int TM = WTM / 32;
   constexpr int TN = WTN / 32;
-  constexpr int A_CH = BM * 8 / NT;      // 16-byte chunks per thread per stage
-  constexpr int B_CH = BN * 8 / NT;
+  constexpr int NW = NT / 64;
+  constexpr int A_INS = BM / 8 / NW;     // 8-row global->LDS loads per wave per stage
+  constexpr int B_INS = BN / 8 / NW;
   constexpr int STAGE = (BM + BN) * BK;  // bf16 elements per stage
   static_assert(WTM % 32 == 0 && WTN % 32 == 0, "wave tile must be MFMA-aligned");
-  static_assert((BM * 8) % NT == 0 && (BN * 8) % NT == 0, "chunks must divide evenly");
+  static_assert((BM / 8) % NW == 0 && (BN / 8) % NW == 0, "row blocks must divide evenly");
 
-  __shared__ __attribute__((aligned(16))) uint16_t s_tile[2 * STAGE];
+  // Two stages as distinct objects, so the compiler can tell the loads into
+  // one from the reads of the other and need not wait between them.
+  __shared__ __attribute__((aligned(16))) uint16_t s_st0[STAGE];
+  __shared__ __attribute__((aligned(16))) uint16_t s_st1[STAGE];
   __shared__ int s_pref[kMaxGroups + 1];
   __shared__ int s_tmp[NT / 64];
 
@@ -241,7 +281,8 @@ __global__ __launch_bounds__(WAVES_M *WAVES_N * 64) void grouped_gemm_bf16_kerne
   const int begin = xcd * part;
   const int end = min(total, begin + part);
   const int nk = a.K / BK;
-  const int kc = tid & 7;                 // this thread's 16-byte chunk column
+  const int lrow = lane >> 3;                       // row within an 8-row block
+  const int lchunk = (lane & 7) ^ lrow;             // logical chunk this lane fetches
 
   for (int L = begin + slot; L < end; L += nslots) {
     int mt, nt;
@@ -250,21 +291,19 @@ __global__ __launch_bounds__(WAVES_M *WAVES_N * 64) void grouped_gemm_bf16_kerne
     const TileView<uint16_t> v = tile_view<uint16_t>(a, g, mt - s_pref[g], BM);
     const int n0 = nt * BN;
 
-    const uint16_t *a_src[A_CH];
-    const uint16_t *b_src[B_CH];
+    const uint16_t *a_src[A_INS];
+    const uint16_t *b_src[B_INS];
 #pragma unroll
-    for (int i = 0; i < A_CH; ++i) {
-      const int row = (tid >> 3) + i * (NT / 8);
-      a_src[i] = a_row_ptr(a, v, v.row0 + row) + kc * 8;
+    for (int j = 0; j < A_INS; ++j) {
+      const int row = (j * NW + wave) * 8 + lrow;
+      a_src[j] = a_row_ptr(a, v, v.row0 + row) + lchunk * 8;
     }
 #pragma unroll
-    for (int i = 0; i < B_CH; ++i) {
-      int n = n0 + (tid >> 3) + i * (NT / 8);
+    for (int j = 0; j < B_INS; ++j) {
+      int n = n0 + (j * NW + wave) * 8 + lrow;
       if (n >= a.Nout) n = a.Nout - 1;
-      b_src[i] = v.W + static_cast<int64_t>(n) * a.K + kc * 8;
+      b_src[j] = v.W + static_cast<int64_t>(n) * a.K + lchunk * 8;
     }
-
-    u32x4_t ra[A_CH], rb[B_CH];
     f32x16_t acc[TN][TM];
 #pragma unroll
     for (int i = 0; i < TN; ++i)
@@ -273,72 +312,82 @@ __global__ __launch_bounds__(WAVES_M *WAVES_N * 64) void grouped_gemm_bf16_kerne
 #pragma unroll
         for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 
-    gload_tiles<A_CH, B_CH, BK>(ra, rb, a_src, b_src, 0);
-    lstore_tiles<A_CH, B_CH, BM, BK, NT>(s_tile, ra, rb, tid, kc);
+    // Two LDS stages: the loads of step kb+1 land in one while step kb is
+    // multiplied out of the other; the barrier at the end of each step both
+    // publishes the new stage and frees the old one.
+    issue_stage<A_INS, B_INS, NW, BM, BK>(s_st0, a_src, b_src, 0, wave);
     __syncthreads();
-    for (int kb = 0; kb < nk; ++kb) {
-      const int cur = kb & 1;
-      if (kb + 1 < nk) gload_tiles<A_CH, B_CH, BK>(ra, rb, a_src, b_src, kb + 1);
-      const uint16_t *sa = s_tile + cur * STAGE;
-      const uint16_t *sb = sa + BM * BK;
-#pragma unroll
-      for (int ks = 0; ks < BK / 16; ++ks) {
-        const int c = ks * 2 + (lane >> 5);
-        bf16x8_t fa[TM], fb[TN];
-#pragma unroll
-        for (int mi = 0; mi < TM; ++mi) {
-          const int row = wm * WTM + mi * 32 + (lane & 31);
-          fa[mi] = *reinterpret_cast<const bf16x8_t *>(sa + row * BK + ((c ^ (row & 7)) << 3));
-        }
-#pragma unroll
-        for (int ni = 0; ni < TN; ++ni) {
-          const int row = wn * WTN + ni * 32 + (lane & 31);
-          fb[ni] = *reinterpret_cast<const bf16x8_t *>(sb + row * BK + ((c ^ (row & 7)) << 3));
-        }
-#pragma unroll
-        for (int ni = 0; ni < TN; ++ni)
-#pragma unroll
-          for (int mi = 0; mi < TM; ++mi)
-            acc[ni][mi] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[ni], fa[mi], acc[ni][mi], 0, 0, 0);
-      }
-      if (kb + 1 < nk) lstore_tiles<A_CH, B_CH, BM, BK, NT>(s_tile + (cur ^ 1) * STAGE, ra, rb, tid, kc);
+    int kb = 0;
+    for (; kb + 1 < nk; kb += 2) {
+      issue_stage<A_INS, B_INS, NW, BM, BK>(s_st1, a_src, b_src, kb + 1, wave);
+      mma_stage<TM, TN, BM, BK, WTM, WTN>(s_st0, acc, wm, wn, lane);
+      __syncthreads();
+      if (kb + 2 < nk) issue_stage<A_INS, B_INS, NW, BM, BK>(s_st0, a_src, b_src, kb + 2, wave);
+      mma_stage<TM, TN, BM, BK, WTM, WTN>(s_st1, acc, wm, wn, lane);
+      __syncthreads();
+    }
+    if (kb < nk) {   // odd number of K-steps: the last one sits in stage 0
+      mma_stage<TM, TN, BM, BK, WTM, WTN>(s_st0, acc, wm, wn, lane);
       __syncthreads();
     }
 
-    // epilogue: acc[ni][mi][q*4 + j] holds feature n = base + q*8 + (lane>>5)*4 + j
-    // of row m = wm*WTM + mi*32 + (lane & 31)
+    // Epilogue through LDS: bias, SiLU and bf16 rounding per accumulator,
+    // into a [BM][BN] bf16 tile whose 16-byte chunks are XOR-swizzled by row
+    // (acc[ni][mi][q*4 + j] holds feature wn*WTN + ni*32 + q*8 + (lane/32)*4 + j
+    // of row wm*WTM + mi*32 + lane%32); then whole rows leave in 16-byte stores.
+    // Opaque copies of the lane coordinates keep the epilogue's address
+    // arithmetic below the K loop instead of live across it.
+    int el = lane, ewm = wm, ewn = wn, etid = tid;
+    asm volatile("" : "+v"(el), "+v"(etid), "+s"(ewm), "+s"(ewn));
+    constexpr int CH = BN / 8;                       // 16-byte chunks per tile row
+    constexpr int XM = (CH < 32 ? CH : 32) - 1;      // swizzle mask
+    // the C tile takes stage 0, spilling its second half of rows into stage 1
+    constexpr bool kSplitC = BM * BN > STAGE;
+    static_assert(!kSplitC || (BM * BN) / 2 <= STAGE, "C tile must fit in the LDS stages");
+#define MOE_CROW(r) ((kSplitC && (r) >= BM / 2) ? s_st1 + ((r) - BM / 2) * BN : s_st0 + (r) * BN)
 #pragma unroll
-    for (int mi = 0; mi < TM; ++mi) {
-      const int64_t r = v.row0 + wm * WTM + mi * 32 + (lane & 31);
-      if (r >= v.rows) continue;
-      uint16_t *out_row = v.C + (v.out_base + r) * a.Nout;
+    for (int ni = 0; ni < TN; ++ni) {
 #pragma unroll
-      for (int ni = 0; ni < TN; ++ni) {
+      for (int q = 0; q < 4; ++q) {
+        const int nl = ewn * WTN + ni * 32 + q * 8 + (el >> 5) * 4;
+        const int n = n0 + nl;
+        float bv[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+        if (v.bias && n < a.Nout) {
+          const uint2 bq = *reinterpret_cast<const uint2 *>(v.bias + n);
+          bv[0] = __uint_as_float(bq.x << 16);
+          bv[1] = __uint_as_float(bq.x & 0xFFFF0000u);
+          bv[2] = __uint_as_float(bq.y << 16);
+          bv[3] = __uint_as_float(bq.y & 0xFFFF0000u);
+        }
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const int n = n0 + wn * WTN + ni * 32 + q * 8 + (lane >> 5) * 4;
-          if (n >= a.Nout) continue;
+        for (int mi = 0; mi < TM; ++mi) {
+          const int ml = ewm * WTM + mi * 32 + (el & 31);
           float o[4];
 #pragma unroll
-          for (int j = 0; j < 4; ++j) o[j] = acc[ni][mi][q * 4 + j];
-          if (v.bias) {
-            const uint2 bq = *reinterpret_cast<const uint2 *>(v.bias + n);
-            o[0] += __uint_as_float(bq.x << 16);
-            o[1] += __uint_as_float(bq.x & 0xFFFF0000u);
-            o[2] += __uint_as_float(bq.y << 16);
-            o[3] += __uint_as_float(bq.y & 0xFFFF0000u);
-          }
-          if (EPI == kEpiBiasSilu) {
-#pragma unroll
-            for (int j = 0; j < 4; ++j) o[j] = silu(o[j]);
+          for (int j = 0; j < 4; ++j) {
+            o[j] = acc[ni][mi][q * 4 + j] + bv[j];
+            if (EPI == kEpiBiasSilu) o[j] = silu(o[j]);
           }
           uint2 packed;
           packed.x = f32_to_bf16(o[0]) | (static_cast<uint32_t>(f32_to_bf16(o[1])) << 16);
           packed.y = f32_to_bf16(o[2]) | (static_cast<uint32_t>(f32_to_bf16(o[3])) << 16);
-          *reinterpret_cast<uint2 *>(out_row + n) = packed;
+          const int pos = (nl >> 3) ^ (ml & XM);
+          *reinterpret_cast<uint2 *>(MOE_CROW(ml) + pos * 8 + ((nl >> 2) & 1) * 4) = packed;
         }
       }
     }
+    __syncthreads();
+    for (int i = etid; i < BM * CH; i += NT) {
+      const int r = i / CH, c = i % CH;
+      const int64_t row = v.row0 + r;
+      const int n = n0 + c * 8;
+      if (row < v.rows && n < a.Nout) {
+        const u32x4_t val = *reinterpret_cast<const u32x4_t *>(MOE_CROW(r) + ((c ^ (r & XM)) << 3));
+        *reinterpret_cast<u32x4_t *>(v.C + (v.out_base + row) * a.Nout + n) = val;
+      }
+    }
+#undef MOE_CROW
+    __syncthreads();
   }
 }
 
@@ -497,6 +546,7 @@ hipError_t launch_grouped_gemm(bool bf16, const GemmGroups &g, Epilogue epi, hip
     const int64_t mean_rows = g.max_routed_rows / groups;
     if (mean_rows <= 48 && g.T_sh <= 256)
       return launch_bf16<32, 128, 1, 4, 8>(a, g, epi, 2, s);
+    if (mean_rows >= 384) return launch_bf16<256, 256, 2, 2, 4>(a, g, epi, 1, s);
     return launch_bf16<128, 128, 2, 2, 8>(a, g, epi, 2, s);
   }
   const unsigned grid = persistent_grid(tiles_upper_bound(g, 64, 64), 4);
