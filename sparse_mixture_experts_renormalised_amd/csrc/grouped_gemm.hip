@@ -392,6 +392,270 @@ __global__ __launch_bounds__(WAVES_M *WAVES_N * 64) void grouped_gemm_bf16_kerne
 }
 
 // ---------------------------------------------------------------------------
+// bf16 MFMA kernel, deep pipeline: 256x256 tiles, four 128x128 wave tiles,
+// K-steps of 32 in four LDS stages (32 KB each), loads issued three steps
+// ahead.  Each step ends with a wait for just the stage needed next
+// (s_waitcnt vmcnt(N) on this wave's own loads) and a plain s_barrier, so the
+// loads of the two younger stages stay in flight across it.
+// ---------------------------------------------------------------------------
+namespace deep {
+constexpr int BM = 256, BN = 256, BK = 32, NT = 256, NW = 4, WTM = 128, WTN = 128;
+constexpr int TM = WTM / 32, TN = WTN / 32;
+constexpr int ROWS_PER_INS = 16;                       // 1 KB per wave instruction
+constexpr int A_INS = BM / ROWS_PER_INS / NW;          // 4
+constexpr int B_INS = BN / ROWS_PER_INS / NW;          // 4
+constexpr int LOADS_PER_STAGE = A_INS + B_INS;         // per wave
+constexpr int STAGE = (BM + BN) * BK;                  // 16384 bf16 = 32 KB
+static_assert(STAGE == 64 * BN, "each stage holds 64 rows of the C tile");
+
+// 64-byte rows, 4 chunks of 16 B; chunk c of row r sits at c ^ ((r >> 1) & 3),
+// which keeps 8 consecutive rows read at one logical chunk on distinct banks.
+__device__ __forceinline__ int pos(int r, int c) { return c ^ ((r >> 1) & 3); }
+
+// LDS byte address of a __shared__ object (wave-uniform).
+__device__ __forceinline__ uint32_t lds_addr(const void *p) {
+  return static_cast<uint32_t>(
+      reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) const void *)p));
+}
+
+// One wave-wide LDS DMA (64 lanes x 16 B) written as inline assembly, so the
+// compiler does not treat every later LDS read as a possible alias of it and
+// drain all loads in flight; the wait before each barrier covers it instead.
+// M0 carries the LDS byte address of the 1 KB block (wave-uniform).
+__device__ __forceinline__ void dma16(const uint16_t *src, uint32_t m0) {
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+               :
+               : "v"(src), "s"(m0)
+               : "memory", "m0");
+}
+
+// Loads of K-step kb into the stage at LDS byte address `stage` (A rows first,
+// then B rows; 16 rows of 64 B per instruction).
+__device__ __forceinline__ void issue(uint32_t stage, const uint16_t *const (&a_src)[A_INS],
+                                      const uint16_t *const (&b_src)[B_INS], int kb, int wave) {
+  constexpr uint32_t kBlock = ROWS_PER_INS * BK * 2;   // bytes per instruction
+#pragma unroll
+  for (int j = 0; j < A_INS; ++j)
+    dma16(a_src[j] + kb * BK, stage + (j * NW + wave) * kBlock);
+#pragma unroll
+  for (int j = 0; j < B_INS; ++j)
+    dma16(b_src[j] + kb * BK, stage + BM * BK * 2 + (j * NW + wave) * kBlock);
+}
+
+// Fragments of one K-step (two 16-wide slices): lane l holds 8 consecutive k
+// of row l%32 of each 32-row block (k offset 8*(l/32) within the slice).
+struct Frags {
+  bf16x8_t a[2][TM];
+  bf16x8_t b[2][TN];
+};
+
+__device__ __forceinline__ void read_frags(const uint16_t *sa, Frags &f, int wm, int wn, int lane) {
+  const uint16_t *sb = sa + BM * BK;
+#pragma unroll
+  for (int ks = 0; ks < BK / 16; ++ks) {
+    const int c = ks * 2 + (lane >> 5);
+#pragma unroll
+    for (int mi = 0; mi < TM; ++mi) {
+      const int row = wm * WTM + mi * 32 + (lane & 31);
+      f.a[ks][mi] = *reinterpret_cast<const bf16x8_t *>(sa + row * BK + (pos(row, c) << 3));
+    }
+#pragma unroll
+    for (int ni = 0; ni < TN; ++ni) {
+      const int row = wn * WTN + ni * 32 + (lane & 31);
+      f.b[ks][ni] = *reinterpret_cast<const bf16x8_t *>(sb + row * BK + (pos(row, c) << 3));
+    }
+  }
+}
+
+__device__ __forceinline__ void mfma_frags(const Frags &f, f32x16_t (&acc)[TN][TM]) {
+#pragma unroll
+  for (int ks = 0; ks < BK / 16; ++ks)
+#pragma unroll
+    for (int ni = 0; ni < TN; ++ni)
+#pragma unroll
+      for (int mi = 0; mi < TM; ++mi)
+        acc[ni][mi] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.b[ks][ni], f.a[ks][mi], acc[ni][mi],
+                                                              0, 0, 0);
+}
+
+// Interleave the next step's 16 fragment reads with this step's 32 MFMAs.
+__device__ __forceinline__ void interleave_reads_with_mfma() {
+#pragma unroll
+  for (int i = 0; i < (BK / 16) * (TM + TN); ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);   // 2 MFMA
+    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // 1 DS read
+  }
+}
+
+// Wait until at most N of this wave's loads are in flight and its LDS reads
+// are done, then meet the other waves.  The empty asm statements keep the
+// compiler from moving memory operations across the barrier.
+template <int N>
+__device__ __forceinline__ void wait_and_barrier() {
+  asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)" ::"n"(N) : "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+}  // namespace deep
+
+template <int EPI, int GM>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void grouped_gemm_bf16_deep_kernel(GemmArgs a) {
+  using namespace deep;
+  __shared__ __attribute__((aligned(16))) uint16_t s0[STAGE];
+  __shared__ __attribute__((aligned(16))) uint16_t s1[STAGE];
+  __shared__ __attribute__((aligned(16))) uint16_t s2[STAGE];
+  __shared__ __attribute__((aligned(16))) uint16_t s3[STAGE];
+  __shared__ int s_pref[kMaxGroups + 1];
+  __shared__ int s_tmp[NT / 64];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = uniform(tid >> 6);
+  const int wm = wave & 1, wn = wave >> 1;
+  const int n_groups = a.n_routed + a.n_shared;
+  const int total_m = build_tile_prefix<NT, BM>(a, s_pref, s_tmp);
+  const int n_nt = (a.Nout + BN - 1) / BN;
+  const int total = total_m * n_nt;
+  const int xcd = blockIdx.x % kXcds;
+  const int slot = blockIdx.x / kXcds;
+  const int nslots = gridDim.x / kXcds;
+  const int part = (total + kXcds - 1) / kXcds;
+  const int begin = xcd * part;
+  const int end = min(total, begin + part);
+  const int nk = a.K / BK;                     // multiple of 2 (K % 64 == 0)
+  const int lrow = lane >> 2;                  // row within a 16-row block
+  const int lchunk = (lane & 3) ^ ((lane >> 3) & 3);
+  const uint32_t a0 = uniform(static_cast<int>(lds_addr(s0)));
+  const uint32_t a1 = uniform(static_cast<int>(lds_addr(s1)));
+  const uint32_t a2 = uniform(static_cast<int>(lds_addr(s2)));
+  const uint32_t a3 = uniform(static_cast<int>(lds_addr(s3)));
+
+  for (int L = begin + slot; L < end; L += nslots) {
+    int mt, nt;
+    decode_tile<GM>(L, total_m, n_nt, &mt, &nt);
+    const int g = find_group(s_pref, n_groups, mt);
+    const TileView<uint16_t> v = tile_view<uint16_t>(a, g, mt - s_pref[g], BM);
+    const int n0 = nt * BN;
+    const uint16_t *a_src[A_INS];
+    const uint16_t *b_src[B_INS];
+#pragma unroll
+    for (int j = 0; j < A_INS; ++j)
+      a_src[j] = a_row_ptr(a, v, v.row0 + (j * NW + wave) * ROWS_PER_INS + lrow) + lchunk * 8;
+#pragma unroll
+    for (int j = 0; j < B_INS; ++j) {
+      int n = n0 + (j * NW + wave) * ROWS_PER_INS + lrow;
+      if (n >= a.Nout) n = a.Nout - 1;
+      b_src[j] = v.W + static_cast<int64_t>(n) * a.K + lchunk * 8;
+    }
+    f32x16_t acc[TN][TM];
+#pragma unroll
+    for (int i = 0; i < TN; ++i)
+#pragma unroll
+      for (int j = 0; j < TM; ++j)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+
+    // Schedule of step kb (stage kb%4 holds step kb, its fragments are in
+    // registers already): barrier (step kb+1 has landed, every wave has read
+    // stage kb%4), issue step kb+4 into stage kb%4, then read step kb+1's
+    // fragments from stage (kb+1)%4 while the MFMAs of step kb run.
+    Frags f0, f1;
+    issue(a0, a_src, b_src, 0, wave);
+    if (nk > 1) issue(a1, a_src, b_src, 1, wave);
+    if (nk > 2) issue(a2, a_src, b_src, 2, wave);
+    if (nk > 3) issue(a3, a_src, b_src, 3, wave);
+    if (nk > 3) wait_and_barrier<3 * LOADS_PER_STAGE>();
+    else wait_and_barrier<0>();
+    read_frags(s0, f0, wm, wn, lane);
+
+#define MOE_DEEP_FULL(DMA_AT, NEXT_STAGE, FCUR, FNXT, KB)                                     \
+    {                                                                                        \
+      wait_and_barrier<2 * LOADS_PER_STAGE>();                                               \
+      issue(DMA_AT, a_src, b_src, (KB) + 4, wave);                                           \
+      read_frags(NEXT_STAGE, FNXT, wm, wn, lane);                                            \
+      mfma_frags(FCUR, acc);                                                                 \
+      interleave_reads_with_mfma();                                                          \
+    }
+    int kb = 0;
+    for (; kb + 7 < nk; kb += 4) {
+      MOE_DEEP_FULL(a0, s1, f0, f1, kb)
+      MOE_DEEP_FULL(a1, s2, f1, f0, kb + 1)
+      MOE_DEEP_FULL(a2, s3, f0, f1, kb + 2)
+      MOE_DEEP_FULL(a3, s0, f1, f0, kb + 3)
+    }
+#undef MOE_DEEP_FULL
+    // tail: the last steps, with every wait covering all loads in flight
+#define MOE_DEEP_TAIL(DMA_AT, NEXT_STAGE, FCUR, FNXT, KB)                                     \
+    {                                                                                        \
+      const int kb_ = (KB);                                                                  \
+      wait_and_barrier<0>();                                                                 \
+      if (kb_ + 4 < nk) issue(DMA_AT, a_src, b_src, kb_ + 4, wave);                          \
+      if (kb_ + 1 < nk) read_frags(NEXT_STAGE, FNXT, wm, wn, lane);                          \
+      mfma_frags(FCUR, acc);                                                                 \
+    }
+    for (; kb < nk; kb += 4) {
+      MOE_DEEP_TAIL(a0, s1, f0, f1, kb)
+      if (kb + 1 < nk) MOE_DEEP_TAIL(a1, s2, f1, f0, kb + 1)
+      if (kb + 2 < nk) MOE_DEEP_TAIL(a2, s3, f0, f1, kb + 2)
+      if (kb + 3 < nk) MOE_DEEP_TAIL(a3, s0, f1, f0, kb + 3)
+    }
+#undef MOE_DEEP_TAIL
+    __syncthreads();
+
+    // Epilogue through LDS: the C tile takes 64 rows per stage.
+    int el = lane, ewm = wm, ewn = wn, etid = tid;
+    asm volatile("" : "+v"(el), "+v"(etid), "+s"(ewm), "+s"(ewn));
+    constexpr int CH = BN / 8;
+#define MOE_DEEP_CROW(r)                                                                      \
+    (((r) >> 6) == 0 ? s0 : ((r) >> 6) == 1 ? s1 : ((r) >> 6) == 2 ? s2 : s3) + ((r) & 63) * BN
+#pragma unroll
+    for (int ni = 0; ni < TN; ++ni) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int nl = ewn * WTN + ni * 32 + q * 8 + (el >> 5) * 4;
+        const int n = n0 + nl;
+        float bv[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+        if (v.bias && n < a.Nout) {
+          const uint2 bq = *reinterpret_cast<const uint2 *>(v.bias + n);
+          bv[0] = __uint_as_float(bq.x << 16);
+          bv[1] = __uint_as_float(bq.x & 0xFFFF0000u);
+          bv[2] = __uint_as_float(bq.y << 16);
+          bv[3] = __uint_as_float(bq.y & 0xFFFF0000u);
+        }
+#pragma unroll
+        for (int mi = 0; mi < TM; ++mi) {
+          const int ml = ewm * WTM + mi * 32 + (el & 31);
+          float o[4];
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            o[j] = acc[ni][mi][q * 4 + j] + bv[j];
+            if (EPI == kEpiBiasSilu) o[j] = silu(o[j]);
+          }
+          uint2 packed;
+          packed.x = f32_to_bf16(o[0]) | (static_cast<uint32_t>(f32_to_bf16(o[1])) << 16);
+          packed.y = f32_to_bf16(o[2]) | (static_cast<uint32_t>(f32_to_bf16(o[3])) << 16);
+          const int p = (nl >> 3) ^ (ml & 31);
+          *reinterpret_cast<uint2 *>(MOE_DEEP_CROW(ml) + p * 8 + ((nl >> 2) & 1) * 4) = packed;
+        }
+      }
+    }
+    __syncthreads();
+    for (int i = etid; i < BM * CH; i += NT) {
+      const int r = i / CH, c = i % CH;
+      const int64_t row = v.row0 + r;
+      const int n = n0 + c * 8;
+      if (row < v.rows && n < a.Nout) {
+        const u32x4_t val = *reinterpret_cast<const u32x4_t *>(MOE_DEEP_CROW(r) + ((c ^ (r & 31)) << 3));
+        *reinterpret_cast<u32x4_t *>(v.C + (v.out_base + row) * a.Nout + n) = val;
+      }
+    }
+#undef MOE_DEEP_CROW
+    __syncthreads();
+  }
+}
+
+// ---------------------------------------------------------------------------
 // fp32 VALU kernel (also accepts bf16 operands): 64x64 tiles, 256 threads
 // ---------------------------------------------------------------------------
 template <typename TA, int EPI>
@@ -534,6 +798,16 @@ hipError_t launch_bf16(const GemmArgs &a, const GemmGroups &g, Epilogue epi, int
   return hipGetLastError();
 }
 
+template <int GM>
+hipError_t launch_bf16_deep(const GemmArgs &a, const GemmGroups &g, Epilogue epi, hipStream_t s) {
+  const unsigned grid = persistent_grid(tiles_upper_bound(g, 256, 256), 1);
+  if (epi == kEpiBiasSilu)
+    hipLaunchKernelGGL((grouped_gemm_bf16_deep_kernel<kEpiBiasSilu, GM>), dim3(grid), dim3(256), 0, s, a);
+  else
+    hipLaunchKernelGGL((grouped_gemm_bf16_deep_kernel<kEpiBias, GM>), dim3(grid), dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
 }  // namespace
 
 hipError_t launch_grouped_gemm(bool bf16, const GemmGroups &g, Epilogue epi, hipStream_t s) {
@@ -546,7 +820,7 @@ hipError_t launch_grouped_gemm(bool bf16, const GemmGroups &g, Epilogue epi, hip
     const int64_t mean_rows = g.max_routed_rows / groups;
     if (mean_rows <= 48 && g.T_sh <= 256)
       return launch_bf16<32, 128, 1, 4, 8>(a, g, epi, 2, s);
-    if (mean_rows >= 384) return launch_bf16<256, 256, 2, 2, 4>(a, g, epi, 1, s);
+    if (mean_rows >= 384) return launch_bf16_deep<8>(a, g, epi, s);
     return launch_bf16<128, 128, 2, 2, 8>(a, g, epi, 2, s);
   }
   const unsigned grid = persistent_grid(tiles_upper_bound(g, 64, 64), 4);
