@@ -656,6 +656,246 @@ void grouped_gemm_bf16_deep_kernel(GemmArgs a) {
 }
 
 // ---------------------------------------------------------------------------
+// bf16 MFMA kernel, register-staged pipeline: 256x256 tiles, four 128x128
+// wave tiles, one LDS buffer of one 64-wide K-step.  Global loads run two
+// K-steps ahead into registers; each step's fragments (all four 16-wide
+// slices) are read from LDS into registers once, so the MFMAs of step kb
+// overlap the LDS writes and global loads of the following steps and the
+// fragment reads of step kb+1.
+// ---------------------------------------------------------------------------
+namespace rs {
+constexpr int BM = 256, BN = 256, BK = 64, NT = 256, WTM = 128, WTN = 128;
+constexpr int TM = WTM / 32, TN = WTN / 32, NS = BK / 16;
+constexpr int A_CH = BM * 8 / NT, B_CH = BN * 8 / NT;   // 16-byte chunks per thread
+constexpr int TILE = (BM + BN) * BK;                    // bf16 elements in LDS
+
+struct Frags {
+  bf16x8_t a[NS][TM];
+  bf16x8_t b[NS][TN];
+};
+
+__device__ __forceinline__ void gload(u32x4_t (&ra)[A_CH], u32x4_t (&rb)[B_CH],
+                                      const uint16_t *const (&a_src)[A_CH],
+                                      const uint16_t *const (&b_src)[B_CH], int kb) {
+#pragma unroll
+  for (int i = 0; i < A_CH; ++i) ra[i] = *reinterpret_cast<const u32x4_t *>(a_src[i] + kb * BK);
+#pragma unroll
+  for (int i = 0; i < B_CH; ++i) rb[i] = *reinterpret_cast<const u32x4_t *>(b_src[i] + kb * BK);
+}
+
+// chunk kc of tile row r at chunk position kc ^ ((r / 2) % 8) of its 128-byte
+// row: with 64 four-byte banks serving 16 lanes of 16 bytes at a time, the
+// 16 rows read together (same logical chunk) then cover all banks once.
+__device__ __forceinline__ int swz(int r, int c) { return c ^ ((r >> 1) & 7); }
+
+__device__ __forceinline__ void lstore(uint16_t *tile, const u32x4_t (&ra)[A_CH],
+                                       const u32x4_t (&rb)[B_CH], int tid) {
+  const int kc = tid & 7;
+#pragma unroll
+  for (int i = 0; i < A_CH; ++i) {
+    const int row = (tid >> 3) + i * (NT / 8);
+    *reinterpret_cast<u32x4_t *>(tile + row * BK + (swz(row, kc) << 3)) = ra[i];
+  }
+#pragma unroll
+  for (int i = 0; i < B_CH; ++i) {
+    const int row = (tid >> 3) + i * (NT / 8);
+    *reinterpret_cast<u32x4_t *>(tile + BM * BK + row * BK + (swz(row, kc) << 3)) = rb[i];
+  }
+}
+
+__device__ __forceinline__ void read_frags(const uint16_t *tile, Frags &f, int wm, int wn,
+                                           int lane) {
+#pragma unroll
+  for (int ks = 0; ks < NS; ++ks) {
+    const int c = ks * 2 + (lane >> 5);
+#pragma unroll
+    for (int mi = 0; mi < TM; ++mi) {
+      const int row = wm * WTM + mi * 32 + (lane & 31);
+      f.a[ks][mi] = *reinterpret_cast<const bf16x8_t *>(tile + row * BK + (swz(row, c) << 3));
+    }
+#pragma unroll
+    for (int ni = 0; ni < TN; ++ni) {
+      const int row = wn * WTN + ni * 32 + (lane & 31);
+      f.b[ks][ni] =
+          *reinterpret_cast<const bf16x8_t *>(tile + BM * BK + row * BK + (swz(row, c) << 3));
+    }
+  }
+}
+
+__device__ __forceinline__ void mfma_all(const Frags &f, f32x16_t (&acc)[TN][TM]) {
+#pragma unroll
+  for (int ks = 0; ks < NS; ++ks)
+#pragma unroll
+    for (int ni = 0; ni < TN; ++ni)
+#pragma unroll
+      for (int mi = 0; mi < TM; ++mi)
+        acc[ni][mi] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.b[ks][ni], f.a[ks][mi], acc[ni][mi],
+                                                              0, 0, 0);
+}
+
+// Instruction order of one steady-state step (64 MFMAs): each global load
+// and LDS write shares a slot with three MFMAs, then two fragment reads
+// precede each of the last sixteen MFMAs.
+__device__ __forceinline__ void schedule_step() {
+#pragma unroll
+  for (int i = 0; i < A_CH + B_CH; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);   // DS write
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA
+    __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);   // VMEM read
+    __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);   // MFMA
+  }
+#pragma unroll
+  for (int i = 0; i < NS * (TM + TN) / 2; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);   // DS read
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA
+  }
+}
+// Workgroup barrier that also waits for this wave's LDS operations.  As an
+// asm statement it orders memory operations but lets MFMAs move across it,
+// so a whole K-step stays one scheduling region.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+}  // namespace rs
+
+template <int EPI, int GM>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void grouped_gemm_bf16_rs_kernel(GemmArgs a) {
+  using namespace rs;
+  __shared__ __attribute__((aligned(16))) uint16_t s_tile[TILE];
+  __shared__ int s_pref[kMaxGroups + 1];
+  __shared__ int s_tmp[NT / 64];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = uniform(tid >> 6);
+  const int wm = wave & 1, wn = wave >> 1;
+  const int n_groups = a.n_routed + a.n_shared;
+  const int total_m = build_tile_prefix<NT, BM>(a, s_pref, s_tmp);
+  const int n_nt = (a.Nout + BN - 1) / BN;
+  const int total = total_m * n_nt;
+  const int xcd = blockIdx.x % kXcds;
+  const int slot = blockIdx.x / kXcds;
+  const int nslots = gridDim.x / kXcds;
+  const int part = (total + kXcds - 1) / kXcds;
+  const int begin = xcd * part;
+  const int end = min(total, begin + part);
+  const int nk = a.K / BK;
+  const int kc = tid & 7;
+
+  for (int L = begin + slot; L < end; L += nslots) {
+    int mt, nt;
+    decode_tile<GM>(L, total_m, n_nt, &mt, &nt);
+    const int g = find_group(s_pref, n_groups, mt);
+    const TileView<uint16_t> v = tile_view<uint16_t>(a, g, mt - s_pref[g], BM);
+    const int n0 = nt * BN;
+    const uint16_t *a_src[A_CH];
+    const uint16_t *b_src[B_CH];
+#pragma unroll
+    for (int i = 0; i < A_CH; ++i)
+      a_src[i] = a_row_ptr(a, v, v.row0 + (tid >> 3) + i * (NT / 8)) + kc * 8;
+#pragma unroll
+    for (int i = 0; i < B_CH; ++i) {
+      int n = n0 + (tid >> 3) + i * (NT / 8);
+      if (n >= a.Nout) n = a.Nout - 1;
+      b_src[i] = v.W + static_cast<int64_t>(n) * a.K + kc * 8;
+    }
+    f32x16_t acc[TN][TM];
+#pragma unroll
+    for (int i = 0; i < TN; ++i)
+#pragma unroll
+      for (int j = 0; j < TM; ++j)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+
+    u32x4_t ra[A_CH], rb[B_CH];
+    Frags f;
+    gload(ra, rb, a_src, b_src, 0);
+    lstore(s_tile, ra, rb, tid);
+    if (nk > 1) gload(ra, rb, a_src, b_src, 1);
+    __syncthreads();
+    read_frags(s_tile, f, wm, wn, lane);
+    __builtin_amdgcn_sched_barrier(0);
+    // steady state (no branches, so each step is one scheduling region)
+    int kb = 0;
+    for (; kb + 2 < nk; ++kb) {
+      lds_barrier();                        // every wave has its fragments of step kb
+      lstore(s_tile, ra, rb, tid);          // step kb+1 into LDS
+      gload(ra, rb, a_src, b_src, kb + 2);  // step kb+2 into registers
+      mfma_all(f, acc);                     // step kb
+      lds_barrier();                        // step kb+1 is in LDS
+      read_frags(s_tile, f, wm, wn, lane);
+      schedule_step();
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    if (kb + 1 < nk) {                      // step nk-2: nothing left to load
+      lds_barrier();
+      lstore(s_tile, ra, rb, tid);
+      mfma_all(f, acc);
+      lds_barrier();
+      read_frags(s_tile, f, wm, wn, lane);
+    }
+    mfma_all(f, acc);                       // last step
+    __syncthreads();
+
+    // Epilogue through LDS in two passes of 128 rows (the tile buffer holds
+    // 128 x 256 bf16): in pass p every wave stores its row blocks mi = 2p,
+    // 2p+1, so all four waves work in both passes.
+    int el = lane, ewm = wm, ewn = wn, etid = tid;
+    asm volatile("" : "+v"(el), "+v"(etid), "+s"(ewm), "+s"(ewn));
+    constexpr int CH = BN / 8;
+    static_assert(TILE >= 128 * BN, "128 C-tile rows must fit");
+#pragma unroll
+    for (int pass = 0; pass < 2; ++pass) {
+#pragma unroll
+      for (int ni = 0; ni < TN; ++ni) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int nl = ewn * WTN + ni * 32 + q * 8 + (el >> 5) * 4;
+          const int n = n0 + nl;
+          float bv[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+          if (v.bias && n < a.Nout) {
+            const uint2 bq = *reinterpret_cast<const uint2 *>(v.bias + n);
+            bv[0] = __uint_as_float(bq.x << 16);
+            bv[1] = __uint_as_float(bq.x & 0xFFFF0000u);
+            bv[2] = __uint_as_float(bq.y << 16);
+            bv[3] = __uint_as_float(bq.y & 0xFFFF0000u);
+          }
+#pragma unroll
+          for (int mm = 0; mm < 2; ++mm) {
+            const int mi = pass * 2 + mm;
+            const int ml = ewm * 64 + mm * 32 + (el & 31);   // row within the pass
+            float o[4];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+              o[j] = acc[ni][mi][q * 4 + j] + bv[j];
+              if (EPI == kEpiBiasSilu) o[j] = silu_fast(o[j]);
+            }
+            uint2 packed;
+            packed.x = f32_to_bf16(o[0]) | (static_cast<uint32_t>(f32_to_bf16(o[1])) << 16);
+            packed.y = f32_to_bf16(o[2]) | (static_cast<uint32_t>(f32_to_bf16(o[3])) << 16);
+            const int p = (nl >> 3) ^ (ml & 31);
+            *reinterpret_cast<uint2 *>(s_tile + ml * BN + p * 8 + ((nl >> 2) & 1) * 4) = packed;
+          }
+        }
+      }
+      __syncthreads();
+      // LDS row ml of the pass is tile row (ml/64)*128 + pass*64 + ml%64
+      for (int i = etid; i < 128 * CH; i += NT) {
+        const int r = i / CH, c = i % CH;
+        const int64_t row = v.row0 + (r >> 6) * 128 + pass * 64 + (r & 63);
+        const int n = n0 + c * 8;
+        if (row < v.rows && n < a.Nout) {
+          const u32x4_t val = *reinterpret_cast<const u32x4_t *>(s_tile + r * BN + ((c ^ (r & 31)) << 3));
+          *reinterpret_cast<u32x4_t *>(v.C + (v.out_base + row) * a.Nout + n) = val;
+        }
+      }
+      __syncthreads();
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
 // fp32 VALU kernel (also accepts bf16 operands): 64x64 tiles, 256 threads
 // ---------------------------------------------------------------------------
 template <typename TA, int EPI>
@@ -808,6 +1048,16 @@ hipError_t launch_bf16_deep(const GemmArgs &a, const GemmGroups &g, Epilogue epi
   return hipGetLastError();
 }
 
+template <int GM>
+hipError_t launch_bf16_rs(const GemmArgs &a, const GemmGroups &g, Epilogue epi, hipStream_t s) {
+  const unsigned grid = persistent_grid(tiles_upper_bound(g, 256, 256), 1);
+  if (epi == kEpiBiasSilu)
+    hipLaunchKernelGGL((grouped_gemm_bf16_rs_kernel<kEpiBiasSilu, GM>), dim3(grid), dim3(256), 0, s, a);
+  else
+    hipLaunchKernelGGL((grouped_gemm_bf16_rs_kernel<kEpiBias, GM>), dim3(grid), dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
 }  // namespace
 
 hipError_t launch_grouped_gemm(bool bf16, const GemmGroups &g, Epilogue epi, hipStream_t s) {
@@ -820,7 +1070,7 @@ hipError_t launch_grouped_gemm(bool bf16, const GemmGroups &g, Epilogue epi, hip
     const int64_t mean_rows = g.max_routed_rows / groups;
     if (mean_rows <= 48 && g.T_sh <= 256)
       return launch_bf16<32, 128, 1, 4, 8>(a, g, epi, 2, s);
-    if (mean_rows >= 384) return launch_bf16_deep<8>(a, g, epi, s);
+    if (mean_rows >= 384) return launch_bf16_rs<8>(a, g, epi, s);
     return launch_bf16<128, 128, 2, 2, 8>(a, g, epi, 2, s);
   }
   const unsigned grid = persistent_grid(tiles_upper_bound(g, 64, 64), 4);

@@ -35,6 +35,12 @@ template <> struct Act<uint16_t> {
 
 __device__ __forceinline__ float silu(float z) { return z / (1.0f + __expf(-z)); }
 
+// SiLU with the hardware exp2 and reciprocal (about 1 ulp each in float32),
+// for epilogues that round to bfloat16 right after.
+__device__ __forceinline__ float silu_fast(float z) {
+  return z * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-z * 1.4426950408889634f));
+}
+
 __device__ __forceinline__ int uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
 
 }  // namespace moe

@@ -6,11 +6,9 @@
 // optional per-expert bias that is part of the logit.
 //
 // Fixed float32 order: for every (t, e) one fused multiply-add chain over k
-// ascending from +0, then the bias with one rounding.  Each lane owns whole
+// ascending from +0, then the bias with one rounding.  Each thread owns whole
 // logits, so no reduction tree is involved and the bits do not depend on the
-// launch shape.  A wave covers 64 tokens (one per lane) and ME experts; the
-// expert weights are wave-uniform and come in through scalar loads, so each
-// fused multiply-add is one VALU instruction with an SGPR operand.
+// launch shape.
 //
 // Top-K: one wave per token, N logits spread over the lanes' registers, K
 // rounds of a wave-wide arg-max on the key (logit desc, expert id asc).  Gates
@@ -21,63 +19,131 @@
 namespace moe {
 namespace {
 
-template <int ME, bool BF16>
+// Logits as a register-tiled product: a workgroup covers BT tokens x BE
+// experts, each thread MT tokens x ME experts; K advances in chunks of KC
+// staged through LDS (x converted to float32 exactly, layout [k][token] and
+// [k][expert] so each thread reads its MT / ME values as one vector).  Every
+// accumulator still sees its terms one at a time in ascending k.
+template <int BT, int BE, int MT, int ME, int KC, bool BF16>
 __global__ __launch_bounds__(256) void router_logits_kernel(
     const void *__restrict__ xv, const float *__restrict__ w, const float *__restrict__ bias,
     float *__restrict__ logits, int64_t T, int d, int N) {
-  const int wave = uniform(threadIdx.x >> 6);
-  const int lane = threadIdx.x & 63;
-  const int n_eg = N / ME;
-  const int64_t gw = static_cast<int64_t>(blockIdx.x) * 4 + wave;
-  const int64_t tg = gw / n_eg;
-  const int eg = static_cast<int>(gw - tg * n_eg);
-  const int64_t t0 = tg * kWave;
-  if (t0 >= T) return;
-  const int64_t t = t0 + lane;
-  const bool valid = t < T;
-  const int64_t tc = valid ? t : T - 1;
-  const float *__restrict__ wr = w + static_cast<int64_t>(eg) * ME * d;
+  constexpr int NTT = BT / MT;                  // thread columns over tokens
+  static_assert(NTT * (BE / ME) == 256, "256 threads per workgroup");
+  constexpr int XV = BF16 ? 8 : 4;              // x elements per 16-byte load
+  constexpr int X_LOADS = BT * KC / XV;         // 16-byte loads per x chunk
+  constexpr int W_LOADS = BE * KC / 4;          // 16-byte loads per W chunk
+  constexpr int XPT = (X_LOADS + 255) / 256;    // per thread
+  constexpr int WPT = (W_LOADS + 255) / 256;
+  __shared__ __attribute__((aligned(16))) float s_x[2][KC][BT];
+  __shared__ __attribute__((aligned(16))) float s_w[2][KC][BE];
 
-  float acc[ME];
-#pragma unroll
-  for (int e = 0; e < ME; ++e) acc[e] = 0.0f;
+  const int tid = threadIdx.x;
+  const int64_t t0 = static_cast<int64_t>(blockIdx.x) * BT;
+  const int e0 = blockIdx.y * BE;
+  const int tm = tid % NTT, te = tid / NTT;
 
-  if constexpr (BF16) {
-    const uint4 *xr = reinterpret_cast<const uint4 *>(static_cast<const uint16_t *>(xv) + tc * d);
-    for (int k8 = 0; k8 < (d >> 3); ++k8) {
-      const uint4 q = xr[k8];
-      float xs[8];
-      xs[0] = __uint_as_float(q.x << 16); xs[1] = __uint_as_float(q.x & 0xFFFF0000u);
-      xs[2] = __uint_as_float(q.y << 16); xs[3] = __uint_as_float(q.y & 0xFFFF0000u);
-      xs[4] = __uint_as_float(q.z << 16); xs[5] = __uint_as_float(q.z & 0xFFFF0000u);
-      xs[6] = __uint_as_float(q.w << 16); xs[7] = __uint_as_float(q.w & 0xFFFF0000u);
-      const float *wk = wr + (k8 << 3);
+  uint4 rx[XPT];
+  float4 rw[WPT];
+  auto gload = [&](int k0) {
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
-#pragma unroll
-        for (int e = 0; e < ME; ++e) acc[e] = __builtin_fmaf(xs[j], wk[e * d + j], acc[e]);
+    for (int i = 0; i < XPT; ++i) {
+      const int id = tid + i * 256;
+      if (id < X_LOADS) {
+        const int r = id / (KC / XV), c = id % (KC / XV);
+        int64_t t = t0 + r;
+        if (t >= T) t = T - 1;
+        if constexpr (BF16)
+          rx[i] = *reinterpret_cast<const uint4 *>(static_cast<const uint16_t *>(xv) + t * d + k0 + c * XV);
+        else
+          rx[i] = *reinterpret_cast<const uint4 *>(static_cast<const float *>(xv) + t * d + k0 + c * XV);
       }
     }
-  } else {
-    const float4 *xr = reinterpret_cast<const float4 *>(static_cast<const float *>(xv) + tc * d);
-    for (int k8 = 0; k8 < (d >> 3); ++k8) {
-      const float4 a = xr[2 * k8], b = xr[2 * k8 + 1];
-      const float xs[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
-      const float *wk = wr + (k8 << 3);
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
-#pragma unroll
-        for (int e = 0; e < ME; ++e) acc[e] = __builtin_fmaf(xs[j], wk[e * d + j], acc[e]);
+    for (int i = 0; i < WPT; ++i) {
+      const int id = tid + i * 256;
+      if (id < W_LOADS) {
+        const int r = id / (KC / 4), c = id % (KC / 4);
+        int e = e0 + r;
+        if (e >= N) e = N - 1;
+        rw[i] = *reinterpret_cast<const float4 *>(w + static_cast<int64_t>(e) * d + k0 + c * 4);
       }
     }
+  };
+  auto lstore = [&](int buf) {
+#pragma unroll
+    for (int i = 0; i < XPT; ++i) {
+      const int id = tid + i * 256;
+      if (id < X_LOADS) {
+        const int r = id / (KC / XV), c = id % (KC / XV);
+        if constexpr (BF16) {
+          const uint32_t q[4] = {rx[i].x, rx[i].y, rx[i].z, rx[i].w};
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            s_x[buf][c * 8 + 2 * j][r] = __uint_as_float(q[j] << 16);
+            s_x[buf][c * 8 + 2 * j + 1][r] = __uint_as_float(q[j] & 0xFFFF0000u);
+          }
+        } else {
+          s_x[buf][c * 4 + 0][r] = __uint_as_float(rx[i].x);
+          s_x[buf][c * 4 + 1][r] = __uint_as_float(rx[i].y);
+          s_x[buf][c * 4 + 2][r] = __uint_as_float(rx[i].z);
+          s_x[buf][c * 4 + 3][r] = __uint_as_float(rx[i].w);
+        }
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < WPT; ++i) {
+      const int id = tid + i * 256;
+      if (id < W_LOADS) {
+        const int r = id / (KC / 4), c = id % (KC / 4);
+        s_w[buf][c * 4 + 0][r] = rw[i].x;
+        s_w[buf][c * 4 + 1][r] = rw[i].y;
+        s_w[buf][c * 4 + 2][r] = rw[i].z;
+        s_w[buf][c * 4 + 3][r] = rw[i].w;
+      }
+    }
+  };
+
+  float acc[MT][ME];
+#pragma unroll
+  for (int i = 0; i < MT; ++i)
+#pragma unroll
+    for (int j = 0; j < ME; ++j) acc[i][j] = 0.0f;
+
+  const int nchunks = d / KC;
+  gload(0);
+  lstore(0);
+  __syncthreads();
+  for (int ch = 0; ch < nchunks; ++ch) {
+    const int buf = ch & 1;
+    if (ch + 1 < nchunks) gload((ch + 1) * KC);
+#pragma unroll
+    for (int k = 0; k < KC; ++k) {
+      float xs[MT], ws[ME];
+#pragma unroll
+      for (int i = 0; i < MT; ++i) xs[i] = s_x[buf][k][tm * MT + i];
+#pragma unroll
+      for (int j = 0; j < ME; ++j) ws[j] = s_w[buf][k][te * ME + j];
+#pragma unroll
+      for (int i = 0; i < MT; ++i)
+#pragma unroll
+        for (int j = 0; j < ME; ++j) acc[i][j] = __builtin_fmaf(xs[i], ws[j], acc[i][j]);
+    }
+    if (ch + 1 < nchunks) lstore(buf ^ 1);
+    __syncthreads();
   }
-  if (!valid) return;
-  float *out = logits + t * N + static_cast<int64_t>(eg) * ME;
 #pragma unroll
-  for (int e = 0; e < ME; ++e) {
-    float v = acc[e];
-    if (bias) v = v + bias[eg * ME + e];
-    out[e] = v;
+  for (int i = 0; i < MT; ++i) {
+    const int64_t t = t0 + tm * MT + i;
+    if (t >= T) continue;
+#pragma unroll
+    for (int j = 0; j < ME; ++j) {
+      const int e = e0 + te * ME + j;
+      if (e >= N) continue;
+      float v = acc[i][j];
+      if (bias) v = v + bias[e];
+      logits[t * N + e] = v;
+    }
   }
 }
 
@@ -139,32 +205,28 @@ __global__ __launch_bounds__(256) void topk_gates_kernel(const float *__restrict
 hipError_t launch_router_logits(bool bf16, const void *x, const float *w, const float *bias,
                                 float *logits, int64_t T, int d, int N, hipStream_t s) {
   if (T <= 0) return hipSuccess;
-  // experts per wave: keep at least ~2048 waves in flight when the shape allows
-  const int64_t tgroups = (T + kWave - 1) / kWave;
-  int me = 1;
-  for (int cand : {16, 8, 4, 2}) {
-    if (N % cand == 0 && tgroups * (N / cand) >= 2048) { me = cand; break; }
+  // Wide routers with many tokens: 64x64 blocks, 4x4 per thread (fewer LDS
+  // bytes per multiply-add).  Otherwise 64x8 blocks with two outputs per
+  // thread, so short batches and narrow routers still spread over the chip.
+  const bool wide = N >= 64 && T * static_cast<int64_t>(N) >= (int64_t(1) << 19);
+  const int64_t tb = (T + 63) / 64;
+  const int kc32 = d % 32 == 0;
+#define MOE_ROUTER_LAUNCH(BE, MT, ME, KC)                                                       \
+  {                                                                                             \
+    const dim3 grid(static_cast<unsigned>(tb), static_cast<unsigned>((N + BE - 1) / BE));       \
+    if (bf16)                                                                                   \
+      hipLaunchKernelGGL((router_logits_kernel<64, BE, MT, ME, KC, true>), grid, dim3(256), 0, \
+                         s, x, w, bias, logits, T, d, N);                                       \
+    else                                                                                        \
+      hipLaunchKernelGGL((router_logits_kernel<64, BE, MT, ME, KC, false>), grid, dim3(256), 0,\
+                         s, x, w, bias, logits, T, d, N);                                       \
   }
-  const int64_t waves = tgroups * (N / me);
-  const dim3 grid(static_cast<unsigned>((waves + 3) / 4)), block(256);
-#define MOE_ROUTER_CASE(ME)                                                                   \
-  case ME:                                                                                    \
-    if (bf16)                                                                                 \
-      hipLaunchKernelGGL((router_logits_kernel<ME, true>), grid, block, 0, s, x, w, bias,    \
-                         logits, T, d, N);                                                    \
-    else                                                                                      \
-      hipLaunchKernelGGL((router_logits_kernel<ME, false>), grid, block, 0, s, x, w, bias,   \
-                         logits, T, d, N);                                                    \
-    break;
-  switch (me) {
-    MOE_ROUTER_CASE(1)
-    MOE_ROUTER_CASE(2)
-    MOE_ROUTER_CASE(4)
-    MOE_ROUTER_CASE(8)
-    MOE_ROUTER_CASE(16)
-    default: return hipErrorInvalidValue;
+  if (wide) {
+    if (kc32) MOE_ROUTER_LAUNCH(64, 4, 4, 32) else MOE_ROUTER_LAUNCH(64, 4, 4, 16)
+  } else {
+    if (kc32) MOE_ROUTER_LAUNCH(8, 2, 1, 32) else MOE_ROUTER_LAUNCH(8, 2, 1, 16)
   }
-#undef MOE_ROUTER_CASE
+#undef MOE_ROUTER_LAUNCH
   return hipGetLastError();
 }
 
