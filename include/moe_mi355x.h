@@ -151,11 +151,19 @@ size_t moe_permute_workspace_size(const moe_config *cfg);
  *   w1 [G][f][d], b1 [G][f] or NULL, w2 [G][d][f], b2 [G][d] or NULL (act)
  *   h           [max_rows][f] act output (hidden activations)
  *   y_rows      [max_rows][d] act output
+ *   ws          optional device scratch of moe_grouped_ffn_workspace_size
+ *               bytes (NULL allowed); with it, products with too few row
+ *               blocks to fill the GPU are split along their reduction
+ *               dimension and the parts summed in a fixed order.  A non-NULL
+ *               ws smaller than that size is MOE_ERR_WORKSPACE.
  * Only cfg->d_model, cfg->d_ff and cfg->dtype are read.
  */
 int moe_grouped_ffn(const moe_config *cfg, int32_t n_groups, const void *x_rows,
                     const int32_t *offsets, int64_t max_rows, const void *w1, const void *b1,
-                    const void *w2, const void *b2, void *h, void *y_rows, void *stream);
+                    const void *w2, const void *b2, void *h, void *y_rows, void *ws,
+                    size_t ws_bytes, void *stream);
+size_t moe_grouped_ffn_workspace_size(const moe_config *cfg, int32_t n_groups,
+                                      int64_t max_rows);
 
 /*
  * moe_combine — y_t = sum_i S_i[t] + sum_{k: slot_row[t,k] >= 0}

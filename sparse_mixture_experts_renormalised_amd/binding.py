@@ -23,7 +23,7 @@ STATUS = {0: "ok", -1: "invalid argument", -2: "unsupported size", -3: "workspac
 
 # Symbols declared in include/moe_mi355x.h.
 EXPORTS = ("moe_route", "moe_permute", "moe_permute_workspace_size", "moe_grouped_ffn",
-           "moe_combine", "moe_layer_forward", "moe_layer_forward_events",
+           "moe_grouped_ffn_workspace_size", "moe_combine", "moe_layer_forward", "moe_layer_forward_events",
            "moe_layer_workspace_size", "moe_capacity", "moe_status_string", "moe_version")
 STAGES = ("router", "topk", "dispatch", "up", "down", "combine")
 
@@ -65,7 +65,8 @@ def lib():
             "moe_route": (I, [C, P, P, P, P, P, P, P]),
             "moe_permute": (I, [C, P, P, P, P, P, P, P, P, P, Z, P]),
             "moe_permute_workspace_size": (Z, [C]),
-            "moe_grouped_ffn": (I, [C, ctypes.c_int32, P, P, I64, P, P, P, P, P, P, P]),
+            "moe_grouped_ffn": (I, [C, ctypes.c_int32, P, P, I64, P, P, P, P, P, P, P, Z, P]),
+            "moe_grouped_ffn_workspace_size": (Z, [C, ctypes.c_int32, I64]),
             "moe_combine": (I, [C, P, P, P, P, P, P]),
             "moe_layer_forward": (I, [C, ctypes.POINTER(Weights), P, P, P, P, P, P, Z, P]),
             "moe_layer_forward_events": (I, [C, ctypes.POINTER(Weights), P, P, P, P, P, P, Z,
@@ -131,12 +132,18 @@ def permute(cfg: Config, topk_idx, x, counts, offsets, row_token, slot_row, n_dr
                                             _ptr(ws), nbytes, _stream(stream)))
 
 
+def grouped_ffn_workspace_size(cfg: Config, n_groups, max_rows) -> int:
+    return int(lib().moe_grouped_ffn_workspace_size(ctypes.byref(cfg), int(n_groups), int(max_rows)))
+
+
 def grouped_ffn(cfg: Config, n_groups, x_rows, offsets, max_rows, w1, b1, w2, b2, h, y_rows,
-                stream=None):
+                ws=None, stream=None):
+    nbytes = 0 if ws is None else ws.numel() * ws.element_size()
     _check("moe_grouped_ffn", lib().moe_grouped_ffn(ctypes.byref(cfg), int(n_groups), _ptr(x_rows),
                                                     _ptr(offsets), int(max_rows), _ptr(w1),
                                                     _ptr(b1), _ptr(w2), _ptr(b2), _ptr(h),
-                                                    _ptr(y_rows), _stream(stream)))
+                                                    _ptr(y_rows), _ptr(ws), nbytes,
+                                                    _stream(stream)))
 
 
 def combine(cfg: Config, y_rows, slot_row, topk_gate, shared_out, y, stream=None):

@@ -58,7 +58,16 @@ struct GemmArgs {
   int n_shared;
   int Nout;
   int K;
+  // Only groups whose row count lies in [cls_lo, cls_hi] get tiles, so two
+  // kernels can split one grouped product by group size.
+  int64_t cls_lo;
+  int64_t cls_hi;
 };
+
+__device__ __forceinline__ int64_t group_rows(const GemmArgs &a, int g) {
+  const int64_t rows = g < a.n_routed ? (a.offsets[g + 1] - a.offsets[g]) : a.T_sh;
+  return (rows >= a.cls_lo && rows <= a.cls_hi) ? rows : 0;
+}
 
 // Block-wide exclusive scan of one int per thread (NT threads, NT % 64 == 0).
 template <int NT>
@@ -91,16 +100,12 @@ __device__ int build_tile_prefix(const GemmArgs &a, int *s_pref, int *s_tmp) {
   const int g0 = threadIdx.x * per;
   const int g1 = min(g0 + per, n_groups);
   int local = 0;
-  for (int g = g0; g < g1; ++g) {
-    const int64_t rows = g < a.n_routed ? (a.offsets[g + 1] - a.offsets[g]) : a.T_sh;
-    local += static_cast<int>((rows + BM - 1) / BM);
-  }
+  for (int g = g0; g < g1; ++g) local += static_cast<int>((group_rows(a, g) + BM - 1) / BM);
   int total;
   int run = block_excl_scan<NT>(local, s_tmp, &total);
   for (int g = g0; g < g1; ++g) {
     s_pref[g] = run;
-    const int64_t rows = g < a.n_routed ? (a.offsets[g + 1] - a.offsets[g]) : a.T_sh;
-    run += static_cast<int>((rows + BM - 1) / BM);
+    run += static_cast<int>((group_rows(a, g) + BM - 1) / BM);
   }
   if (threadIdx.x == 0) s_pref[n_groups] = total;
   __syncthreads();
@@ -392,270 +397,6 @@ __global__ __launch_bounds__(WAVES_M *WAVES_N * 64) void grouped_gemm_bf16_kerne
 }
 
 // ---------------------------------------------------------------------------
-// bf16 MFMA kernel, deep pipeline: 256x256 tiles, four 128x128 wave tiles,
-// K-steps of 32 in four LDS stages (32 KB each), loads issued three steps
-// ahead.  Each step ends with a wait for just the stage needed next
-// (s_waitcnt vmcnt(N) on this wave's own loads) and a plain s_barrier, so the
-// loads of the two younger stages stay in flight across it.
-// ---------------------------------------------------------------------------
-namespace deep {
-constexpr int BM = 256, BN = 256, BK = 32, NT = 256, NW = 4, WTM = 128, WTN = 128;
-constexpr int TM = WTM / 32, TN = WTN / 32;
-constexpr int ROWS_PER_INS = 16;                       // 1 KB per wave instruction
-constexpr int A_INS = BM / ROWS_PER_INS / NW;          // 4
-constexpr int B_INS = BN / ROWS_PER_INS / NW;          // 4
-constexpr int LOADS_PER_STAGE = A_INS + B_INS;         // per wave
-constexpr int STAGE = (BM + BN) * BK;                  // 16384 bf16 = 32 KB
-static_assert(STAGE == 64 * BN, "each stage holds 64 rows of the C tile");
-
-// 64-byte rows, 4 chunks of 16 B; chunk c of row r sits at c ^ ((r >> 1) & 3),
-// which keeps 8 consecutive rows read at one logical chunk on distinct banks.
-__device__ __forceinline__ int pos(int r, int c) { return c ^ ((r >> 1) & 3); }
-
-// LDS byte address of a __shared__ object (wave-uniform).
-__device__ __forceinline__ uint32_t lds_addr(const void *p) {
-  return static_cast<uint32_t>(
-      reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) const void *)p));
-}
-
-// One wave-wide LDS DMA (64 lanes x 16 B) written as inline assembly, so the
-// compiler does not treat every later LDS read as a possible alias of it and
-// drain all loads in flight; the wait before each barrier covers it instead.
-// M0 carries the LDS byte address of the 1 KB block (wave-uniform).
-__device__ __forceinline__ void dma16(const uint16_t *src, uint32_t m0) {
-  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
-               :
-               : "v"(src), "s"(m0)
-               : "memory", "m0");
-}
-
-// Loads of K-step kb into the stage at LDS byte address `stage` (A rows first,
-// then B rows; 16 rows of 64 B per instruction).
-__device__ __forceinline__ void issue(uint32_t stage, const uint16_t *const (&a_src)[A_INS],
-                                      const uint16_t *const (&b_src)[B_INS], int kb, int wave) {
-  constexpr uint32_t kBlock = ROWS_PER_INS * BK * 2;   // bytes per instruction
-#pragma unroll
-  for (int j = 0; j < A_INS; ++j)
-    dma16(a_src[j] + kb * BK, stage + (j * NW + wave) * kBlock);
-#pragma unroll
-  for (int j = 0; j < B_INS; ++j)
-    dma16(b_src[j] + kb * BK, stage + BM * BK * 2 + (j * NW + wave) * kBlock);
-}
-
-// Fragments of one K-step (two 16-wide slices): lane l holds 8 consecutive k
-// of row l%32 of each 32-row block (k offset 8*(l/32) within the slice).
-struct Frags {
-  bf16x8_t a[2][TM];
-  bf16x8_t b[2][TN];
-};
-
-__device__ __forceinline__ void read_frags(const uint16_t *sa, Frags &f, int wm, int wn, int lane) {
-  const uint16_t *sb = sa + BM * BK;
-#pragma unroll
-  for (int ks = 0; ks < BK / 16; ++ks) {
-    const int c = ks * 2 + (lane >> 5);
-#pragma unroll
-    for (int mi = 0; mi < TM; ++mi) {
-      const int row = wm * WTM + mi * 32 + (lane & 31);
-      f.a[ks][mi] = *reinterpret_cast<const bf16x8_t *>(sa + row * BK + (pos(row, c) << 3));
-    }
-#pragma unroll
-    for (int ni = 0; ni < TN; ++ni) {
-      const int row = wn * WTN + ni * 32 + (lane & 31);
-      f.b[ks][ni] = *reinterpret_cast<const bf16x8_t *>(sb + row * BK + (pos(row, c) << 3));
-    }
-  }
-}
-
-__device__ __forceinline__ void mfma_frags(const Frags &f, f32x16_t (&acc)[TN][TM]) {
-#pragma unroll
-  for (int ks = 0; ks < BK / 16; ++ks)
-#pragma unroll
-    for (int ni = 0; ni < TN; ++ni)
-#pragma unroll
-      for (int mi = 0; mi < TM; ++mi)
-        acc[ni][mi] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.b[ks][ni], f.a[ks][mi], acc[ni][mi],
-                                                              0, 0, 0);
-}
-
-// Interleave the next step's 16 fragment reads with this step's 32 MFMAs.
-__device__ __forceinline__ void interleave_reads_with_mfma() {
-#pragma unroll
-  for (int i = 0; i < (BK / 16) * (TM + TN); ++i) {
-    __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);   // 2 MFMA
-    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // 1 DS read
-  }
-}
-
-// Wait until at most N of this wave's loads are in flight and its LDS reads
-// are done, then meet the other waves.  The empty asm statements keep the
-// compiler from moving memory operations across the barrier.
-template <int N>
-__device__ __forceinline__ void wait_and_barrier() {
-  asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)" ::"n"(N) : "memory");
-  __builtin_amdgcn_s_barrier();
-  asm volatile("" ::: "memory");
-}
-}  // namespace deep
-
-template <int EPI, int GM>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
-void grouped_gemm_bf16_deep_kernel(GemmArgs a) {
-  using namespace deep;
-  __shared__ __attribute__((aligned(16))) uint16_t s0[STAGE];
-  __shared__ __attribute__((aligned(16))) uint16_t s1[STAGE];
-  __shared__ __attribute__((aligned(16))) uint16_t s2[STAGE];
-  __shared__ __attribute__((aligned(16))) uint16_t s3[STAGE];
-  __shared__ int s_pref[kMaxGroups + 1];
-  __shared__ int s_tmp[NT / 64];
-
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = uniform(tid >> 6);
-  const int wm = wave & 1, wn = wave >> 1;
-  const int n_groups = a.n_routed + a.n_shared;
-  const int total_m = build_tile_prefix<NT, BM>(a, s_pref, s_tmp);
-  const int n_nt = (a.Nout + BN - 1) / BN;
-  const int total = total_m * n_nt;
-  const int xcd = blockIdx.x % kXcds;
-  const int slot = blockIdx.x / kXcds;
-  const int nslots = gridDim.x / kXcds;
-  const int part = (total + kXcds - 1) / kXcds;
-  const int begin = xcd * part;
-  const int end = min(total, begin + part);
-  const int nk = a.K / BK;                     // multiple of 2 (K % 64 == 0)
-  const int lrow = lane >> 2;                  // row within a 16-row block
-  const int lchunk = (lane & 3) ^ ((lane >> 3) & 3);
-  const uint32_t a0 = uniform(static_cast<int>(lds_addr(s0)));
-  const uint32_t a1 = uniform(static_cast<int>(lds_addr(s1)));
-  const uint32_t a2 = uniform(static_cast<int>(lds_addr(s2)));
-  const uint32_t a3 = uniform(static_cast<int>(lds_addr(s3)));
-
-  for (int L = begin + slot; L < end; L += nslots) {
-    int mt, nt;
-    decode_tile<GM>(L, total_m, n_nt, &mt, &nt);
-    const int g = find_group(s_pref, n_groups, mt);
-    const TileView<uint16_t> v = tile_view<uint16_t>(a, g, mt - s_pref[g], BM);
-    const int n0 = nt * BN;
-    const uint16_t *a_src[A_INS];
-    const uint16_t *b_src[B_INS];
-#pragma unroll
-    for (int j = 0; j < A_INS; ++j)
-      a_src[j] = a_row_ptr(a, v, v.row0 + (j * NW + wave) * ROWS_PER_INS + lrow) + lchunk * 8;
-#pragma unroll
-    for (int j = 0; j < B_INS; ++j) {
-      int n = n0 + (j * NW + wave) * ROWS_PER_INS + lrow;
-      if (n >= a.Nout) n = a.Nout - 1;
-      b_src[j] = v.W + static_cast<int64_t>(n) * a.K + lchunk * 8;
-    }
-    f32x16_t acc[TN][TM];
-#pragma unroll
-    for (int i = 0; i < TN; ++i)
-#pragma unroll
-      for (int j = 0; j < TM; ++j)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
-
-    // Schedule of step kb (stage kb%4 holds step kb, its fragments are in
-    // registers already): barrier (step kb+1 has landed, every wave has read
-    // stage kb%4), issue step kb+4 into stage kb%4, then read step kb+1's
-    // fragments from stage (kb+1)%4 while the MFMAs of step kb run.
-    Frags f0, f1;
-    issue(a0, a_src, b_src, 0, wave);
-    if (nk > 1) issue(a1, a_src, b_src, 1, wave);
-    if (nk > 2) issue(a2, a_src, b_src, 2, wave);
-    if (nk > 3) issue(a3, a_src, b_src, 3, wave);
-    if (nk > 3) wait_and_barrier<3 * LOADS_PER_STAGE>();
-    else wait_and_barrier<0>();
-    read_frags(s0, f0, wm, wn, lane);
-
-#define MOE_DEEP_FULL(DMA_AT, NEXT_STAGE, FCUR, FNXT, KB)                                     \
-    {                                                                                        \
-      wait_and_barrier<2 * LOADS_PER_STAGE>();                                               \
-      issue(DMA_AT, a_src, b_src, (KB) + 4, wave);                                           \
-      read_frags(NEXT_STAGE, FNXT, wm, wn, lane);                                            \
-      mfma_frags(FCUR, acc);                                                                 \
-      interleave_reads_with_mfma();                                                          \
-    }
-    int kb = 0;
-    for (; kb + 7 < nk; kb += 4) {
-      MOE_DEEP_FULL(a0, s1, f0, f1, kb)
-      MOE_DEEP_FULL(a1, s2, f1, f0, kb + 1)
-      MOE_DEEP_FULL(a2, s3, f0, f1, kb + 2)
-      MOE_DEEP_FULL(a3, s0, f1, f0, kb + 3)
-    }
-#undef MOE_DEEP_FULL
-    // tail: the last steps, with every wait covering all loads in flight
-#define MOE_DEEP_TAIL(DMA_AT, NEXT_STAGE, FCUR, FNXT, KB)                                     \
-    {                                                                                        \
-      const int kb_ = (KB);                                                                  \
-      wait_and_barrier<0>();                                                                 \
-      if (kb_ + 4 < nk) issue(DMA_AT, a_src, b_src, kb_ + 4, wave);                          \
-      if (kb_ + 1 < nk) read_frags(NEXT_STAGE, FNXT, wm, wn, lane);                          \
-      mfma_frags(FCUR, acc);                                                                 \
-    }
-    for (; kb < nk; kb += 4) {
-      MOE_DEEP_TAIL(a0, s1, f0, f1, kb)
-      if (kb + 1 < nk) MOE_DEEP_TAIL(a1, s2, f1, f0, kb + 1)
-      if (kb + 2 < nk) MOE_DEEP_TAIL(a2, s3, f0, f1, kb + 2)
-      if (kb + 3 < nk) MOE_DEEP_TAIL(a3, s0, f1, f0, kb + 3)
-    }
-#undef MOE_DEEP_TAIL
-    __syncthreads();
-
-    // Epilogue through LDS: the C tile takes 64 rows per stage.
-    int el = lane, ewm = wm, ewn = wn, etid = tid;
-    asm volatile("" : "+v"(el), "+v"(etid), "+s"(ewm), "+s"(ewn));
-    constexpr int CH = BN / 8;
-#define MOE_DEEP_CROW(r)                                                                      \
-    (((r) >> 6) == 0 ? s0 : ((r) >> 6) == 1 ? s1 : ((r) >> 6) == 2 ? s2 : s3) + ((r) & 63) * BN
-#pragma unroll
-    for (int ni = 0; ni < TN; ++ni) {
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int nl = ewn * WTN + ni * 32 + q * 8 + (el >> 5) * 4;
-        const int n = n0 + nl;
-        float bv[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-        if (v.bias && n < a.Nout) {
-          const uint2 bq = *reinterpret_cast<const uint2 *>(v.bias + n);
-          bv[0] = __uint_as_float(bq.x << 16);
-          bv[1] = __uint_as_float(bq.x & 0xFFFF0000u);
-          bv[2] = __uint_as_float(bq.y << 16);
-          bv[3] = __uint_as_float(bq.y & 0xFFFF0000u);
-        }
-#pragma unroll
-        for (int mi = 0; mi < TM; ++mi) {
-          const int ml = ewm * WTM + mi * 32 + (el & 31);
-          float o[4];
-#pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            o[j] = acc[ni][mi][q * 4 + j] + bv[j];
-            if (EPI == kEpiBiasSilu) o[j] = silu(o[j]);
-          }
-          uint2 packed;
-          packed.x = f32_to_bf16(o[0]) | (static_cast<uint32_t>(f32_to_bf16(o[1])) << 16);
-          packed.y = f32_to_bf16(o[2]) | (static_cast<uint32_t>(f32_to_bf16(o[3])) << 16);
-          const int p = (nl >> 3) ^ (ml & 31);
-          *reinterpret_cast<uint2 *>(MOE_DEEP_CROW(ml) + p * 8 + ((nl >> 2) & 1) * 4) = packed;
-        }
-      }
-    }
-    __syncthreads();
-    for (int i = etid; i < BM * CH; i += NT) {
-      const int r = i / CH, c = i % CH;
-      const int64_t row = v.row0 + r;
-      const int n = n0 + c * 8;
-      if (row < v.rows && n < a.Nout) {
-        const u32x4_t val = *reinterpret_cast<const u32x4_t *>(MOE_DEEP_CROW(r) + ((c ^ (r & 31)) << 3));
-        *reinterpret_cast<u32x4_t *>(v.C + (v.out_base + row) * a.Nout + n) = val;
-      }
-    }
-#undef MOE_DEEP_CROW
-    __syncthreads();
-  }
-}
-
-// ---------------------------------------------------------------------------
 // bf16 MFMA kernel, register-staged pipeline: 256x256 tiles, four 128x128
 // wave tiles, one LDS buffer of one 64-wide K-step.  Global loads run two
 // K-steps ahead into registers; each step's fragments (all four 16-wide
@@ -896,6 +637,318 @@ void grouped_gemm_bf16_rs_kernel(GemmArgs a) {
 }
 
 // ---------------------------------------------------------------------------
+// bf16 stream kernel for groups with few rows (decode batches, the many small
+// experts of a skewed prefill), bound by the weight stream: a deep ring of
+// LDS stages keeps about 100 KB of weights in flight per CU.
+//
+// Work unit: (group, block of 32*NTB rows, block of 128*MB output features,
+// k-split part); a wave owns 32*MB features of the unit.  Each 64-wide
+// k-chunk of weights and activations goes from HBM straight into one LDS
+// stage (global_load_lds: one wave instruction moves 8 rows x 128 bytes, so
+// every request uses whole cache lines), rows of 128 bytes with the 16-byte
+// pieces swizzled (piece c of row r sits at c ^ ((r >> 1) & 7)) so that the
+// MFMA fragment reads of 32 rows hit distinct banks.  A chunk is loaded S-1
+// chunks ahead; each step waits for its own wave's copies of the chunk, meets
+// the other waves at a barrier (which also frees the oldest stage), refills
+// that stage and runs the chunk's MFMAs.
+//
+// Few units (a decode batch touches few experts) would leave CUs idle, so
+// the kernel splits K into up to ks_cap parts when there are fewer than four
+// units per workgroup; every workgroup derives the same split from the
+// device-side counts.  Split parts write float32 partial sums per output row,
+// and stream_reduce_kernel adds them in part order and applies the epilogue.
+// ---------------------------------------------------------------------------
+struct StreamSplit {
+  float *partial;      // [ks_cap][part_rows + n_shared * T_sh][Nout] or null
+  int *ks_used;        // device scalar: the split the kernel chose
+  int64_t part_rows;   // routed rows in the partial buffer (host bound)
+  int ks_cap;          // 1: never split
+};
+
+namespace st {
+constexpr int NT = 256, NW = 4, KCH = 64;
+
+// LDS byte address of a __shared__ object (wave-uniform).
+__device__ __forceinline__ uint32_t lds_addr(const void *p) {
+  return static_cast<uint32_t>(
+      reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) const void *)p));
+}
+
+// One wave-wide LDS DMA (64 lanes x 16 B into the 1 KB block at LDS byte
+// address m0), written as inline assembly so the compiler does not drain
+// every load in flight before later LDS reads; the explicit waits cover it.
+// The s_nop separates the compiler's write of M0 from the copy that reads it.
+__device__ __forceinline__ void dma16(const uint16_t *src, uint32_t m0) {
+  asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, off" : : "v"(src), "{m0}"(m0) : "memory");
+}
+
+// Wait until at most N of this wave's copies are in flight and its LDS reads
+// are done, then meet the other waves.
+template <int N>
+__device__ __forceinline__ void wait_and_barrier() {
+  asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)" ::"n"(N) : "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+// wait_and_barrier<n * LPS> for a run-time n in [0, MAXN].
+template <int LPS, int MAXN>
+__device__ __forceinline__ void wait_chunks(int n) {
+  if constexpr (MAXN >= 0) {
+    if (n >= MAXN) {
+      wait_and_barrier<MAXN * LPS>();
+      return;
+    }
+    wait_chunks<LPS, MAXN - 1>(n);
+  }
+}
+
+__device__ __forceinline__ int swz(int r, int c) { return c ^ ((r >> 1) & 7); }
+
+// Split chosen from the unit count: at least four units per workgroup.
+__device__ __forceinline__ int stream_split(int base_units, int nkc, int ks_cap, int grid,
+                                            int *kc_per) {
+  int ks = 1;
+  if (ks_cap > 1 && base_units > 0) {
+    ks = (4 * grid + base_units - 1) / base_units;
+    ks = min(ks, ks_cap);
+    ks = min(ks, max(1, nkc / 4));   // keep at least four chunks per part
+    ks = max(ks, 1);
+  }
+  const int per = (nkc + ks - 1) / ks;
+  *kc_per = per;
+  return (nkc + per - 1) / per;      // no empty parts
+}
+}  // namespace st
+
+template <int MB, int NTB, int S, int EPI>
+__global__ __launch_bounds__(256) void grouped_gemm_bf16_stream_kernel(GemmArgs a, StreamSplit sp) {
+  using namespace st;
+  constexpr int MR = 32 * NTB;                   // rows per unit
+  constexpr int NB = 4 * 32 * MB;                // features per unit
+  constexpr int W_INS = NB / 8 / NW;             // weight copies per wave per chunk
+  constexpr int X_INS = MR / 8 / NW;             // activation copies per wave per chunk
+  constexpr int LPS = W_INS + X_INS;
+  constexpr int STAGE = (NB + MR) * KCH;         // bf16 elements
+  static_assert((S - 2) * LPS <= 63, "vmcnt range");
+  __shared__ __attribute__((aligned(16))) uint16_t s_ring[S * STAGE];
+  __shared__ int s_pref[kMaxGroups + 1];
+  __shared__ int s_tmp[NT / 64];
+
+  const int lane = threadIdx.x & 63;
+  const int wave = uniform(threadIdx.x >> 6);
+  const int r32 = lane & 31, h = lane >> 5;
+  const int n_groups = a.n_routed + a.n_shared;
+  const int total_m = build_tile_prefix<NT, MR>(a, s_pref, s_tmp);
+  const int n_nb = (a.Nout + NB - 1) / NB;
+  const int nkc = a.K / KCH;
+  int kc_per;
+  const int ks = stream_split(total_m * n_nb, nkc, sp.ks_cap, gridDim.x, &kc_per);
+  if (blockIdx.x == 0 && threadIdx.x == 0 && sp.ks_used) *sp.ks_used = ks;
+  const int total = total_m * n_nb * ks;
+  const int xcd = blockIdx.x % kXcds;
+  const int slot = blockIdx.x / kXcds;
+  const int nslots = gridDim.x / kXcds;
+  const int part = (total + kXcds - 1) / kXcds;
+  const int begin = xcd * part;
+  const int end = min(total, begin + part);
+  const uint32_t ring0 = uniform(static_cast<int>(lds_addr(s_ring)));
+  // lane's place in a copy: row lane/8 of an 8-row block, LDS piece lane%8
+  const int crow = lane >> 3, cpos = lane & 7;
+  int stage = 0;                                 // ring position of the next chunk
+
+  for (int L = begin + slot; L < end; L += nslots) {
+    // unit order: part fastest, then row block, then feature block, so the
+    // workgroups running together share a weight block in L2
+    const int kp = L % ks;
+    const int u = L / ks;
+    const int g = find_group(s_pref, n_groups, u / n_nb);
+    const int mg = s_pref[g + 1] - s_pref[g];
+    const int uu = u - s_pref[g] * n_nb;
+    const int nb = uu / mg, rb = uu % mg;
+    const TileView<uint16_t> v = tile_view<uint16_t>(a, g, rb, MR);
+    const int n0 = nb * NB;
+    const int kc0 = kp * kc_per;
+    const int nch = min(nkc, kc0 + kc_per) - kc0;
+
+    // sources of this wave's copies (chunk 0 of the part)
+    const uint16_t *w_src[W_INS];
+    const uint16_t *x_src[X_INS];
+#pragma unroll
+    for (int i = 0; i < W_INS; ++i) {
+      const int r = (i * NW + wave) * 8 + crow;
+      const int n = min(n0 + r, a.Nout - 1);
+      w_src[i] = v.W + static_cast<int64_t>(n) * a.K + kc0 * KCH + swz(r, cpos) * 8;
+    }
+#pragma unroll
+    for (int i = 0; i < X_INS; ++i) {
+      const int r = (i * NW + wave) * 8 + crow;
+      x_src[i] = a_row_ptr(a, v, v.row0 + r) + kc0 * KCH + swz(r, cpos) * 8;
+    }
+    auto issue = [&](int c, int st_idx) {
+      const uint32_t base = ring0 + static_cast<uint32_t>(st_idx) * (STAGE * 2);
+#pragma unroll
+      for (int i = 0; i < W_INS; ++i) dma16(w_src[i] + c * KCH, base + (i * NW + wave) * 1024);
+#pragma unroll
+      for (int i = 0; i < X_INS; ++i)
+        dma16(x_src[i] + c * KCH, base + NB * KCH * 2 + (i * NW + wave) * 1024);
+    };
+
+    f32x16_t acc[MB][NTB];
+#pragma unroll
+    for (int i = 0; i < MB; ++i)
+#pragma unroll
+      for (int j = 0; j < NTB; ++j)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+
+    const int pro = min(S - 1, nch);
+    for (int c = 0; c < pro; ++c) issue(c, (stage + c) % S);
+    for (int c = 0; c < nch; ++c) {
+      // copies of chunks c+1 .. min(c+S-2, nch-1) may stay in flight
+      const int later = min(S - 2, nch - 1 - c);
+      if (later == S - 2) wait_and_barrier<(S - 2) * LPS>();
+      else wait_chunks<LPS, S - 3>(later);
+      const int cur = (stage + c) % S;
+      if (c + S - 1 < nch) issue(c + S - 1, (stage + c + S - 1) % S);
+      const uint16_t *sw = s_ring + cur * STAGE;
+      const uint16_t *sx = sw + NB * KCH;
+#pragma unroll
+      for (int kst = 0; kst < 4; ++kst) {
+        const int p = 2 * kst + h;
+        bf16x8_t fw[MB], fx[NTB];
+#pragma unroll
+        for (int i = 0; i < MB; ++i) {
+          const int r = wave * 32 * MB + 32 * i + r32;
+          fw[i] = *reinterpret_cast<const bf16x8_t *>(sw + r * KCH + swz(r, p) * 8);
+        }
+#pragma unroll
+        for (int j = 0; j < NTB; ++j) {
+          const int r = 32 * j + r32;
+          fx[j] = *reinterpret_cast<const bf16x8_t *>(sx + r * KCH + swz(r, p) * 8);
+        }
+#pragma unroll
+        for (int i = 0; i < MB; ++i)
+#pragma unroll
+          for (int j = 0; j < NTB; ++j)
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fw[i], fx[j], acc[i][j], 0, 0, 0);
+      }
+    }
+    stage = (stage + nch) % S;
+
+    // lane holds row r32 of each 32-row block and features 8q + 4h .. +3 of
+    // each 32-feature block
+    const int nw0 = n0 + wave * 32 * MB;
+#pragma unroll
+    for (int j = 0; j < NTB; ++j) {
+      const int64_t lr = v.row0 + 32 * j + r32;
+      if (lr >= v.rows) continue;
+      if (ks > 1) {
+        const int64_t prow = g < a.n_routed
+                                 ? v.out_base + lr
+                                 : sp.part_rows + static_cast<int64_t>(g - a.n_routed) * a.T_sh + lr;
+        const int64_t nrows = sp.part_rows + static_cast<int64_t>(a.n_shared) * a.T_sh;
+        float *dst = sp.partial + (static_cast<int64_t>(kp) * nrows + prow) * a.Nout;
+#pragma unroll
+        for (int i = 0; i < MB; ++i)
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const int n = nw0 + 32 * i + 8 * q + 4 * h;
+            if (n < a.Nout) {
+              const f32x16_t &c = acc[i][j];
+              *reinterpret_cast<float4 *>(dst + n) =
+                  make_float4(c[4 * q], c[4 * q + 1], c[4 * q + 2], c[4 * q + 3]);
+            }
+          }
+      } else {
+        uint16_t *dst = v.C + (v.out_base + lr) * a.Nout;
+#pragma unroll
+        for (int i = 0; i < MB; ++i)
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const int n = nw0 + 32 * i + 8 * q + 4 * h;
+            if (n < a.Nout) {
+              float bv[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+              if (v.bias) {
+                const uint2 bq = *reinterpret_cast<const uint2 *>(v.bias + n);
+                bv[0] = __uint_as_float(bq.x << 16);
+                bv[1] = __uint_as_float(bq.x & 0xFFFF0000u);
+                bv[2] = __uint_as_float(bq.y << 16);
+                bv[3] = __uint_as_float(bq.y & 0xFFFF0000u);
+              }
+              float o[4];
+#pragma unroll
+              for (int e = 0; e < 4; ++e) {
+                o[e] = acc[i][j][4 * q + e] + bv[e];
+                if (EPI == kEpiBiasSilu) o[e] = silu_fast(o[e]);
+              }
+              uint2 packed;
+              packed.x = f32_to_bf16(o[0]) | (static_cast<uint32_t>(f32_to_bf16(o[1])) << 16);
+              packed.y = f32_to_bf16(o[2]) | (static_cast<uint32_t>(f32_to_bf16(o[3])) << 16);
+              *reinterpret_cast<uint2 *>(dst + n) = packed;
+            }
+          }
+      }
+    }
+  }
+}
+
+// Sum of the k-split partials in part order, bias, epilogue, bf16 store.
+// One thread per four features of one output row; rows of routed groups past
+// offsets[n_routed] do not exist and are skipped.
+template <int EPI>
+__global__ __launch_bounds__(256) void stream_reduce_kernel(GemmArgs a, StreamSplit sp) {
+  const int ks = *sp.ks_used;
+  if (ks <= 1) return;
+  const int64_t prow = blockIdx.y;
+  const int n = (blockIdx.x * 256 + threadIdx.x) * 4;
+  if (n >= a.Nout) return;
+  const int64_t nrows = sp.part_rows + static_cast<int64_t>(a.n_shared) * a.T_sh;
+  const uint16_t *bias;
+  uint16_t *dst;
+  if (prow < sp.part_rows) {
+    if (prow >= a.offsets[a.n_routed]) return;
+    int lo = 0, hi = a.n_routed;   // offsets[lo] <= prow < offsets[hi]
+    while (hi - lo > 1) {
+      const int mid = (lo + hi) >> 1;
+      if (a.offsets[mid] <= prow) lo = mid; else hi = mid;
+    }
+    if (group_rows(a, lo) == 0) return;   // another kernel's group
+    bias = a.bias ? static_cast<const uint16_t *>(a.bias) + static_cast<int64_t>(lo) * a.Nout : nullptr;
+    dst = static_cast<uint16_t *>(a.C) + prow * a.Nout;
+  } else {
+    const int gs = static_cast<int>((prow - sp.part_rows) / a.T_sh);
+    if (group_rows(a, a.n_routed + gs) == 0) return;
+    bias = a.bias_sh ? static_cast<const uint16_t *>(a.bias_sh) + static_cast<int64_t>(gs) * a.Nout
+                     : nullptr;
+    dst = static_cast<uint16_t *>(a.C_sh) + (prow - sp.part_rows) * a.Nout;
+  }
+  float4 s = *reinterpret_cast<const float4 *>(sp.partial + prow * a.Nout + n);
+  for (int p = 1; p < ks; ++p) {
+    const float4 t = *reinterpret_cast<const float4 *>(sp.partial + (p * nrows + prow) * a.Nout + n);
+    s.x += t.x;
+    s.y += t.y;
+    s.z += t.z;
+    s.w += t.w;
+  }
+  float o[4] = {s.x, s.y, s.z, s.w};
+  if (bias) {
+    const uint2 bq = *reinterpret_cast<const uint2 *>(bias + n);
+    o[0] += __uint_as_float(bq.x << 16);
+    o[1] += __uint_as_float(bq.x & 0xFFFF0000u);
+    o[2] += __uint_as_float(bq.y << 16);
+    o[3] += __uint_as_float(bq.y & 0xFFFF0000u);
+  }
+  if (EPI == kEpiBiasSilu)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) o[e] = silu_fast(o[e]);
+  uint2 packed;
+  packed.x = f32_to_bf16(o[0]) | (static_cast<uint32_t>(f32_to_bf16(o[1])) << 16);
+  packed.y = f32_to_bf16(o[2]) | (static_cast<uint32_t>(f32_to_bf16(o[3])) << 16);
+  *reinterpret_cast<uint2 *>(dst + n) = packed;
+}
+
+// ---------------------------------------------------------------------------
 // fp32 VALU kernel (also accepts bf16 operands): 64x64 tiles, 256 threads
 // ---------------------------------------------------------------------------
 template <typename TA, int EPI>
@@ -1005,6 +1058,8 @@ GemmArgs make_args(const GemmGroups &g) {
   a.n_shared = g.n_shared;
   a.Nout = g.Nout;
   a.K = g.K;
+  a.cls_lo = 0;
+  a.cls_hi = INT64_MAX;
   return a;
 }
 
@@ -1038,13 +1093,40 @@ hipError_t launch_bf16(const GemmArgs &a, const GemmGroups &g, Epilogue epi, int
   return hipGetLastError();
 }
 
-template <int GM>
-hipError_t launch_bf16_deep(const GemmArgs &a, const GemmGroups &g, Epilogue epi, hipStream_t s) {
-  const unsigned grid = persistent_grid(tiles_upper_bound(g, 256, 256), 1);
+constexpr int kSplitCap = 8;
+constexpr int64_t kSplitMaxRows = 8192;   // partial rows (reduce grid.y, scratch size)
+
+int64_t split_rows(const GemmGroups &g) {
+  return g.max_routed_rows + static_cast<int64_t>(g.n_shared) * g.T_sh;
+}
+
+template <int MB, int NTB, int S>
+hipError_t launch_bf16_stream(const GemmArgs &a, const GemmGroups &g, Epilogue epi, int per_cu,
+                              hipStream_t s) {
+  StreamSplit sp{};
+  sp.ks_cap = 1;
+  const int64_t prows = split_rows(g);
+  if (g.split_ws && g.split_cap > 1 && prows <= kSplitMaxRows) {
+    sp.ks_used = static_cast<int *>(g.split_ws);
+    sp.partial = reinterpret_cast<float *>(static_cast<char *>(g.split_ws) + 256);
+    sp.part_rows = g.max_routed_rows;
+    sp.ks_cap = g.split_cap < kSplitCap ? g.split_cap : kSplitCap;
+  }
+  const unsigned grid =
+      persistent_grid(tiles_upper_bound(g, 32 * NTB, 128 * MB) * sp.ks_cap, per_cu);
   if (epi == kEpiBiasSilu)
-    hipLaunchKernelGGL((grouped_gemm_bf16_deep_kernel<kEpiBiasSilu, GM>), dim3(grid), dim3(256), 0, s, a);
+    hipLaunchKernelGGL((grouped_gemm_bf16_stream_kernel<MB, NTB, S, kEpiBiasSilu>),
+                       dim3(grid), dim3(256), 0, s, a, sp);
   else
-    hipLaunchKernelGGL((grouped_gemm_bf16_deep_kernel<kEpiBias, GM>), dim3(grid), dim3(256), 0, s, a);
+    hipLaunchKernelGGL((grouped_gemm_bf16_stream_kernel<MB, NTB, S, kEpiBias>), dim3(grid),
+                       dim3(256), 0, s, a, sp);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || sp.ks_cap <= 1) return e;
+  const dim3 rgrid(static_cast<unsigned>((g.Nout / 4 + 255) / 256), static_cast<unsigned>(prows));
+  if (epi == kEpiBiasSilu)
+    hipLaunchKernelGGL((stream_reduce_kernel<kEpiBiasSilu>), rgrid, dim3(256), 0, s, a, sp);
+  else
+    hipLaunchKernelGGL((stream_reduce_kernel<kEpiBias>), rgrid, dim3(256), 0, s, a, sp);
   return hipGetLastError();
 }
 
@@ -1060,18 +1142,34 @@ hipError_t launch_bf16_rs(const GemmArgs &a, const GemmGroups &g, Epilogue epi, 
 
 }  // namespace
 
+size_t grouped_gemm_split_bytes(const GemmGroups &g, int cap) {
+  const int64_t prows = split_rows(g);
+  if (cap <= 1 || prows > kSplitMaxRows) return 0;
+  if (cap > kSplitCap) cap = kSplitCap;
+  return 256 + sizeof(float) * static_cast<size_t>(cap) * prows * g.Nout;
+}
+
 hipError_t launch_grouped_gemm(bool bf16, const GemmGroups &g, Epilogue epi, hipStream_t s) {
-  const GemmArgs a = make_args(g);
+  GemmArgs a = make_args(g);
   if (g.n_routed + g.n_shared <= 0 || g.Nout <= 0) return hipSuccess;
   if (bf16 && g.K % 64 == 0 && g.Nout % 4 == 0) {
-    // rows per routed group decide the tile: few rows -> stream weights with a
-    // short M tile; many rows -> square tiles for operand reuse
+    // Groups of up to kStreamRows rows are bound by their weight stream and
+    // go to the stream kernel; larger groups reuse each weight tile across
+    // 256 rows in the 256x256 kernel.  Each kernel takes its own size class.
+    constexpr int64_t kStreamRows = 256;
     const int64_t groups = g.n_routed > 0 ? g.n_routed : 1;
     const int64_t mean_rows = g.max_routed_rows / groups;
-    if (mean_rows <= 48 && g.T_sh <= 256)
-      return launch_bf16<32, 128, 1, 4, 8>(a, g, epi, 2, s);
-    if (mean_rows >= 384) return launch_bf16_rs<8>(a, g, epi, s);
-    return launch_bf16<128, 128, 2, 2, 8>(a, g, epi, 2, s);
+    const int64_t max_rows = g.n_routed > 0 ? g.max_group_rows : 0;
+    const bool any_big = max_rows > kStreamRows || (g.n_shared > 0 && g.T_sh > kStreamRows);
+    const bool any_small = (g.n_routed > 0 && mean_rows < 384) || (g.n_shared > 0 && g.T_sh <= kStreamRows);
+    if (!any_big) return launch_bf16_stream<1, 1, 6>(a, g, epi, 1, s);
+    if (!any_small) return launch_bf16_rs<8>(a, g, epi, s);
+    a.cls_lo = kStreamRows + 1;
+    hipError_t e = launch_bf16_rs<8>(a, g, epi, s);
+    if (e != hipSuccess) return e;
+    a.cls_lo = 0;
+    a.cls_hi = kStreamRows;
+    return launch_bf16_stream<1, 2, 6>(a, g, epi, 1, s);
   }
   const unsigned grid = persistent_grid(tiles_upper_bound(g, 64, 64), 4);
   if (bf16) {

@@ -66,8 +66,34 @@ struct LayerWs {
   void *h_sh;    // shared hidden [Ks][T][f]
   void *y_rows;  // routed outputs [T*K][d]
   void *s_out;   // shared outputs [Ks][T][d]
+  void *split;   // k-split scratch of the expert GEMMs (may be empty)
   size_t bytes;
 };
+
+// Row bounds the dispatch guarantees: a routed group holds at most T rows
+// (a token meets an expert once) and at most C; all groups at most T*K and
+// N*C rows together.
+int64_t routed_rows_bound(const moe_config *c) {
+  const int64_t C = capacity_of(c);
+  const int64_t tk = c->T * c->top_k;
+  return C >= 0 && C * c->n_routed < tk ? C * c->n_routed : tk;
+}
+int64_t group_rows_bound(const moe_config *c) {
+  const int64_t C = capacity_of(c);
+  return C >= 0 && C < c->T ? C : c->T;
+}
+
+// Split scratch the layer's two expert GEMMs may use (shared by both).
+size_t layer_split_bytes(const moe_config *c) {
+  if (c->dtype != MOE_BF16) return 0;
+  GemmGroups g{};
+  g.n_routed = c->n_routed;
+  g.n_shared = c->n_shared;
+  g.T_sh = c->T;
+  g.max_routed_rows = routed_rows_bound(c);
+  g.Nout = c->d_ff > c->d_model ? c->d_ff : c->d_model;
+  return moe::grouped_gemm_split_bytes(g, 8);
+}
 
 LayerWs layer_ws(const moe_config *c, void *base) {
   LayerWs w;
@@ -93,6 +119,8 @@ LayerWs layer_ws(const moe_config *c, void *base) {
   w.h_sh = take(ab * Ks * T * c->d_ff);
   w.y_rows = take(ab * T * K * c->d_model);
   w.s_out = take(ab * Ks * T * c->d_model);
+  const size_t sb = layer_split_bytes(c);
+  w.split = sb ? take(sb) : nullptr;
   w.bytes = off;
   return w;
 }
@@ -162,9 +190,20 @@ int moe_permute(const moe_config *cfg, const int32_t *topk_idx, const void *x, i
                                             cfg->d_model, x_perm, s));
 }
 
+size_t moe_grouped_ffn_workspace_size(const moe_config *cfg, int32_t n_groups, int64_t max_rows) {
+  if (check_config(cfg, false, true) != MOE_OK || n_groups <= 0 || max_rows < 0) return 0;
+  if (cfg->dtype != MOE_BF16) return 0;
+  GemmGroups g{};
+  g.n_routed = n_groups;
+  g.max_routed_rows = max_rows;
+  g.Nout = cfg->d_ff > cfg->d_model ? cfg->d_ff : cfg->d_model;
+  return moe::grouped_gemm_split_bytes(g, 8);
+}
+
 int moe_grouped_ffn(const moe_config *cfg, int32_t n_groups, const void *x_rows,
                     const int32_t *offsets, int64_t max_rows, const void *w1, const void *b1,
-                    const void *w2, const void *b2, void *h, void *y_rows, void *stream) {
+                    const void *w2, const void *b2, void *h, void *y_rows, void *ws,
+                    size_t ws_bytes, void *stream) {
   int st = check_config(cfg, false, true);
   if (st != MOE_OK) return st;
   if (n_groups <= 0 || max_rows < 0) return MOE_ERR_INVALID_ARG;
@@ -175,6 +214,8 @@ int moe_grouped_ffn(const moe_config *cfg, int32_t n_groups, const void *x_rows,
   if (!aligned16(x_rows) || !aligned16(w1) || !aligned16(w2) || !aligned16(h) ||
       !aligned16(y_rows))
     return MOE_ERR_INVALID_ARG;
+  const size_t need = moe_grouped_ffn_workspace_size(cfg, n_groups, max_rows);
+  if (ws && ws_bytes < need) return MOE_ERR_WORKSPACE;
   const bool bf16 = cfg->dtype == MOE_BF16;
   hipStream_t s = static_cast<hipStream_t>(stream);
   GemmGroups g{};
@@ -187,6 +228,9 @@ int moe_grouped_ffn(const moe_config *cfg, int32_t n_groups, const void *x_rows,
   g.Nout = cfg->d_ff;
   g.K = cfg->d_model;
   g.max_routed_rows = max_rows;
+  g.max_group_rows = max_rows;
+  g.split_ws = ws && need ? ws : nullptr;
+  g.split_cap = g.split_ws ? 8 : 1;
   st = hip_status(moe::launch_grouped_gemm(bf16, g, moe::kEpiBiasSilu, s));
   if (st != MOE_OK) return st;
   g.A = h;
@@ -285,7 +329,10 @@ int moe_layer_forward_events(const moe_config *cfg, const moe_weights *w, const 
   g.C_sh = L.h_sh;
   g.Nout = cfg->d_ff;
   g.K = cfg->d_model;
-  g.max_routed_rows = T * K;
+  g.max_routed_rows = routed_rows_bound(cfg);
+  g.max_group_rows = group_rows_bound(cfg);
+  g.split_ws = L.split;
+  g.split_cap = L.split ? 8 : 1;
   if ((st = mark(MOE_STAGE_UP)) != MOE_OK) return st;
   st = hip_status(moe::launch_grouped_gemm(bf16, g, moe::kEpiBiasSilu, s));
   if (st != MOE_OK) return st;

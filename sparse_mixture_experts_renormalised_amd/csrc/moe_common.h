@@ -71,7 +71,17 @@ struct GemmGroups {
   void *C, *C_sh;
   int Nout, K;
   int64_t max_routed_rows;   // host upper bound on offsets[n_routed]
+  int64_t max_group_rows;    // host upper bound on the rows of one routed group
+  // Optional scratch for splitting K when a product has too few units to
+  // fill the chip: split_cap partial sums of (max_routed_rows + n_shared *
+  // T_sh) rows x Nout floats, plus one int (grouped_gemm_split_bytes).
+  void *split_ws;
+  int split_cap;
 };
+
+// Bytes of split scratch launch_grouped_gemm can use for this product
+// (0 when it never splits such a product).
+size_t grouped_gemm_split_bytes(const GemmGroups &g, int cap);
 
 enum Epilogue { kEpiBias = 0, kEpiBiasSilu = 1 };
 

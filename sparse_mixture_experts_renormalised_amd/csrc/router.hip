@@ -205,26 +205,29 @@ __global__ __launch_bounds__(256) void topk_gates_kernel(const float *__restrict
 hipError_t launch_router_logits(bool bf16, const void *x, const float *w, const float *bias,
                                 float *logits, int64_t T, int d, int N, hipStream_t s) {
   if (T <= 0) return hipSuccess;
-  // Wide routers with many tokens: 64x64 blocks, 4x4 per thread (fewer LDS
-  // bytes per multiply-add).  Otherwise 64x8 blocks with two outputs per
-  // thread, so short batches and narrow routers still spread over the chip.
-  const bool wide = N >= 64 && T * static_cast<int64_t>(N) >= (int64_t(1) << 19);
-  const int64_t tb = (T + 63) / 64;
+  // Block shapes measured on MI355X: wide routers over many tokens use 32x64
+  // blocks with 2x4 logits per thread, mid-sized ones 32x32 with 2x2, and
+  // short batches or narrow routers 64x8 with 2x1, so that they still spread
+  // over the chip.
+  const int64_t TN = T * static_cast<int64_t>(N);
   const int kc32 = d % 32 == 0;
-#define MOE_ROUTER_LAUNCH(BE, MT, ME, KC)                                                       \
+#define MOE_ROUTER_LAUNCH(BT, BE, MT, ME, KC)                                                   \
   {                                                                                             \
-    const dim3 grid(static_cast<unsigned>(tb), static_cast<unsigned>((N + BE - 1) / BE));       \
+    const dim3 grid(static_cast<unsigned>((T + BT - 1) / BT),                                   \
+                    static_cast<unsigned>((N + BE - 1) / BE));                                  \
     if (bf16)                                                                                   \
-      hipLaunchKernelGGL((router_logits_kernel<64, BE, MT, ME, KC, true>), grid, dim3(256), 0, \
+      hipLaunchKernelGGL((router_logits_kernel<BT, BE, MT, ME, KC, true>), grid, dim3(256), 0, \
                          s, x, w, bias, logits, T, d, N);                                       \
     else                                                                                        \
-      hipLaunchKernelGGL((router_logits_kernel<64, BE, MT, ME, KC, false>), grid, dim3(256), 0,\
+      hipLaunchKernelGGL((router_logits_kernel<BT, BE, MT, ME, KC, false>), grid, dim3(256), 0,\
                          s, x, w, bias, logits, T, d, N);                                       \
   }
-  if (wide) {
-    if (kc32) MOE_ROUTER_LAUNCH(64, 4, 4, 32) else MOE_ROUTER_LAUNCH(64, 4, 4, 16)
+  if (N >= 64 && TN >= (int64_t(1) << 19)) {
+    if (kc32) MOE_ROUTER_LAUNCH(32, 64, 2, 4, 32) else MOE_ROUTER_LAUNCH(32, 64, 2, 4, 16)
+  } else if (N >= 32 && TN >= (int64_t(1) << 17)) {
+    if (kc32) MOE_ROUTER_LAUNCH(32, 32, 2, 2, 32) else MOE_ROUTER_LAUNCH(32, 32, 2, 2, 16)
   } else {
-    if (kc32) MOE_ROUTER_LAUNCH(8, 2, 1, 32) else MOE_ROUTER_LAUNCH(8, 2, 1, 16)
+    if (kc32) MOE_ROUTER_LAUNCH(64, 8, 2, 1, 32) else MOE_ROUTER_LAUNCH(64, 8, 2, 1, 16)
   }
 #undef MOE_ROUTER_LAUNCH
   return hipGetLastError();

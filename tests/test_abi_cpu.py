@@ -87,9 +87,9 @@ def test_invalid_arguments_are_rejected_before_launch(B):
                                None, None, 1 << 30, P(4096)) == -1
     # grouped FFN argument checks
     assert L.moe_grouped_ffn(ctypes.byref(good), 0, None, None, 10, None, None, None, None, None,
-                             None, None) == -1
+                             None, None, 0, None) == -1
     assert L.moe_grouped_ffn(ctypes.byref(good), 3, None, None, 10, None, None, None, None, None,
-                             None, None) == -1
+                             None, None, 0, None) == -1
     # combine needs shared outputs when shared experts exist
     sh = B.config(64, 128, 8, 2, 2, 256, "bf16")
     assert L.moe_combine(ctypes.byref(sh), P(16), P(16), P(16), None, P(16), None) == -1
@@ -111,3 +111,14 @@ def test_workspace_sizes_grow_with_the_layer(B):
     # hidden + expert outputs of every assignment dominate: T*K*(d+f) act elements
     assert big >= 4096 * 8 * (7168 + 2048) * 2
     assert B.layer_workspace_size(B.config(64, 128, 8, 9, 0, 256, "f32")) == 0
+
+
+def test_grouped_ffn_split_workspace_size(B):
+    bf = B.config(128, 7168, 256, 8, 1, 2048, "bf16")
+    n = B.grouped_ffn_workspace_size(bf, 256, 1024)
+    # one int, then up to 8 float32 partial sums of every row x max(d, f)
+    assert n == 256 + 4 * 8 * 1024 * 7168
+    assert B.grouped_ffn_workspace_size(bf, 256, 1 << 20) == 0   # large products never split
+    f32 = B.config(64, 128, 8, 2, 0, 256, "f32")
+    assert B.grouped_ffn_workspace_size(f32, 8, 128) == 0
+    assert B.grouped_ffn_workspace_size(bf, 0, 1024) == 0

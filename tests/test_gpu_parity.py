@@ -237,14 +237,17 @@ def test_grouped_ffn_matches_oracle(case):
     offs = np.concatenate([[0], np.cumsum(rows)]).astype(np.int32)
     offsets = torch.from_numpy(offs).cuda()
     act = act_dtype(wl)
-    h = torch.zeros((max(R, 1), f), dtype=act, device="cuda")
-    y = torch.zeros((max(R, 1), d), dtype=act, device="cuda")
-    b.grouped_ffn(cfg, G, x_rows, offsets, R, w1, b1, w2, b2, h, y)
-    torch.cuda.synchronize()
     routed, _ = providers_host(wl)
     H, Y = oracle.grouped_ffn(host(x_rows), offs, routed, G)
-    assert rel_l2(host(h)[:R], H) <= TOL[dtype]
-    assert rel_l2(host(y)[:R], Y) <= TOL[dtype]
+    # without scratch, then with the scratch that lets small products split K
+    nws = b.grouped_ffn_workspace_size(cfg, G, R)
+    for ws in (None, torch.empty(max(nws, 1), dtype=torch.uint8, device="cuda") if nws else None):
+        h = torch.zeros((max(R, 1), f), dtype=act, device="cuda")
+        y = torch.zeros((max(R, 1), d), dtype=act, device="cuda")
+        b.grouped_ffn(cfg, G, x_rows, offsets, R, w1, b1, w2, b2, h, y, ws=ws)
+        torch.cuda.synchronize()
+        assert rel_l2(host(h)[:R], H) <= TOL[dtype]
+        assert rel_l2(host(y)[:R], Y) <= TOL[dtype]
 
 
 # ---------------------------------------------------------------------------
