@@ -499,9 +499,162 @@ __device__ __forceinline__ void lds_barrier() {
 }
 }  // namespace rs
 
-template <int EPI, int GM>
+// Epilogue of a 256x256 tile through LDS in two passes of 128 rows (the tile
+// buffer holds 128 x 256 bf16): in pass p every wave stores its row blocks
+// mi = 2p, 2p+1, so all four waves work in both passes.
+template <int EPI>
+__device__ __forceinline__ void rs_epilogue(const f32x16_t (&acc)[rs::TN][rs::TM],
+                                            const GemmArgs &a, const TileView<uint16_t> &v,
+                                            int n0, uint16_t *s_tile, int lane, int wm, int wn,
+                                            int tid) {
+  using namespace rs;
+  int el = lane, ewm = wm, ewn = wn, etid = tid;
+  asm volatile("" : "+v"(el), "+v"(etid), "+s"(ewm), "+s"(ewn));
+  constexpr int CH = BN / 8;
+  static_assert(TILE >= 128 * BN, "128 C-tile rows must fit");
+#pragma unroll
+  for (int pass = 0; pass < 2; ++pass) {
+#pragma unroll
+    for (int ni = 0; ni < TN; ++ni) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int nl = ewn * WTN + ni * 32 + q * 8 + (el >> 5) * 4;
+        const int n = n0 + nl;
+        float bv[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+        if (v.bias && n < a.Nout) {
+          const uint2 bq = *reinterpret_cast<const uint2 *>(v.bias + n);
+          bv[0] = __uint_as_float(bq.x << 16);
+          bv[1] = __uint_as_float(bq.x & 0xFFFF0000u);
+          bv[2] = __uint_as_float(bq.y << 16);
+          bv[3] = __uint_as_float(bq.y & 0xFFFF0000u);
+        }
+#pragma unroll
+        for (int mm = 0; mm < 2; ++mm) {
+          const int mi = pass * 2 + mm;
+          const int ml = ewm * 64 + mm * 32 + (el & 31);   // row within the pass
+          float o[4];
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            o[j] = acc[ni][mi][q * 4 + j] + bv[j];
+            if (EPI == kEpiBiasSilu) o[j] = silu_fast(o[j]);
+          }
+          uint2 packed;
+          packed.x = f32_to_bf16(o[0]) | (static_cast<uint32_t>(f32_to_bf16(o[1])) << 16);
+          packed.y = f32_to_bf16(o[2]) | (static_cast<uint32_t>(f32_to_bf16(o[3])) << 16);
+          const int p = (nl >> 3) ^ (ml & 31);
+          *reinterpret_cast<uint2 *>(s_tile + ml * BN + p * 8 + ((nl >> 2) & 1) * 4) = packed;
+        }
+      }
+    }
+    __syncthreads();
+    // LDS row ml of the pass is tile row (ml/64)*128 + pass*64 + ml%64
+    for (int i = etid; i < 128 * CH; i += NT) {
+      const int r = i / CH, c = i % CH;
+      const int64_t row = v.row0 + (r >> 6) * 128 + pass * 64 + (r & 63);
+      const int n = n0 + c * 8;
+      if (row < v.rows && n < a.Nout) {
+        const u32x4_t val = *reinterpret_cast<const u32x4_t *>(s_tile + r * BN + ((c ^ (r & 31)) << 3));
+        *reinterpret_cast<u32x4_t *>(v.C + (v.out_base + row) * a.Nout + n) = val;
+      }
+    }
+    __syncthreads();
+  }
+}
+
+// Splitting the last, partly filled round of tiles along K.  Per XCD the
+// tiles form full rounds (one tile per workgroup of that XCD) and a remainder
+// of rem tiles; when rem is at most half the XCD's workgroups, each
+// remainder tile is cut into P contiguous K ranges computed by P workgroups
+// at once.  Each piece stores its float32 accumulators (native register
+// layout) in the scratch slot of its workgroup, and rs_fixup_kernel adds the
+// pieces of a tile in piece order and runs the usual epilogue.
+struct RsSplit {
+  float *partial;      // [max_blocks][256 * 256] floats, or null: never split
+  int max_blocks;      // grids wider than this do not split
+};
+
+struct RsPlan {
+  int begin, full, end, rem, P, kper;
+};
+
+__device__ __forceinline__ RsPlan rs_plan(int total, int xcd, int nslots, int nk, bool can_split) {
+  RsPlan p;
+  const int part = (total + kXcds - 1) / kXcds;
+  p.begin = xcd * part;
+  p.end = min(total, p.begin + part);
+  const int cnt = max(0, p.end - p.begin);
+  p.full = (cnt / nslots) * nslots;
+  p.rem = cnt - p.full;
+  int P = 1;
+  if (can_split && p.rem > 0 && 2 * p.rem <= nslots) P = min(nslots / p.rem, nk / 32);
+  if (P < 2) P = 1;
+  p.kper = (nk + P - 1) / P;
+  p.P = (nk + p.kper - 1) / p.kper;   // no empty pieces
+  return p;
+}
+
+// Accumulators of one 256x256 tile over K-steps k0 .. k0+nk-1.
+__device__ __forceinline__ void rs_tile(const GemmArgs &a, const TileView<uint16_t> &v, int n0,
+                                        int k0, int nk, uint16_t *s_tile, int tid, int lane,
+                                        int wm, int wn, f32x16_t (&acc)[rs::TN][rs::TM]) {
+  using namespace rs;
+  const int kc = tid & 7;
+  const uint16_t *a_src[A_CH];
+  const uint16_t *b_src[B_CH];
+#pragma unroll
+  for (int i = 0; i < A_CH; ++i)
+    a_src[i] = a_row_ptr(a, v, v.row0 + (tid >> 3) + i * (NT / 8)) + kc * 8 + k0 * BK;
+#pragma unroll
+  for (int i = 0; i < B_CH; ++i) {
+    int n = n0 + (tid >> 3) + i * (NT / 8);
+    if (n >= a.Nout) n = a.Nout - 1;
+    b_src[i] = v.W + static_cast<int64_t>(n) * a.K + kc * 8 + k0 * BK;
+  }
+#pragma unroll
+  for (int i = 0; i < TN; ++i)
+#pragma unroll
+    for (int j = 0; j < TM; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+
+  u32x4_t ra[A_CH], rb[B_CH];
+  Frags f;
+  gload(ra, rb, a_src, b_src, 0);
+  lstore(s_tile, ra, rb, tid);
+  if (nk > 1) gload(ra, rb, a_src, b_src, 1);
+  __syncthreads();
+  read_frags(s_tile, f, wm, wn, lane);
+  __builtin_amdgcn_sched_barrier(0);
+  // steady state (no branches, so each step is one scheduling region)
+  int kb = 0;
+  for (; kb + 2 < nk; ++kb) {
+    lds_barrier();                        // every wave has its fragments of step kb
+    lstore(s_tile, ra, rb, tid);          // step kb+1 into LDS
+    gload(ra, rb, a_src, b_src, kb + 2);  // step kb+2 into registers
+    mfma_all(f, acc);                     // step kb
+    lds_barrier();                        // step kb+1 is in LDS
+    read_frags(s_tile, f, wm, wn, lane);
+    schedule_step();
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  if (kb + 1 < nk) {                      // step nk-2: nothing left to load
+    lds_barrier();
+    lstore(s_tile, ra, rb, tid);
+    mfma_all(f, acc);
+    lds_barrier();
+    read_frags(s_tile, f, wm, wn, lane);
+  }
+  mfma_all(f, acc);                       // last step
+  __syncthreads();
+}
+
+// PIECE = false: whole tiles of the full rounds (of every round when there is
+// no split).  PIECE = true: the K pieces of the remainder tiles, one per
+// workgroup, stored as float32 partial tiles (launched right after, with the
+// same grid, so both derive the same plan).
+template <int EPI, int GM, bool PIECE>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
-void grouped_gemm_bf16_rs_kernel(GemmArgs a) {
+void grouped_gemm_bf16_rs_kernel(GemmArgs a, RsSplit sp) {
   using namespace rs;
   __shared__ __attribute__((aligned(16))) uint16_t s_tile[TILE];
   __shared__ int s_pref[kMaxGroups + 1];
@@ -514,125 +667,115 @@ void grouped_gemm_bf16_rs_kernel(GemmArgs a) {
   const int n_groups = a.n_routed + a.n_shared;
   const int total_m = build_tile_prefix<NT, BM>(a, s_pref, s_tmp);
   const int n_nt = (a.Nout + BN - 1) / BN;
-  const int total = total_m * n_nt;
   const int xcd = blockIdx.x % kXcds;
   const int slot = blockIdx.x / kXcds;
   const int nslots = gridDim.x / kXcds;
-  const int part = (total + kXcds - 1) / kXcds;
-  const int begin = xcd * part;
-  const int end = min(total, begin + part);
   const int nk = a.K / BK;
-  const int kc = tid & 7;
-
-  for (int L = begin + slot; L < end; L += nslots) {
+  const RsPlan pl = rs_plan(total_m * n_nt, xcd, nslots, nk,
+                            sp.partial != nullptr && static_cast<int>(gridDim.x) <= sp.max_blocks);
+  f32x16_t acc[TN][TM];
+  if constexpr (PIECE) {
+    if (pl.P <= 1 || slot >= pl.rem * pl.P) return;
     int mt, nt;
-    decode_tile<GM>(L, total_m, n_nt, &mt, &nt);
+    decode_tile<GM>(pl.begin + pl.full + slot / pl.P, total_m, n_nt, &mt, &nt);
     const int g = find_group(s_pref, n_groups, mt);
     const TileView<uint16_t> v = tile_view<uint16_t>(a, g, mt - s_pref[g], BM);
-    const int n0 = nt * BN;
-    const uint16_t *a_src[A_CH];
-    const uint16_t *b_src[B_CH];
-#pragma unroll
-    for (int i = 0; i < A_CH; ++i)
-      a_src[i] = a_row_ptr(a, v, v.row0 + (tid >> 3) + i * (NT / 8)) + kc * 8;
-#pragma unroll
-    for (int i = 0; i < B_CH; ++i) {
-      int n = n0 + (tid >> 3) + i * (NT / 8);
-      if (n >= a.Nout) n = a.Nout - 1;
-      b_src[i] = v.W + static_cast<int64_t>(n) * a.K + kc * 8;
-    }
-    f32x16_t acc[TN][TM];
+    const int k0 = (slot % pl.P) * pl.kper;
+    rs_tile(a, v, nt * BN, k0, min(nk, k0 + pl.kper) - k0, s_tile, tid, lane, wm, wn, acc);
+    float4 *dst = reinterpret_cast<float4 *>(sp.partial + static_cast<int64_t>(blockIdx.x) * (BM * BN));
 #pragma unroll
     for (int i = 0; i < TN; ++i)
 #pragma unroll
       for (int j = 0; j < TM; ++j)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+        for (int q = 0; q < 4; ++q)
+          dst[((i * TM + j) * 4 + q) * NT + tid] =
+              make_float4(acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2],
+                          acc[i][j][4 * q + 3]);
+  } else {
+    const int end = pl.P > 1 ? pl.begin + pl.full : pl.end;
+    for (int L = pl.begin + slot; L < end; L += nslots) {
+      int mt, nt;
+      decode_tile<GM>(L, total_m, n_nt, &mt, &nt);
+      const int g = find_group(s_pref, n_groups, mt);
+      const TileView<uint16_t> v = tile_view<uint16_t>(a, g, mt - s_pref[g], BM);
+      rs_tile(a, v, nt * BN, 0, nk, s_tile, tid, lane, wm, wn, acc);
+      rs_epilogue<EPI>(acc, a, v, nt * BN, s_tile, lane, wm, wn, tid);
+    }
+  }
+}
 
-    u32x4_t ra[A_CH], rb[B_CH];
-    Frags f;
-    gload(ra, rb, a_src, b_src, 0);
-    lstore(s_tile, ra, rb, tid);
-    if (nk > 1) gload(ra, rb, a_src, b_src, 1);
-    __syncthreads();
-    read_frags(s_tile, f, wm, wn, lane);
-    __builtin_amdgcn_sched_barrier(0);
-    // steady state (no branches, so each step is one scheduling region)
-    int kb = 0;
-    for (; kb + 2 < nk; ++kb) {
-      lds_barrier();                        // every wave has its fragments of step kb
-      lstore(s_tile, ra, rb, tid);          // step kb+1 into LDS
-      gload(ra, rb, a_src, b_src, kb + 2);  // step kb+2 into registers
-      mfma_all(f, acc);                     // step kb
-      lds_barrier();                        // step kb+1 is in LDS
-      read_frags(s_tile, f, wm, wn, lane);
-      schedule_step();
-      __builtin_amdgcn_sched_barrier(0);
-    }
-    if (kb + 1 < nk) {                      // step nk-2: nothing left to load
-      lds_barrier();
-      lstore(s_tile, ra, rb, tid);
-      mfma_all(f, acc);
-      lds_barrier();
-      read_frags(s_tile, f, wm, wn, lane);
-    }
-    mfma_all(f, acc);                       // last step
-    __syncthreads();
-
-    // Epilogue through LDS in two passes of 128 rows (the tile buffer holds
-    // 128 x 256 bf16): in pass p every wave stores its row blocks mi = 2p,
-    // 2p+1, so all four waves work in both passes.
-    int el = lane, ewm = wm, ewn = wn, etid = tid;
-    asm volatile("" : "+v"(el), "+v"(etid), "+s"(ewm), "+s"(ewn));
-    constexpr int CH = BN / 8;
-    static_assert(TILE >= 128 * BN, "128 C-tile rows must fit");
+// Sum of the K pieces of the split remainder tiles (in piece order), then
+// bias, SiLU and the bf16 store.  Workgroup b takes a quarter (16 of the 64
+// float4 register chunks) of remainder tile (b / 8) / 4 of XCD b % 8 of a
+// grouped_gemm_bf16_rs_kernel launch with gemm_grid workgroups; thread tid
+// handles the values that thread tid of the GEMM held.
+template <int EPI, int GM>
+__global__ __launch_bounds__(256) void rs_fixup_kernel(GemmArgs a, RsSplit sp, int gemm_grid) {
+  using namespace rs;
+  __shared__ int s_pref[kMaxGroups + 1];
+  __shared__ int s_tmp[NT / 64];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int wm = wave & 1, wn = wave >> 1;
+  const int n_groups = a.n_routed + a.n_shared;
+  const int total_m = build_tile_prefix<NT, BM>(a, s_pref, s_tmp);
+  const int n_nt = (a.Nout + BN - 1) / BN;
+  const int xcd = blockIdx.x % kXcds;
+  const int t = (blockIdx.x / kXcds) >> 2;
+  const int quarter = (blockIdx.x / kXcds) & 3;
+  const RsPlan pl = rs_plan(total_m * n_nt, xcd, gemm_grid / kXcds, a.K / BK,
+                            sp.partial != nullptr && gemm_grid <= sp.max_blocks);
+  if (pl.P <= 1 || t >= pl.rem) return;
+  int mt, nt;
+  decode_tile<GM>(pl.begin + pl.full + t, total_m, n_nt, &mt, &nt);
+  const int g = find_group(s_pref, n_groups, mt);
+  const TileView<uint16_t> v = tile_view<uint16_t>(a, g, mt - s_pref[g], BM);
+  const int n0 = nt * BN;
+  const int64_t blk0 = static_cast<int64_t>(t * pl.P) * kXcds + xcd;   // piece 0's workgroup
+  // all 16 chunks of one piece are loaded together, pieces are added in order
+  float4 acc[16];
+  for (int pc = 0; pc < pl.P; ++pc) {
+    const float4 *src = reinterpret_cast<const float4 *>(
+        sp.partial + (blk0 + static_cast<int64_t>(pc) * kXcds) * (BM * BN));
+    float4 p[16];
 #pragma unroll
-    for (int pass = 0; pass < 2; ++pass) {
+    for (int cc = 0; cc < 16; ++cc) p[cc] = src[(quarter * 16 + cc) * NT + tid];
 #pragma unroll
-      for (int ni = 0; ni < TN; ++ni) {
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const int nl = ewn * WTN + ni * 32 + q * 8 + (el >> 5) * 4;
-          const int n = n0 + nl;
-          float bv[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-          if (v.bias && n < a.Nout) {
-            const uint2 bq = *reinterpret_cast<const uint2 *>(v.bias + n);
-            bv[0] = __uint_as_float(bq.x << 16);
-            bv[1] = __uint_as_float(bq.x & 0xFFFF0000u);
-            bv[2] = __uint_as_float(bq.y << 16);
-            bv[3] = __uint_as_float(bq.y & 0xFFFF0000u);
-          }
-#pragma unroll
-          for (int mm = 0; mm < 2; ++mm) {
-            const int mi = pass * 2 + mm;
-            const int ml = ewm * 64 + mm * 32 + (el & 31);   // row within the pass
-            float o[4];
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-              o[j] = acc[ni][mi][q * 4 + j] + bv[j];
-              if (EPI == kEpiBiasSilu) o[j] = silu_fast(o[j]);
-            }
-            uint2 packed;
-            packed.x = f32_to_bf16(o[0]) | (static_cast<uint32_t>(f32_to_bf16(o[1])) << 16);
-            packed.y = f32_to_bf16(o[2]) | (static_cast<uint32_t>(f32_to_bf16(o[3])) << 16);
-            const int p = (nl >> 3) ^ (ml & 31);
-            *reinterpret_cast<uint2 *>(s_tile + ml * BN + p * 8 + ((nl >> 2) & 1) * 4) = packed;
-          }
-        }
+    for (int cc = 0; cc < 16; ++cc) {
+      if (pc == 0) {
+        acc[cc] = p[cc];
+      } else {
+        acc[cc].x += p[cc].x;
+        acc[cc].y += p[cc].y;
+        acc[cc].z += p[cc].z;
+        acc[cc].w += p[cc].w;
       }
-      __syncthreads();
-      // LDS row ml of the pass is tile row (ml/64)*128 + pass*64 + ml%64
-      for (int i = etid; i < 128 * CH; i += NT) {
-        const int r = i / CH, c = i % CH;
-        const int64_t row = v.row0 + (r >> 6) * 128 + pass * 64 + (r & 63);
-        const int n = n0 + c * 8;
-        if (row < v.rows && n < a.Nout) {
-          const u32x4_t val = *reinterpret_cast<const u32x4_t *>(s_tile + r * BN + ((c ^ (r & 31)) << 3));
-          *reinterpret_cast<u32x4_t *>(v.C + (v.out_base + row) * a.Nout + n) = val;
-        }
-      }
-      __syncthreads();
     }
+  }
+#pragma unroll
+  for (int cc = 0; cc < 16; ++cc) {
+    const int c = quarter * 16 + cc;          // (ni * TM + mi) * 4 + q
+    const int ni = c >> 4, mi = (c >> 2) & 3, q = c & 3;
+    const int64_t row = v.row0 + wm * WTM + mi * 32 + (lane & 31);
+    const int n = n0 + wn * WTN + ni * 32 + q * 8 + (lane >> 5) * 4;
+    if (row >= v.rows || n >= a.Nout) continue;
+    float o[4] = {acc[cc].x, acc[cc].y, acc[cc].z, acc[cc].w};
+    if (v.bias) {
+      const uint2 bq = *reinterpret_cast<const uint2 *>(v.bias + n);
+      o[0] += __uint_as_float(bq.x << 16);
+      o[1] += __uint_as_float(bq.x & 0xFFFF0000u);
+      o[2] += __uint_as_float(bq.y << 16);
+      o[3] += __uint_as_float(bq.y & 0xFFFF0000u);
+    }
+    if (EPI == kEpiBiasSilu)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) o[e] = silu_fast(o[e]);
+    uint2 packed;
+    packed.x = f32_to_bf16(o[0]) | (static_cast<uint32_t>(f32_to_bf16(o[1])) << 16);
+    packed.y = f32_to_bf16(o[2]) | (static_cast<uint32_t>(f32_to_bf16(o[3])) << 16);
+    *reinterpret_cast<uint2 *>(v.C + (v.out_base + row) * a.Nout + n) = packed;
   }
 }
 
@@ -1094,7 +1237,7 @@ hipError_t launch_bf16(const GemmArgs &a, const GemmGroups &g, Epilogue epi, int
 }
 
 constexpr int kSplitCap = 8;
-constexpr int64_t kSplitMaxRows = 8192;   // partial rows (reduce grid.y, scratch size)
+constexpr int64_t kSplitMaxRows = 4096;   // partial rows (reduce grid.y, scratch size)
 
 int64_t split_rows(const GemmGroups &g) {
   return g.max_routed_rows + static_cast<int64_t>(g.n_shared) * g.T_sh;
@@ -1106,11 +1249,15 @@ hipError_t launch_bf16_stream(const GemmArgs &a, const GemmGroups &g, Epilogue e
   StreamSplit sp{};
   sp.ks_cap = 1;
   const int64_t prows = split_rows(g);
-  if (g.split_ws && g.split_cap > 1 && prows <= kSplitMaxRows) {
-    sp.ks_used = static_cast<int *>(g.split_ws);
-    sp.partial = reinterpret_cast<float *>(static_cast<char *>(g.split_ws) + 256);
-    sp.part_rows = g.max_routed_rows;
-    sp.ks_cap = g.split_cap < kSplitCap ? g.split_cap : kSplitCap;
+  if (g.split_ws && prows <= kSplitMaxRows && g.split_bytes > 256) {
+    const int64_t per = prows * g.Nout * static_cast<int64_t>(sizeof(float));
+    const int64_t cap = (static_cast<int64_t>(g.split_bytes) - 256) / per;
+    if (cap > 1) {
+      sp.ks_used = static_cast<int *>(g.split_ws);
+      sp.partial = reinterpret_cast<float *>(static_cast<char *>(g.split_ws) + 256);
+      sp.part_rows = g.max_routed_rows;
+      sp.ks_cap = static_cast<int>(cap < kSplitCap ? cap : kSplitCap);
+    }
   }
   const unsigned grid =
       persistent_grid(tiles_upper_bound(g, 32 * NTB, 128 * MB) * sp.ks_cap, per_cu);
@@ -1130,23 +1277,46 @@ hipError_t launch_bf16_stream(const GemmArgs &a, const GemmGroups &g, Epilogue e
   return hipGetLastError();
 }
 
+constexpr int64_t kRsPieceBytes = 256 * 256 * sizeof(float);
+constexpr int kRsMaxBlocks = 256;
+
 template <int GM>
 hipError_t launch_bf16_rs(const GemmArgs &a, const GemmGroups &g, Epilogue epi, hipStream_t s) {
   const unsigned grid = persistent_grid(tiles_upper_bound(g, 256, 256), 1);
+  RsSplit sp{};
+  if (g.split_ws && g.K / 64 >= 64) {
+    sp.max_blocks = static_cast<int>(static_cast<int64_t>(g.split_bytes) / kRsPieceBytes);
+    if (sp.max_blocks >= static_cast<int>(grid)) sp.partial = static_cast<float *>(g.split_ws);
+  }
   if (epi == kEpiBiasSilu)
-    hipLaunchKernelGGL((grouped_gemm_bf16_rs_kernel<kEpiBiasSilu, GM>), dim3(grid), dim3(256), 0, s, a);
+    hipLaunchKernelGGL((grouped_gemm_bf16_rs_kernel<kEpiBiasSilu, GM, false>), dim3(grid), dim3(256), 0, s, a, sp);
   else
-    hipLaunchKernelGGL((grouped_gemm_bf16_rs_kernel<kEpiBias, GM>), dim3(grid), dim3(256), 0, s, a);
+    hipLaunchKernelGGL((grouped_gemm_bf16_rs_kernel<kEpiBias, GM, false>), dim3(grid), dim3(256), 0, s, a, sp);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || !sp.partial) return e;
+  hipLaunchKernelGGL((grouped_gemm_bf16_rs_kernel<kEpiBias, GM, true>), dim3(grid), dim3(256), 0, s, a, sp);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  // at most half of each XCD's workgroups hold remainder tiles; four
+  // fixup workgroups per tile
+  const dim3 fgrid(static_cast<unsigned>(kXcds * 4 * (grid / kXcds / 2 > 0 ? grid / kXcds / 2 : 1)));
+  if (epi == kEpiBiasSilu)
+    hipLaunchKernelGGL((rs_fixup_kernel<kEpiBiasSilu, GM>), fgrid, dim3(256), 0, s, a, sp, static_cast<int>(grid));
+  else
+    hipLaunchKernelGGL((rs_fixup_kernel<kEpiBias, GM>), fgrid, dim3(256), 0, s, a, sp, static_cast<int>(grid));
   return hipGetLastError();
 }
 
 }  // namespace
 
-size_t grouped_gemm_split_bytes(const GemmGroups &g, int cap) {
+size_t grouped_gemm_split_bytes(const GemmGroups &g) {
+  // K split of the stream kernel (small products), or of the last round of
+  // the 256x256 kernel (one 256x256 float32 tile per workgroup)
   const int64_t prows = split_rows(g);
-  if (cap <= 1 || prows > kSplitMaxRows) return 0;
-  if (cap > kSplitCap) cap = kSplitCap;
-  return 256 + sizeof(float) * static_cast<size_t>(cap) * prows * g.Nout;
+  const size_t stream = prows <= kSplitMaxRows
+                            ? 256 + sizeof(float) * static_cast<size_t>(kSplitCap) * prows * g.Nout
+                            : 0;
+  const size_t rs = static_cast<size_t>(kRsMaxBlocks) * kRsPieceBytes;
+  return stream > rs ? stream : rs;
 }
 
 hipError_t launch_grouped_gemm(bool bf16, const GemmGroups &g, Epilogue epi, hipStream_t s) {

@@ -92,7 +92,7 @@ size_t layer_split_bytes(const moe_config *c) {
   g.T_sh = c->T;
   g.max_routed_rows = routed_rows_bound(c);
   g.Nout = c->d_ff > c->d_model ? c->d_ff : c->d_model;
-  return moe::grouped_gemm_split_bytes(g, 8);
+  return moe::grouped_gemm_split_bytes(g);
 }
 
 LayerWs layer_ws(const moe_config *c, void *base) {
@@ -197,7 +197,7 @@ size_t moe_grouped_ffn_workspace_size(const moe_config *cfg, int32_t n_groups, i
   g.n_routed = n_groups;
   g.max_routed_rows = max_rows;
   g.Nout = cfg->d_ff > cfg->d_model ? cfg->d_ff : cfg->d_model;
-  return moe::grouped_gemm_split_bytes(g, 8);
+  return moe::grouped_gemm_split_bytes(g);
 }
 
 int moe_grouped_ffn(const moe_config *cfg, int32_t n_groups, const void *x_rows,
@@ -230,7 +230,7 @@ int moe_grouped_ffn(const moe_config *cfg, int32_t n_groups, const void *x_rows,
   g.max_routed_rows = max_rows;
   g.max_group_rows = max_rows;
   g.split_ws = ws && need ? ws : nullptr;
-  g.split_cap = g.split_ws ? 8 : 1;
+  g.split_bytes = g.split_ws ? need : 0;
   st = hip_status(moe::launch_grouped_gemm(bf16, g, moe::kEpiBiasSilu, s));
   if (st != MOE_OK) return st;
   g.A = h;
@@ -332,7 +332,7 @@ int moe_layer_forward_events(const moe_config *cfg, const moe_weights *w, const 
   g.max_routed_rows = routed_rows_bound(cfg);
   g.max_group_rows = group_rows_bound(cfg);
   g.split_ws = L.split;
-  g.split_cap = L.split ? 8 : 1;
+  g.split_bytes = L.split ? layer_split_bytes(cfg) : 0;
   if ((st = mark(MOE_STAGE_UP)) != MOE_OK) return st;
   st = hip_status(moe::launch_grouped_gemm(bf16, g, moe::kEpiBiasSilu, s));
   if (st != MOE_OK) return st;

@@ -72,16 +72,16 @@ struct GemmGroups {
   int Nout, K;
   int64_t max_routed_rows;   // host upper bound on offsets[n_routed]
   int64_t max_group_rows;    // host upper bound on the rows of one routed group
-  // Optional scratch for splitting K when a product has too few units to
-  // fill the chip: split_cap partial sums of (max_routed_rows + n_shared *
-  // T_sh) rows x Nout floats, plus one int (grouped_gemm_split_bytes).
+  // Optional scratch (split_bytes bytes, 256-aligned) for splitting K when
+  // a product's work does not divide evenly over the chip; NULL: never split.
   void *split_ws;
-  int split_cap;
+  size_t split_bytes;
 };
 
-// Bytes of split scratch launch_grouped_gemm can use for this product
-// (0 when it never splits such a product).
-size_t grouped_gemm_split_bytes(const GemmGroups &g, int cap);
+// Scratch bytes with which launch_grouped_gemm splits this product (and
+// every smaller one) as it sees fit; needs only Nout, n_routed, n_shared,
+// T_sh and max_routed_rows.
+size_t grouped_gemm_split_bytes(const GemmGroups &g);
 
 enum Epilogue { kEpiBias = 0, kEpiBiasSilu = 1 };
 

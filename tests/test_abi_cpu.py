@@ -118,7 +118,9 @@ def test_grouped_ffn_split_workspace_size(B):
     n = B.grouped_ffn_workspace_size(bf, 256, 1024)
     # one int, then up to 8 float32 partial sums of every row x max(d, f)
     assert n == 256 + 4 * 8 * 1024 * 7168
-    assert B.grouped_ffn_workspace_size(bf, 256, 1 << 20) == 0   # large products never split
+    # large products only split the last round of 256x256 tiles: one float32
+    # tile per workgroup of up to 256
+    assert B.grouped_ffn_workspace_size(bf, 256, 1 << 20) == 256 * 256 * 256 * 4
     f32 = B.config(64, 128, 8, 2, 0, 256, "f32")
     assert B.grouped_ffn_workspace_size(f32, 8, 128) == 0
     assert B.grouped_ffn_workspace_size(bf, 0, 1024) == 0

@@ -220,15 +220,21 @@ FFN_CASES = [
     ("bf16_large_groups", [385, 0, 700, 513], 192, 320, "bf16", True),
     # one and two k-steps of 64
     ("bf16_large_short_k", [400, 450], 64, 128, "bf16", False),
+    # a loose row bound widens the grid so that every XCD's tiles form a
+    # partial round, which is split along K and reassembled: the first Linear
+    # in 2 pieces, then the second in 4
+    ("bf16_ksplit_up", [700, 300, 520], 4096, 2048, "bf16", True, 8192),
+    ("bf16_ksplit_down", [700, 300, 520], 1024, 8192, "bf16", True, 8192),
 ]
 
 
 @pytest.mark.parametrize("case", FFN_CASES, ids=lambda c: c[0])
 def test_grouped_ffn_matches_oracle(case):
     b = B()
-    name, rows, d, f, dtype, eb = case
+    name, rows, d, f, dtype, eb = case[:6]
     G = len(rows)
     R = int(sum(rows))
+    max_rows = case[6] if len(case) > 6 else R
     wl = W.custom_workload(name, T=max(R, 1), d_model=d, n_routed=G, top_k=1, n_shared=0, d_ff=f,
                            dtype=dtype, expert_bias=eb)
     cfg = cfg_of(wl)
@@ -240,11 +246,11 @@ def test_grouped_ffn_matches_oracle(case):
     routed, _ = providers_host(wl)
     H, Y = oracle.grouped_ffn(host(x_rows), offs, routed, G)
     # without scratch, then with the scratch that lets small products split K
-    nws = b.grouped_ffn_workspace_size(cfg, G, R)
+    nws = b.grouped_ffn_workspace_size(cfg, G, max_rows)
     for ws in (None, torch.empty(max(nws, 1), dtype=torch.uint8, device="cuda") if nws else None):
         h = torch.zeros((max(R, 1), f), dtype=act, device="cuda")
         y = torch.zeros((max(R, 1), d), dtype=act, device="cuda")
-        b.grouped_ffn(cfg, G, x_rows, offsets, R, w1, b1, w2, b2, h, y, ws=ws)
+        b.grouped_ffn(cfg, G, x_rows, offsets, max_rows, w1, b1, w2, b2, h, y, ws=ws)
         torch.cuda.synchronize()
         assert rel_l2(host(h)[:R], H) <= TOL[dtype]
         assert rel_l2(host(y)[:R], Y) <= TOL[dtype]
