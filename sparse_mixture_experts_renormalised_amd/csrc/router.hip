@@ -147,6 +147,117 @@ __global__ __launch_bounds__(256) void router_logits_kernel(
   }
 }
 
+// Short batches (and narrow routers) have few logits, each a long chain, so
+// the LDS tiles above cannot keep enough memory traffic in flight.  Here a
+// workgroup of 128 threads owns 16 tokens x 8 experts, one logit per thread,
+// and streams 64-wide k-chunks of x (bf16, as stored) and W (float32) into a
+// ring of S LDS stages with global-to-LDS copies issued S-1 chunks ahead.  A
+// copy instruction moves 1 KB: 8 rows of x or 4 rows of W.  x rows are 128
+// bytes of 8 pieces; piece c of row r sits at c ^ ((r >> 1) & 7), so the 16
+// tokens read by a 16-lane group hit distinct banks; the W row of such a
+// group is one broadcast address.
+namespace ring {
+constexpr int NT = 128, BT = 16, BE = 8, KC = 64;
+
+__device__ __forceinline__ uint32_t lds_addr(const void *p) {
+  return static_cast<uint32_t>(
+      reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) const void *)p));
+}
+
+// One wave-wide copy of 64 x 16 bytes into the LDS block at byte address m0.
+__device__ __forceinline__ void dma16(const void *src, uint32_t m0) {
+  asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, off" : : "v"(src), "{m0}"(m0) : "memory");
+}
+
+template <int N>
+__device__ __forceinline__ void wait_and_barrier() {
+  asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)" ::"n"(N) : "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+template <int LPS, int MAXN>
+__device__ __forceinline__ void wait_chunks(int n) {
+  if constexpr (MAXN >= 0) {
+    if (n >= MAXN) {
+      wait_and_barrier<MAXN * LPS>();
+      return;
+    }
+    wait_chunks<LPS, MAXN - 1>(n);
+  }
+}
+}  // namespace ring
+
+template <int S>
+__global__ __launch_bounds__(128) void router_logits_ring_kernel(
+    const uint16_t *__restrict__ x, const float *__restrict__ w, const float *__restrict__ bias,
+    float *__restrict__ logits, int64_t T, int d, int N) {
+  using namespace ring;
+  constexpr int XB = BT * KC * 2;                // bytes of x per stage (2 KB)
+  constexpr int WB = BE * KC * 4;                // bytes of W per stage (2 KB)
+  constexpr int STAGE = XB + WB;
+  constexpr int LPS = 2;                         // copies per wave per stage
+  static_assert((S - 2) * LPS <= 63, "vmcnt range");
+  __shared__ __attribute__((aligned(16))) uint8_t s_ring[S * STAGE];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = uniform(tid >> 6);
+  const int tt = tid & 15, te = tid >> 4;
+  const int64_t t0 = static_cast<int64_t>(blockIdx.x) * BT;
+  const int e0 = blockIdx.y * BE;
+  const uint32_t ring0 = uniform(static_cast<int>(lds_addr(s_ring)));
+
+  // wave w copies x rows 8w .. 8w+7 and W rows 4w .. 4w+3 of every chunk
+  const int xr = 8 * wave + (lane >> 3);
+  int64_t xt = t0 + xr;
+  if (xt >= T) xt = T - 1;
+  const uint16_t *x_src = x + xt * d + ((lane & 7) ^ ((xr >> 1) & 7)) * 8;
+  const int wr = 4 * wave + (lane >> 4);
+  const int we = min(e0 + wr, N - 1);
+  const float *w_src = w + static_cast<int64_t>(we) * d + (lane & 15) * 4;
+  auto issue = [&](int c, int st) {
+    const uint32_t base = ring0 + static_cast<uint32_t>(st) * STAGE;
+    dma16(x_src + c * KC, base + wave * 1024);
+    dma16(w_src + c * KC, base + XB + wave * 1024);
+  };
+
+  const int nch = d / KC;
+  float acc = 0.0f;
+  const int pro = min(S - 1, nch);
+  for (int c = 0; c < pro; ++c) issue(c, c % S);
+  for (int c = 0; c < nch; ++c) {
+    const int later = min(S - 2, nch - 1 - c);
+    if (later == S - 2) wait_and_barrier<(S - 2) * LPS>();
+    else wait_chunks<LPS, S - 3>(later);
+    if (c + S - 1 < nch) issue(c + S - 1, (c + S - 1) % S);
+    const uint8_t *st = s_ring + (c % S) * STAGE;
+    const uint16_t *xs = reinterpret_cast<const uint16_t *>(st) + tt * KC;
+    const float *ws = reinterpret_cast<const float *>(st + XB) + te * KC;
+#pragma unroll
+    for (int pc = 0; pc < KC / 8; ++pc) {
+      const uint4 xq = *reinterpret_cast<const uint4 *>(xs + ((pc ^ ((tt >> 1) & 7)) << 3));
+      const float4 wa = *reinterpret_cast<const float4 *>(ws + pc * 8);
+      const float4 wb = *reinterpret_cast<const float4 *>(ws + pc * 8 + 4);
+      acc = __builtin_fmaf(__uint_as_float(xq.x << 16), wa.x, acc);
+      acc = __builtin_fmaf(__uint_as_float(xq.x & 0xFFFF0000u), wa.y, acc);
+      acc = __builtin_fmaf(__uint_as_float(xq.y << 16), wa.z, acc);
+      acc = __builtin_fmaf(__uint_as_float(xq.y & 0xFFFF0000u), wa.w, acc);
+      acc = __builtin_fmaf(__uint_as_float(xq.z << 16), wb.x, acc);
+      acc = __builtin_fmaf(__uint_as_float(xq.z & 0xFFFF0000u), wb.y, acc);
+      acc = __builtin_fmaf(__uint_as_float(xq.w << 16), wb.z, acc);
+      acc = __builtin_fmaf(__uint_as_float(xq.w & 0xFFFF0000u), wb.w, acc);
+    }
+  }
+  const int64_t t = t0 + tt;
+  const int e = e0 + te;
+  if (t < T && e < N) {
+    float v = acc;
+    if (bias) v = v + bias[e];
+    logits[t * N + e] = v;
+  }
+}
+
 // Key order: a beats b iff a.v > b.v, or equal values and a.i < b.i.
 __device__ __forceinline__ bool key_better(float va, int ia, float vb, int ib) {
   return va > vb || (va == vb && ia < ib);
@@ -205,10 +316,10 @@ __global__ __launch_bounds__(256) void topk_gates_kernel(const float *__restrict
 hipError_t launch_router_logits(bool bf16, const void *x, const float *w, const float *bias,
                                 float *logits, int64_t T, int d, int N, hipStream_t s) {
   if (T <= 0) return hipSuccess;
-  // Block shapes measured on MI355X: wide routers over many tokens use 32x64
-  // blocks with 2x4 logits per thread, mid-sized ones 32x32 with 2x2, and
-  // short batches or narrow routers 64x8 with 2x1, so that they still spread
-  // over the chip.
+  // Shapes measured on MI355X: few logits in all (a decode batch, a narrow
+  // router) go to the LDS-ring kernel, one logit per thread; otherwise wide
+  // routers over many tokens use 32x64 blocks with 2x4 logits per thread,
+  // mid-sized ones 32x32 with 2x2, and the rest 64x8 with 2x1.
   const int64_t TN = T * static_cast<int64_t>(N);
   const int kc32 = d % 32 == 0;
 #define MOE_ROUTER_LAUNCH(BT, BE, MT, ME, KC)                                                   \
@@ -221,6 +332,13 @@ hipError_t launch_router_logits(bool bf16, const void *x, const float *w, const 
     else                                                                                        \
       hipLaunchKernelGGL((router_logits_kernel<BT, BE, MT, ME, KC, false>), grid, dim3(256), 0,\
                          s, x, w, bias, logits, T, d, N);                                       \
+  }
+  if (bf16 && d % 64 == 0 && TN < (int64_t(1) << 17)) {
+    const dim3 grid(static_cast<unsigned>((T + ring::BT - 1) / ring::BT),
+                    static_cast<unsigned>((N + ring::BE - 1) / ring::BE));
+    hipLaunchKernelGGL((router_logits_ring_kernel<12>), grid, dim3(ring::NT), 0, s,
+                       static_cast<const uint16_t *>(x), w, bias, logits, T, d, N);
+    return hipGetLastError();
   }
   if (N >= 64 && TN >= (int64_t(1) << 19)) {
     if (kc32) MOE_ROUTER_LAUNCH(32, 64, 2, 4, 32) else MOE_ROUTER_LAUNCH(32, 64, 2, 4, 16)
