@@ -1352,7 +1352,7 @@ hipError_t launch_grouped_gemm(bool bf16, const GemmGroups &g, Epilogue epi, hip
     if (e != hipSuccess) return e;
     a.cls_lo = 0;
     a.cls_hi = kStreamRows;
-    return launch_bf16_stream<1, 2, 6>(a, g, epi, 1, s);
+    return launch_bf16_stream<2, 2, 3>(a, g, epi, 1, s);
   }
   const unsigned grid = persistent_grid(tiles_upper_bound(g, 64, 64), 4);
   if (bf16) {
