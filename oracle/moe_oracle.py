@@ -40,6 +40,15 @@ the design notes):
 6. Expert FFN E(z) = W2 SiLU(W1 z + b1) + b2, SiLU(z) = z / (1 + e^-z).
 7. Output y_t = sum of shared experts + sum of kept gate-weighted routed
    experts; no residual term.
+8. Selection-only bias (the bias-based balancing of [TopK] section 負荷均衡,
+   which steers the load without changing the loss): when asked for, the
+   bias enters only the selection key fl32(logit + bias[e]); the gates are
+   the softmax over the K kept unbiased logits, and the logits returned are
+   the unbiased ones.
+9. Balance statistics ([DSMoE] balance-loss equation): f_j is the share of
+   the T*K routed assignments that go to expert j (so the f_j sum to 1 and a
+   perfectly even routing gives L = alpha), P_j the mean over tokens of the
+   full softmax over all N logits.
 """
 from __future__ import annotations
 
@@ -137,8 +146,17 @@ def renormalised_gates(logits: np.ndarray, idx: np.ndarray) -> np.ndarray:
     return p / p.sum(axis=1, keepdims=True)
 
 
-def route(x, w_r, bias, K: int):
-    """Router + top-K + renormalised gates: (logits f32, idx i32, gates f64)."""
+def route(x, w_r, bias, K: int, selection_only_bias: bool = False):
+    """Router + top-K + renormalised gates: (logits f32, idx i32, gates f64).
+
+    With ``selection_only_bias`` (reading 8) the bias only shifts the
+    selection key; the logits returned and the gates are unbiased.
+    """
+    if selection_only_bias and bias is not None:
+        logits = router_logits(x, w_r, None)
+        key = logits + np.asarray(bias, dtype=np.float32)[None, :]   # float32, one rounding
+        idx = select_top_k(key, K)
+        return logits, idx, renormalised_gates(logits, idx)
     logits = router_logits(x, w_r, bias)
     idx = select_top_k(logits, K)
     gates = renormalised_gates(logits, idx)
@@ -281,7 +299,8 @@ def layer_forward(x, w_r, bias, routed_expert: Callable[[int], tuple],
                   shared_expert: Optional[Callable[[int], tuple]], *, top_k: int,
                   n_shared: int, capacity_factor: float = 0.0,
                   capacity: Optional[int] = None,
-                  tokens: Optional[Sequence[int]] = None) -> Dict[str, np.ndarray]:
+                  tokens: Optional[Sequence[int]] = None,
+                  selection_only_bias: bool = False) -> Dict[str, np.ndarray]:
     """Routing for all tokens and y for ``tokens`` (default: all), float64.
 
     The routing (logits, selection, gates, dispatch) always covers every token,
@@ -292,7 +311,7 @@ def layer_forward(x, w_r, bias, routed_expert: Callable[[int], tuple],
     x = np.asarray(x, dtype=np.float32)
     T = x.shape[0]
     N = np.asarray(w_r).shape[0]
-    logits, idx, gates = route(x, w_r, bias, top_k)
+    logits, idx, gates = route(x, w_r, bias, top_k, selection_only_bias)
     C = capacity_limit(capacity_factor, T, top_k, N, capacity)
     disp = dispatch(idx, N, C)
     toks = np.arange(T) if tokens is None else np.asarray(tokens, dtype=np.int64)
@@ -318,7 +337,8 @@ def layer_forward(x, w_r, bias, routed_expert: Callable[[int], tuple],
 
 def dense_masked_forward(x, w_r, bias, routed_expert, shared_expert, *, top_k: int,
                          n_shared: int, capacity_factor: float = 0.0,
-                         capacity: Optional[int] = None) -> np.ndarray:
+                         capacity: Optional[int] = None,
+                         selection_only_bias: bool = False) -> np.ndarray:
     """Brute force in the shape of the pages' reference layer.
 
     Every routed expert is evaluated on every token; for each slot k and each
@@ -328,7 +348,7 @@ def dense_masked_forward(x, w_r, bias, routed_expert, shared_expert, *, top_k: i
     x = np.asarray(x, dtype=np.float32)
     T, d = x.shape
     N = np.asarray(w_r).shape[0]
-    logits, idx, gates = route(x, w_r, bias, top_k)
+    logits, idx, gates = route(x, w_r, bias, top_k, selection_only_bias)
     C = capacity_limit(capacity_factor, T, top_k, N, capacity)
     # kept mask by brute force: count earlier tokens with the same expert
     kept = np.ones((T, top_k), dtype=bool)
@@ -355,7 +375,7 @@ def dense_masked_forward(x, w_r, bias, routed_expert, shared_expert, *, top_k: i
 # ---------------------------------------------------------------------------
 
 def balance_statistics(logits: np.ndarray, idx: np.ndarray, alpha: float = 0.01):
-    """f_j (share of routed assignments), P_j (mean full softmax prob), loss.
+    """f_j (share of routed assignments), P_j (mean full softmax prob), loss (reading 9).
 
     f_j = (number of (t,k) with idx = j) / (T*K); P_j = mean_t softmax(logits_t)_j;
     L = alpha * N * sum_j f_j P_j.  float64.

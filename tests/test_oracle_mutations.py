@@ -97,3 +97,31 @@ def test_dropped_shared_experts_are_caught(monkeypatch):
         return orig(*a, **k)
     patch(monkeypatch, "layer_forward", bad)
     expect_failure(lambda: pins.test_layer_equals_dense_masked_brute_force(pins.SMALL[1]))
+
+
+def test_biased_gates_in_selection_only_mode_are_caught(monkeypatch):
+    orig = oracle.renormalised_gates
+    real_route = mo.route
+
+    def bad(x, w_r, bias, K, selection_only_bias=False):
+        if selection_only_bias and bias is not None:
+            logits = mo.router_logits(x, w_r, bias)      # bias leaks into the gates
+            idx = mo.select_top_k(logits, K)
+            return mo.router_logits(x, w_r, None), idx, orig(logits, idx)
+        return real_route(x, w_r, bias, K, selection_only_bias)
+    patch(monkeypatch, "route", bad)
+    with pytest.raises(AssertionError):
+        pins.test_selection_only_bias_steers_selection_not_gates()
+
+
+def test_assignment_share_over_tokens_instead_of_assignments_is_caught(monkeypatch):
+    def bad(logits, idx, alpha=0.01):
+        l64 = np.asarray(logits, dtype=np.float64)
+        T, N = l64.shape
+        s = np.exp(l64 - l64.max(axis=1, keepdims=True))
+        s /= s.sum(axis=1, keepdims=True)
+        f = np.bincount(np.asarray(idx).ravel(), minlength=N) / T      # share of tokens
+        P = s.mean(axis=0)
+        return f, P, float(alpha * N * np.sum(f * P))
+    patch(monkeypatch, "balance_statistics", bad)
+    expect_failure(pins.test_balance_statistics_invariants_and_even_routing)

@@ -455,3 +455,88 @@ def test_fine_grained_workload_is_the_pages_split():
     d_ff_coarse = wl.d_ff * fg["m"]
     # active routed width per token is unchanged by the split
     assert wl.top_k * wl.d_ff == fg["K"] * d_ff_coarse
+
+
+# ---------------------------------------------------------------------------
+# balance statistics ([DSMoE] balance-loss equation, reading 9)
+# ---------------------------------------------------------------------------
+
+def test_balance_statistics_hand_examples():
+    ln3 = math.log(3.0)
+    # softmax rows (1/4, 3/4) and (3/4, 1/4): P = (1/2, 1/2); one token per
+    # expert: f = (1/2, 1/2); L = alpha * 2 * (1/4 + 1/4) = alpha
+    f, P, L = oracle.balance_statistics(np.array([[0.0, ln3], [ln3, 0.0]]), np.array([[1], [0]]), 0.01)
+    assert np.allclose(P, [0.5, 0.5], atol=1e-15) and np.allclose(f, [0.5, 0.5])
+    assert abs(L - 0.01) < 1e-15
+    # both tokens pick expert 1 with probability 3/4: L = alpha * 2 * 3/4
+    f, P, L = oracle.balance_statistics(np.array([[0.0, ln3], [0.0, ln3]]), np.array([[1], [1]]), 0.01)
+    assert np.allclose(P, [0.25, 0.75], atol=1e-15) and np.allclose(f, [0.0, 1.0])
+    assert abs(L - 0.015) < 1e-15
+
+
+def test_balance_statistics_invariants_and_even_routing():
+    rng = np.random.default_rng(5)
+    T, N, K = 96, 16, 4
+    logits = rng.standard_normal((T, N)).astype(np.float32)
+    idx = oracle.select_top_k(logits, K)
+    f, P, L = oracle.balance_statistics(logits, idx, 0.01)
+    assert abs(f.sum() - 1.0) < 1e-12 and abs(P.sum() - 1.0) < 1e-12
+    # brute-force definition, token by token
+    Pb = np.zeros(N)
+    for t in range(T):
+        e = np.exp(logits[t].astype(np.float64))
+        Pb += e / e.sum()
+    assert np.allclose(P, Pb / T, rtol=1e-12)
+    assert np.allclose(f * T * K, [np.sum(idx == j) for j in range(N)])
+    # equal logits and a perfectly even routing give L = alpha
+    even = np.array([[(t * K + k) % N for k in range(K)] for t in range(T)])
+    f, P, L = oracle.balance_statistics(np.zeros((T, N)), even, 0.01)
+    assert np.allclose(P, 1.0 / N) and np.allclose(f, 1.0 / N) and abs(L - 0.01) < 1e-14
+
+
+# ---------------------------------------------------------------------------
+# selection-only bias (reading 8)
+# ---------------------------------------------------------------------------
+
+def _tiny_router(seed, T=24, d=32, N=8):
+    rng = np.random.default_rng(seed)
+    x = rng.standard_normal((T, d)).astype(np.float32)
+    w = (rng.standard_normal((N, d)) / math.sqrt(d)).astype(np.float32)
+    b = rng.standard_normal(N).astype(np.float32)
+    return x, w, b
+
+
+def test_selection_only_bias_of_zero_is_the_plain_router():
+    x, w, _ = _tiny_router(1)
+    z = np.zeros(w.shape[0], dtype=np.float32)
+    l0, i0, g0 = oracle.route(x, w, None, 3)
+    l1, i1, g1 = oracle.route(x, w, z, 3, selection_only_bias=True)
+    assert np.array_equal(l0, l1) and np.array_equal(i0, i1) and np.array_equal(g0, g1)
+
+
+def test_selection_only_bias_steers_selection_not_gates():
+    x, w, _ = _tiny_router(2)
+    N = w.shape[0]
+    b = np.zeros(N, dtype=np.float32)
+    b[5] = 1.0e4                      # expert 5 always wins the selection
+    logits, idx, gates = oracle.route(x, w, b, 2, selection_only_bias=True)
+    assert np.all(idx[:, 0] == 5)
+    plain = x @ w.T                   # the returned logits carry no bias
+    assert np.allclose(logits, plain, atol=1e-5)
+    # gate of expert 5 from the unbiased logits of the two kept experts
+    for t in range(x.shape[0]):
+        l5, lo = float(logits[t, 5]), float(logits[t, idx[t, 1]])
+        assert abs(gates[t, 0] - 1.0 / (1.0 + math.exp(lo - l5))) < 1e-12
+
+
+def test_selection_only_bias_brute_force():
+    x, w, b = _tiny_router(3, N=6)
+    K = 3
+    logits, idx, gates = oracle.route(x, w, b, K, selection_only_bias=True)
+    key = logits + b[None, :]
+    for t in range(x.shape[0]):
+        best = max(itertools.combinations(range(w.shape[0]), K),
+                   key=lambda s: (sum(float(key[t, j]) for j in s), [-j for j in s]))
+        assert sorted(best) == sorted(idx[t].tolist())
+        kept = np.exp(logits[t, idx[t]].astype(np.float64))
+        assert np.allclose(gates[t], kept / kept.sum(), rtol=1e-12)
