@@ -44,7 +44,9 @@
  *
  * Numerical contract
  *   - Logits: float32, per (t, e) one fused multiply-add chain over k
- *     ascending starting at +0, then + router_bias[e] with one rounding.
+ *     ascending starting at +0, then + router_bias[e] with one rounding
+ *     (with MOE_BIAS_SELECTION_ONLY the bias is added to the selection key
+ *     only).
  *   - Selection: the K largest logits, key (logit desc, expert id asc); slot
  *     k of a token holds its k-th best expert.
  *   - Gates: softmax over the K kept logits (float32), which equals
@@ -90,7 +92,16 @@ typedef struct {
     int32_t dtype;            /* moe_dtype of x, expert weights/biases, hidden, y  */
     float capacity_factor;    /* <= 0: no factor-derived limit                     */
     int32_t capacity;         /* >= 0: explicit per-expert limit; -1: use factor   */
+    int32_t bias_mode;        /* MOE_BIAS_IN_LOGIT or MOE_BIAS_SELECTION_ONLY      */
 } moe_config;
+
+/* How router_bias enters the routing.
+ *   MOE_BIAS_IN_LOGIT: the bias is part of the logit, for selection and gates.
+ *   MOE_BIAS_SELECTION_ONLY: the bias-based balancing of [TopK] section
+ *     負荷均衡 (steers the load without changing the loss): selection uses the
+ *     key fl32(logit + bias[e]); the gates are the softmax over the K kept
+ *     unbiased logits, and the logits written are the unbiased ones. */
+enum { MOE_BIAS_IN_LOGIT = 0, MOE_BIAS_SELECTION_ONLY = 1 };
 
 /* Expert and router weights, nn.Linear layout (out_features, in_features). */
 typedef struct {
@@ -212,6 +223,24 @@ int moe_layer_forward_events(const moe_config *cfg, const moe_weights *w, const 
                              void *y, int32_t *topk_idx, float *topk_gate, int32_t *counts,
                              void *ws, size_t ws_bytes, void *const *stage_events,
                              void *stream);
+
+/*
+ * moe_balance_stats — load statistics of one routing ([DSMoE] section
+ * ルーティングとバランス損失, balance-loss equation):
+ *   f[j]  = (number of (t, k) with topk_idx[t][k] == j) / (T * K)
+ *   P[j]  = (1/T) * sum_t softmax(logits[t])_j   (softmax over all N)
+ *   *loss = alpha * N * sum_j f[j] * P[j]
+ *   logits      [T][N] float32 (as written by moe_route)
+ *   topk_idx    [T][K] int32, values in [0, N)
+ *   f, P        [N] float32 outputs; loss [1] float32 output (device)
+ *   ws          device workspace of moe_balance_stats_workspace_size(cfg) bytes
+ * Counts are exact; P and the loss are float32 sums in a fixed order, so the
+ * results do not depend on timing.  Only T, n_routed and top_k are read.
+ */
+int moe_balance_stats(const moe_config *cfg, const float *logits, const int32_t *topk_idx,
+                      float alpha, float *f, float *P, float *loss, void *ws, size_t ws_bytes,
+                      void *stream);
+size_t moe_balance_stats_workspace_size(const moe_config *cfg);
 
 /* Per-expert capacity the library applies for cfg (-1 = unlimited). */
 int64_t moe_capacity(const moe_config *cfg);

@@ -23,7 +23,8 @@ STATUS = {0: "ok", -1: "invalid argument", -2: "unsupported size", -3: "workspac
 
 # Symbols declared in include/moe_mi355x.h.
 EXPORTS = ("moe_route", "moe_permute", "moe_permute_workspace_size", "moe_grouped_ffn",
-           "moe_grouped_ffn_workspace_size", "moe_combine", "moe_layer_forward", "moe_layer_forward_events",
+           "moe_grouped_ffn_workspace_size", "moe_combine", "moe_balance_stats",
+           "moe_balance_stats_workspace_size", "moe_layer_forward", "moe_layer_forward_events",
            "moe_layer_workspace_size", "moe_capacity", "moe_status_string", "moe_version")
 STAGES = ("router", "topk", "dispatch", "up", "down", "combine")
 
@@ -39,7 +40,7 @@ class Config(ctypes.Structure):
     _fields_ = [("T", ctypes.c_int64), ("d_model", ctypes.c_int32), ("n_routed", ctypes.c_int32),
                 ("top_k", ctypes.c_int32), ("n_shared", ctypes.c_int32), ("d_ff", ctypes.c_int32),
                 ("dtype", ctypes.c_int32), ("capacity_factor", ctypes.c_float),
-                ("capacity", ctypes.c_int32)]
+                ("capacity", ctypes.c_int32), ("bias_mode", ctypes.c_int32)]
 
 
 class Weights(ctypes.Structure):
@@ -67,6 +68,8 @@ def lib():
             "moe_permute_workspace_size": (Z, [C]),
             "moe_grouped_ffn": (I, [C, ctypes.c_int32, P, P, I64, P, P, P, P, P, P, P, Z, P]),
             "moe_grouped_ffn_workspace_size": (Z, [C, ctypes.c_int32, I64]),
+            "moe_balance_stats": (I, [C, P, P, ctypes.c_float, P, P, P, P, Z, P]),
+            "moe_balance_stats_workspace_size": (Z, [C]),
             "moe_combine": (I, [C, P, P, P, P, P, P]),
             "moe_layer_forward": (I, [C, ctypes.POINTER(Weights), P, P, P, P, P, P, Z, P]),
             "moe_layer_forward_events": (I, [C, ctypes.POINTER(Weights), P, P, P, P, P, P, Z,
@@ -102,11 +105,15 @@ def _check(fn: str, st: int):
         raise MoeError(fn, st)
 
 
+MOE_BIAS_IN_LOGIT, MOE_BIAS_SELECTION_ONLY = 0, 1
+
+
 def config(T, d_model, n_routed, top_k, n_shared, d_ff, dtype, capacity_factor=0.0,
-           capacity=-1) -> Config:
+           capacity=-1, selection_only_bias=False) -> Config:
     dt = {"f32": MOE_F32, "bf16": MOE_BF16, MOE_F32: MOE_F32, MOE_BF16: MOE_BF16}[dtype]
     return Config(int(T), int(d_model), int(n_routed), int(top_k), int(n_shared), int(d_ff),
-                  dt, float(capacity_factor), int(capacity))
+                  dt, float(capacity_factor), int(capacity),
+                  MOE_BIAS_SELECTION_ONLY if selection_only_bias else MOE_BIAS_IN_LOGIT)
 
 
 def capacity(cfg: Config) -> int:
@@ -144,6 +151,18 @@ def grouped_ffn(cfg: Config, n_groups, x_rows, offsets, max_rows, w1, b1, w2, b2
                                                     _ptr(b1), _ptr(w2), _ptr(b2), _ptr(h),
                                                     _ptr(y_rows), _ptr(ws), nbytes,
                                                     _stream(stream)))
+
+
+def balance_stats_workspace_size(cfg: Config) -> int:
+    return int(lib().moe_balance_stats_workspace_size(ctypes.byref(cfg)))
+
+
+def balance_stats(cfg: Config, logits, topk_idx, alpha, f, P, loss, ws, stream=None):
+    nbytes = 0 if ws is None else ws.numel() * ws.element_size()
+    _check("moe_balance_stats", lib().moe_balance_stats(ctypes.byref(cfg), _ptr(logits),
+                                                        _ptr(topk_idx), float(alpha), _ptr(f),
+                                                        _ptr(P), _ptr(loss), _ptr(ws), nbytes,
+                                                        _stream(stream)))
 
 
 def combine(cfg: Config, y_rows, slot_row, topk_gate, shared_out, y, stream=None):

@@ -22,7 +22,8 @@ LIB_DIR = os.path.join(HERE, "_lib")
 LIB = os.path.join(LIB_DIR, "libmoe_mi355x.so")
 ARCH = "gfx950"
 
-SOURCES = ["router.hip", "dispatch.hip", "grouped_gemm.hip", "combine.hip", "moe_api.hip"]
+SOURCES = ["router.hip", "dispatch.hip", "grouped_gemm.hip", "combine.hip", "balance.hip",
+           "moe_api.hip"]
 PER_FILE = {"router.hip": ["-ffp-contract=off"]}
 
 

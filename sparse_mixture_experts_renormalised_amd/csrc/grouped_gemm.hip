@@ -870,6 +870,67 @@ __device__ __forceinline__ int stream_split(int base_units, int nkc, int ks_cap,
 }
 }  // namespace st
 
+// Store of a stream unit: lane holds row r32 of each 32-row block and
+// features 8q + 4h .. +3 of each 32-feature block.  Without a K split the
+// bias, SiLU and bf16 rounding are applied here; with one, the float32 part
+// goes to the partial buffer.
+template <int MB, int NTB, int EPI>
+__device__ __forceinline__ void stream_store(const f32x16_t (&acc)[MB][NTB], const GemmArgs &a,
+                                             const TileView<uint16_t> &v, int g, int nw0, int kp,
+                                             int ks, const StreamSplit &sp, int r32, int h) {
+#pragma unroll
+  for (int j = 0; j < NTB; ++j) {
+    const int64_t lr = v.row0 + 32 * j + r32;
+    if (lr >= v.rows) continue;
+    if (ks > 1) {
+      const int64_t prow = g < a.n_routed
+                               ? v.out_base + lr
+                               : sp.part_rows + static_cast<int64_t>(g - a.n_routed) * a.T_sh + lr;
+      const int64_t nrows = sp.part_rows + static_cast<int64_t>(a.n_shared) * a.T_sh;
+      float *dst = sp.partial + (static_cast<int64_t>(kp) * nrows + prow) * a.Nout;
+#pragma unroll
+      for (int i = 0; i < MB; ++i)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int n = nw0 + 32 * i + 8 * q + 4 * h;
+          if (n < a.Nout) {
+            const f32x16_t &c = acc[i][j];
+            *reinterpret_cast<float4 *>(dst + n) =
+                make_float4(c[4 * q], c[4 * q + 1], c[4 * q + 2], c[4 * q + 3]);
+          }
+        }
+    } else {
+      uint16_t *dst = v.C + (v.out_base + lr) * a.Nout;
+#pragma unroll
+      for (int i = 0; i < MB; ++i)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int n = nw0 + 32 * i + 8 * q + 4 * h;
+          if (n < a.Nout) {
+            float bv[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+            if (v.bias) {
+              const uint2 bq = *reinterpret_cast<const uint2 *>(v.bias + n);
+              bv[0] = __uint_as_float(bq.x << 16);
+              bv[1] = __uint_as_float(bq.x & 0xFFFF0000u);
+              bv[2] = __uint_as_float(bq.y << 16);
+              bv[3] = __uint_as_float(bq.y & 0xFFFF0000u);
+            }
+            float o[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              o[e] = acc[i][j][4 * q + e] + bv[e];
+              if (EPI == kEpiBiasSilu) o[e] = silu_fast(o[e]);
+            }
+            uint2 packed;
+            packed.x = f32_to_bf16(o[0]) | (static_cast<uint32_t>(f32_to_bf16(o[1])) << 16);
+            packed.y = f32_to_bf16(o[2]) | (static_cast<uint32_t>(f32_to_bf16(o[3])) << 16);
+            *reinterpret_cast<uint2 *>(dst + n) = packed;
+          }
+        }
+    }
+  }
+}
+
 template <int MB, int NTB, int S, int EPI>
 __global__ __launch_bounds__(256) void grouped_gemm_bf16_stream_kernel(GemmArgs a, StreamSplit sp) {
   using namespace st;
@@ -992,60 +1053,180 @@ __global__ __launch_bounds__(256) void grouped_gemm_bf16_stream_kernel(GemmArgs 
     }
     stage = (stage + nch) % S;
 
-    // lane holds row r32 of each 32-row block and features 8q + 4h .. +3 of
-    // each 32-feature block
-    const int nw0 = n0 + wave * 32 * MB;
+    stream_store<MB, NTB, EPI>(acc, a, v, g, n0 + wave * 32 * MB, kp, ks, sp, r32, h);
+  }
+}
+
+// Register-ring variant of the stream kernel: the same units and operand
+// layout, but every thread prefetches its share of R 64-wide k-chunks into
+// registers with coalesced 16-byte loads (8 lanes per 128-byte row segment),
+// so R chunks (about 200 KB per CU) are in flight instead of the two or three
+// an LDS ring of this size holds.  Each step writes the next chunk from
+// registers into the other half of a double-buffered, swizzled LDS tile and
+// runs the MFMAs of the current one.  Weights of groups with one row block
+// are loaded with the non-temporal policy.
+namespace rst {
+template <int WCH, int XCH>
+struct Chunk {
+  u32x4_t w[WCH];
+  u32x4_t x[XCH];
+};
+
+template <bool NTW, int WCH, int XCH>
+__device__ __forceinline__ void gload(Chunk<WCH, XCH> &r, const uint16_t *const (&wp)[WCH],
+                                      const uint16_t *const (&xp)[XCH], int c) {
 #pragma unroll
-    for (int j = 0; j < NTB; ++j) {
-      const int64_t lr = v.row0 + 32 * j + r32;
-      if (lr >= v.rows) continue;
-      if (ks > 1) {
-        const int64_t prow = g < a.n_routed
-                                 ? v.out_base + lr
-                                 : sp.part_rows + static_cast<int64_t>(g - a.n_routed) * a.T_sh + lr;
-        const int64_t nrows = sp.part_rows + static_cast<int64_t>(a.n_shared) * a.T_sh;
-        float *dst = sp.partial + (static_cast<int64_t>(kp) * nrows + prow) * a.Nout;
+  for (int i = 0; i < WCH; ++i) {
+    const u32x4_t *src = reinterpret_cast<const u32x4_t *>(wp[i] + c * st::KCH);
+    r.w[i] = NTW ? __builtin_nontemporal_load(src) : *src;
+  }
 #pragma unroll
-        for (int i = 0; i < MB; ++i)
+  for (int i = 0; i < XCH; ++i) r.x[i] = *reinterpret_cast<const u32x4_t *>(xp[i] + c * st::KCH);
+}
+}  // namespace rst
+
+template <int MB, int NTB, int R, bool NTW, int EPI>
+__device__ __forceinline__ void rstream_unit(const GemmArgs &a, const StreamSplit &sp,
+                                             const TileView<uint16_t> &v, int g, int n0, int kp,
+                                             int ks, int kc0, int nch, uint16_t *s_tile, int tid,
+                                             int lane, int wave) {
+  using namespace rst;
+  constexpr int MR = 32 * NTB, NB = 4 * 32 * MB, KCH = st::KCH;
+  constexpr int WCH = NB * 8 / st::NT, XCH = MR * 8 / st::NT;
+  constexpr int HALF = (NB + MR) * KCH;          // bf16 elements per LDS buffer
+  const int r32 = lane & 31, h = lane >> 5;
+  const int crow = tid >> 3, cpc = tid & 7;
+  const uint16_t *wp[WCH];
+  const uint16_t *xp[XCH];
 #pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            const int n = nw0 + 32 * i + 8 * q + 4 * h;
-            if (n < a.Nout) {
-              const f32x16_t &c = acc[i][j];
-              *reinterpret_cast<float4 *>(dst + n) =
-                  make_float4(c[4 * q], c[4 * q + 1], c[4 * q + 2], c[4 * q + 3]);
-            }
-          }
-      } else {
-        uint16_t *dst = v.C + (v.out_base + lr) * a.Nout;
+  for (int i = 0; i < WCH; ++i) {
+    const int n = min(n0 + crow + 32 * i, a.Nout - 1);
+    wp[i] = v.W + static_cast<int64_t>(n) * a.K + kc0 * KCH + cpc * 8;
+  }
 #pragma unroll
-        for (int i = 0; i < MB; ++i)
+  for (int i = 0; i < XCH; ++i) xp[i] = a_row_ptr(a, v, v.row0 + crow + 32 * i) + kc0 * KCH + cpc * 8;
+
+  f32x16_t acc[MB][NTB];
 #pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            const int n = nw0 + 32 * i + 8 * q + 4 * h;
-            if (n < a.Nout) {
-              float bv[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-              if (v.bias) {
-                const uint2 bq = *reinterpret_cast<const uint2 *>(v.bias + n);
-                bv[0] = __uint_as_float(bq.x << 16);
-                bv[1] = __uint_as_float(bq.x & 0xFFFF0000u);
-                bv[2] = __uint_as_float(bq.y << 16);
-                bv[3] = __uint_as_float(bq.y & 0xFFFF0000u);
-              }
-              float o[4];
+  for (int i = 0; i < MB; ++i)
 #pragma unroll
-              for (int e = 0; e < 4; ++e) {
-                o[e] = acc[i][j][4 * q + e] + bv[e];
-                if (EPI == kEpiBiasSilu) o[e] = silu_fast(o[e]);
-              }
-              uint2 packed;
-              packed.x = f32_to_bf16(o[0]) | (static_cast<uint32_t>(f32_to_bf16(o[1])) << 16);
-              packed.y = f32_to_bf16(o[2]) | (static_cast<uint32_t>(f32_to_bf16(o[3])) << 16);
-              *reinterpret_cast<uint2 *>(dst + n) = packed;
-            }
-          }
-      }
+    for (int j = 0; j < NTB; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+
+  auto lstore = [&](const Chunk<WCH, XCH> &ck, int buf) {
+    uint16_t *tw = s_tile + buf * HALF;
+    uint16_t *tx = tw + NB * KCH;
+#pragma unroll
+    for (int i = 0; i < WCH; ++i) {
+      const int r = crow + 32 * i;
+      *reinterpret_cast<u32x4_t *>(tw + r * KCH + (st::swz(r, cpc) << 3)) = ck.w[i];
     }
+#pragma unroll
+    for (int i = 0; i < XCH; ++i) {
+      const int r = crow + 32 * i;
+      *reinterpret_cast<u32x4_t *>(tx + r * KCH + (st::swz(r, cpc) << 3)) = ck.x[i];
+    }
+  };
+  auto mma = [&](int buf) {
+    const uint16_t *tw = s_tile + buf * HALF;
+    const uint16_t *tx = tw + NB * KCH;
+#pragma unroll
+    for (int kst = 0; kst < 4; ++kst) {
+      const int p = 2 * kst + h;
+      bf16x8_t fw[MB], fx[NTB];
+#pragma unroll
+      for (int i = 0; i < MB; ++i) {
+        const int r = wave * 32 * MB + 32 * i + r32;
+        fw[i] = *reinterpret_cast<const bf16x8_t *>(tw + r * KCH + (st::swz(r, p) << 3));
+      }
+#pragma unroll
+      for (int j = 0; j < NTB; ++j) {
+        const int r = 32 * j + r32;
+        fx[j] = *reinterpret_cast<const bf16x8_t *>(tx + r * KCH + (st::swz(r, p) << 3));
+      }
+#pragma unroll
+      for (int i = 0; i < MB; ++i)
+#pragma unroll
+        for (int j = 0; j < NTB; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fw[i], fx[j], acc[i][j], 0, 0, 0);
+    }
+  };
+
+  // Ring slot r holds chunk c with c % R == r (R is even, so LDS buffer c & 1
+  // is r & 1); loads past the end re-read the last chunk (cache hits), so the
+  // steady-state steps have no branches.  Step c: write chunk c+1 from its
+  // slot into the other LDS buffer, refill the slot with chunk c+1+R, run the
+  // MFMAs of chunk c, barrier.
+  static_assert(R % 2 == 0, "even ring");
+  Chunk<WCH, XCH> ring[R];
+#pragma unroll
+  for (int r = 0; r < R; ++r) gload<NTW>(ring[r], wp, xp, min(r, nch - 1));
+  lstore(ring[0], 0);
+  gload<NTW>(ring[0], wp, xp, min(R, nch - 1));
+  __syncthreads();
+  int c0 = 0;
+  for (; c0 + R < nch; c0 += R) {
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      const int nr = (r + 1) % R;
+      lstore(ring[nr], (r + 1) & 1);
+      gload<NTW>(ring[nr], wp, xp, min(c0 + r + 1 + R, nch - 1));
+      mma(r & 1);
+      __syncthreads();
+    }
+  }
+#pragma unroll
+  for (int r = 0; r < R; ++r) {                // the last chunks: no refills
+    const int c = c0 + r;
+    if (c < nch) {
+      if (c + 1 < nch) lstore(ring[(r + 1) % R], (r + 1) & 1);
+      mma(r & 1);
+      __syncthreads();
+    }
+  }
+  stream_store<MB, NTB, EPI>(acc, a, v, g, n0 + wave * 32 * MB, kp, ks, sp, r32, h);
+}
+
+template <int MB, int NTB, int R, int EPI>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void grouped_gemm_bf16_rstream_kernel(GemmArgs a, StreamSplit sp) {
+  using namespace st;
+  constexpr int MR = 32 * NTB, NB = 4 * 32 * MB;
+  __shared__ __attribute__((aligned(16))) uint16_t s_tile[2 * (NB + MR) * KCH];
+  __shared__ int s_pref[kMaxGroups + 1];
+  __shared__ int s_tmp[NT / 64];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = uniform(tid >> 6);
+  const int n_groups = a.n_routed + a.n_shared;
+  const int total_m = build_tile_prefix<NT, MR>(a, s_pref, s_tmp);
+  const int n_nb = (a.Nout + NB - 1) / NB;
+  const int nkc = a.K / KCH;
+  int kc_per;
+  const int ks = stream_split(total_m * n_nb, nkc, sp.ks_cap, gridDim.x, &kc_per);
+  if (blockIdx.x == 0 && threadIdx.x == 0 && sp.ks_used) *sp.ks_used = ks;
+  const int total = total_m * n_nb * ks;
+  const int xcd = blockIdx.x % kXcds;
+  const int slot = blockIdx.x / kXcds;
+  const int nslots = gridDim.x / kXcds;
+  const int part = (total + kXcds - 1) / kXcds;
+  const int begin = xcd * part;
+  const int end = min(total, begin + part);
+  for (int L = begin + slot; L < end; L += nslots) {
+    const int kp = L % ks;
+    const int u = L / ks;
+    const int g = find_group(s_pref, n_groups, u / n_nb);
+    const int mg = s_pref[g + 1] - s_pref[g];
+    const int uu = u - s_pref[g] * n_nb;
+    const int nb = uu / mg, rb = uu % mg;
+    const TileView<uint16_t> v = tile_view<uint16_t>(a, g, rb, MR);
+    const int kc0 = kp * kc_per;
+    const int nch = min(nkc, kc0 + kc_per) - kc0;
+    if (mg == 1)
+      rstream_unit<MB, NTB, R, true, EPI>(a, sp, v, g, nb * NB, kp, ks, kc0, nch, s_tile, tid, lane, wave);
+    else
+      rstream_unit<MB, NTB, R, false, EPI>(a, sp, v, g, nb * NB, kp, ks, kc0, nch, s_tile, tid, lane, wave);
   }
 }
 
@@ -1292,6 +1473,40 @@ hipError_t launch_bf16_stream(const GemmArgs &a, const GemmGroups &g, Epilogue e
 
 constexpr int64_t kRsPieceBytes = 256 * 256 * sizeof(float);
 constexpr int kRsMaxBlocks = 256;
+
+template <int MB, int NTB, int R>
+hipError_t launch_bf16_rstream(const GemmArgs &a, const GemmGroups &g, Epilogue epi,
+                               hipStream_t s) {
+  StreamSplit sp{};
+  sp.ks_cap = 1;
+  const int64_t prows = split_rows(g);
+  if (g.split_ws && prows <= kSplitMaxRows && g.split_bytes > 256) {
+    const int64_t per = prows * g.Nout * static_cast<int64_t>(sizeof(float));
+    const int64_t cap = (static_cast<int64_t>(g.split_bytes) - 256) / per;
+    if (cap > 1) {
+      sp.ks_used = static_cast<int *>(g.split_ws);
+      sp.partial = reinterpret_cast<float *>(static_cast<char *>(g.split_ws) + 256);
+      sp.part_rows = g.max_routed_rows;
+      sp.ks_cap = static_cast<int>(cap < kSplitCap ? cap : kSplitCap);
+    }
+  }
+  const unsigned grid =
+      persistent_grid(tiles_upper_bound(g, 32 * NTB, 128 * MB) * sp.ks_cap, 1);
+  if (epi == kEpiBiasSilu)
+    hipLaunchKernelGGL((grouped_gemm_bf16_rstream_kernel<MB, NTB, R, kEpiBiasSilu>),
+                       dim3(grid), dim3(256), 0, s, a, sp);
+  else
+    hipLaunchKernelGGL((grouped_gemm_bf16_rstream_kernel<MB, NTB, R, kEpiBias>), dim3(grid),
+                       dim3(256), 0, s, a, sp);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || sp.ks_cap <= 1) return e;
+  const dim3 rgrid(static_cast<unsigned>((g.Nout / 4 + 255) / 256), static_cast<unsigned>(prows));
+  if (epi == kEpiBiasSilu)
+    hipLaunchKernelGGL((stream_reduce_kernel<kEpiBiasSilu>), rgrid, dim3(256), 0, s, a, sp);
+  else
+    hipLaunchKernelGGL((stream_reduce_kernel<kEpiBias>), rgrid, dim3(256), 0, s, a, sp);
+  return hipGetLastError();
+}
 
 template <int GM>
 hipError_t launch_bf16_rs(const GemmArgs &a, const GemmGroups &g, Epilogue epi, hipStream_t s) {

@@ -31,6 +31,8 @@ int check_config(const moe_config *c, bool need_route, bool need_ffn) {
     if (c->n_routed > moe::kMaxRouted || c->top_k > 64) return MOE_ERR_UNSUPPORTED;
     if (c->T * static_cast<int64_t>(c->top_k) >= (int64_t(1) << 31)) return MOE_ERR_UNSUPPORTED;
     if (c->capacity < -1) return MOE_ERR_INVALID_ARG;
+    if (c->bias_mode != MOE_BIAS_IN_LOGIT && c->bias_mode != MOE_BIAS_SELECTION_ONLY)
+      return MOE_ERR_INVALID_ARG;
   }
   if (need_ffn) {
     if (c->d_ff <= 0) return MOE_ERR_INVALID_ARG;
@@ -157,11 +159,31 @@ int moe_route(const moe_config *cfg, const void *x, const float *w_router,
   if (!aligned16(x) || !aligned16(w_router)) return MOE_ERR_INVALID_ARG;
   hipStream_t s = static_cast<hipStream_t>(stream);
   const bool bf16 = cfg->dtype == MOE_BF16;
-  st = hip_status(moe::launch_router_logits(bf16, x, w_router, router_bias, logits, cfg->T,
-                                            cfg->d_model, cfg->n_routed, s));
+  const bool sel_only = cfg->bias_mode == MOE_BIAS_SELECTION_ONLY;
+  st = hip_status(moe::launch_router_logits(bf16, x, w_router, sel_only ? nullptr : router_bias,
+                                            logits, cfg->T, cfg->d_model, cfg->n_routed, s));
   if (st != MOE_OK) return st;
-  return hip_status(moe::launch_topk_gates(logits, cfg->T, cfg->n_routed, cfg->top_k, topk_idx,
-                                           topk_gate, s));
+  return hip_status(moe::launch_topk_gates(logits, sel_only ? router_bias : nullptr, cfg->T,
+                                           cfg->n_routed, cfg->top_k, topk_idx, topk_gate, s));
+}
+
+size_t moe_balance_stats_workspace_size(const moe_config *cfg) {
+  if (check_config(cfg, true, false) != MOE_OK) return 0;
+  return moe::balance_workspace_bytes(cfg->T, cfg->n_routed);
+}
+
+int moe_balance_stats(const moe_config *cfg, const float *logits, const int32_t *topk_idx,
+                      float alpha, float *f, float *P, float *loss, void *ws, size_t ws_bytes,
+                      void *stream) {
+  int st = check_config(cfg, true, false);
+  if (st != MOE_OK) return st;
+  if (cfg->T == 0) return MOE_OK;
+  if (!logits || !topk_idx || !f || !P || !loss) return MOE_ERR_INVALID_ARG;
+  if (!ws || ws_bytes < moe::balance_workspace_bytes(cfg->T, cfg->n_routed))
+    return MOE_ERR_WORKSPACE;
+  return hip_status(moe::launch_balance_stats(logits, topk_idx, cfg->T, cfg->n_routed,
+                                              cfg->top_k, alpha, f, P, loss, ws,
+                                              static_cast<hipStream_t>(stream)));
 }
 
 size_t moe_permute_workspace_size(const moe_config *cfg) {
@@ -300,11 +322,14 @@ int moe_layer_forward_events(const moe_config *cfg, const moe_weights *w, const 
   };
 
   if ((st = mark(MOE_STAGE_ROUTER)) != MOE_OK) return st;
-  st = hip_status(moe::launch_router_logits(bf16, x, w->w_router, w->router_bias, L.logits, T,
+  const bool sel_only = cfg->bias_mode == MOE_BIAS_SELECTION_ONLY;
+  st = hip_status(moe::launch_router_logits(bf16, x, w->w_router,
+                                            sel_only ? nullptr : w->router_bias, L.logits, T,
                                             cfg->d_model, N, s));
   if (st != MOE_OK) return st;
   if ((st = mark(MOE_STAGE_TOPK)) != MOE_OK) return st;
-  st = hip_status(moe::launch_topk_gates(L.logits, T, N, K, idx, gates, s));
+  st = hip_status(moe::launch_topk_gates(L.logits, sel_only ? w->router_bias : nullptr, T, N, K,
+                                         idx, gates, s));
   if (st != MOE_OK) return st;
   if ((st = mark(MOE_STAGE_DISPATCH)) != MOE_OK) return st;
   st = hip_status(moe::launch_dispatch(idx, T, K, N, capacity_of(cfg), cnt, L.offsets,

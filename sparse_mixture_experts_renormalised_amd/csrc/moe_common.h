@@ -87,8 +87,12 @@ enum Epilogue { kEpiBias = 0, kEpiBiasSilu = 1 };
 
 hipError_t launch_router_logits(bool bf16, const void *x, const float *w, const float *bias,
                                 float *logits, int64_t T, int d, int N, hipStream_t s);
-hipError_t launch_topk_gates(const float *logits, int64_t T, int N, int K, int32_t *idx,
-                             float *gates, hipStream_t s);
+hipError_t launch_topk_gates(const float *logits, const float *sel_bias, int64_t T, int N, int K,
+                             int32_t *idx, float *gates, hipStream_t s);
+size_t balance_workspace_bytes(int64_t T, int N);
+hipError_t launch_balance_stats(const float *logits, const int32_t *idx, int64_t T, int N, int K,
+                                float alpha, float *f, float *P, float *loss, void *ws,
+                                hipStream_t s);
 hipError_t launch_dispatch(const int32_t *idx, int64_t T, int K, int N, int64_t capacity,
                            int32_t *counts, int32_t *offsets, int32_t *row_token,
                            int32_t *slot_row, int32_t *n_dropped, void *ws, hipStream_t s);

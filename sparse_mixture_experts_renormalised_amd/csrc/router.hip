@@ -265,6 +265,7 @@ __device__ __forceinline__ bool key_better(float va, int ia, float vb, int ib) {
 
 template <int J>   // J = ceil(N / 64) logits per lane
 __global__ __launch_bounds__(256) void topk_gates_kernel(const float *__restrict__ logits,
+                                                         const float *__restrict__ sel_bias,
                                                          int64_t T, int N, int K,
                                                          int32_t *__restrict__ idx,
                                                          float *__restrict__ gates) {
@@ -272,36 +273,44 @@ __global__ __launch_bounds__(256) void topk_gates_kernel(const float *__restrict
   const int64_t t = static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6);
   if (t >= T) return;
   const float *row = logits + t * N;
-  float v[J];
+  float v[J], key[J];
 #pragma unroll
   for (int j = 0; j < J; ++j) {
     const int e = lane + 64 * j;
     v[j] = e < N ? row[e] : -__builtin_inff();
+    // selection key: the logit, or (selection-only bias) fl32(logit + bias)
+    key[j] = (sel_bias && e < N) ? v[j] + sel_bias[e] : v[j];
   }
   uint32_t taken = 0;
-  float kept_v = 0.0f;   // lane k keeps slot k's logit
+  float kept_v = -__builtin_inff();   // lane k keeps slot k's (unbiased) logit
   int kept_i = 0;
-  float best0 = 0.0f;
   for (int k = 0; k < K; ++k) {
-    float bv = -__builtin_inff();
+    float bk = -__builtin_inff(), bv = 0.0f;
     int bi = 0x7FFFFFFF;
 #pragma unroll
     for (int j = 0; j < J; ++j) {
       const int e = lane + 64 * j;
-      if (e < N && !((taken >> j) & 1u) && key_better(v[j], e, bv, bi)) { bv = v[j]; bi = e; }
+      if (e < N && !((taken >> j) & 1u) && key_better(key[j], e, bk, bi)) {
+        bk = key[j];
+        bv = v[j];
+        bi = e;
+      }
     }
 #pragma unroll
     for (int off = 32; off >= 1; off >>= 1) {
+      const float ok = __shfl_xor(bk, off);
       const float ov = __shfl_xor(bv, off);
       const int oi = __shfl_xor(bi, off);
-      if (key_better(ov, oi, bv, bi)) { bv = ov; bi = oi; }
+      if (key_better(ok, oi, bk, bi)) { bk = ok; bv = ov; bi = oi; }
     }
     if ((bi & 63) == lane) taken |= 1u << (bi >> 6);
-    if (k == 0) best0 = bv;
     if (lane == k) { kept_v = bv; kept_i = bi; }
   }
-  // softmax over the K kept logits, shifted by the largest (slot 0)
-  const float p = lane < K ? expf(kept_v - best0) : 0.0f;
+  // softmax over the K kept logits, shifted by their largest
+  float m = kept_v;
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) m = fmaxf(m, __shfl_xor(m, off));
+  const float p = lane < K ? expf(kept_v - m) : 0.0f;
   float s = p;
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) s += __shfl_xor(s, off);
@@ -351,21 +360,21 @@ hipError_t launch_router_logits(bool bf16, const void *x, const float *w, const 
   return hipGetLastError();
 }
 
-hipError_t launch_topk_gates(const float *logits, int64_t T, int N, int K, int32_t *idx,
-                             float *gates, hipStream_t s) {
+hipError_t launch_topk_gates(const float *logits, const float *sel_bias, int64_t T, int N, int K,
+                             int32_t *idx, float *gates, hipStream_t s) {
   if (T <= 0) return hipSuccess;
   const dim3 grid(static_cast<unsigned>((T + 3) / 4)), block(256);
   const int J = (N + 63) / 64;
   if (J <= 1) {
-    hipLaunchKernelGGL((topk_gates_kernel<1>), grid, block, 0, s, logits, T, N, K, idx, gates);
+    hipLaunchKernelGGL((topk_gates_kernel<1>), grid, block, 0, s, logits, sel_bias, T, N, K, idx, gates);
   } else if (J <= 2) {
-    hipLaunchKernelGGL((topk_gates_kernel<2>), grid, block, 0, s, logits, T, N, K, idx, gates);
+    hipLaunchKernelGGL((topk_gates_kernel<2>), grid, block, 0, s, logits, sel_bias, T, N, K, idx, gates);
   } else if (J <= 4) {
-    hipLaunchKernelGGL((topk_gates_kernel<4>), grid, block, 0, s, logits, T, N, K, idx, gates);
+    hipLaunchKernelGGL((topk_gates_kernel<4>), grid, block, 0, s, logits, sel_bias, T, N, K, idx, gates);
   } else if (J <= 8) {
-    hipLaunchKernelGGL((topk_gates_kernel<8>), grid, block, 0, s, logits, T, N, K, idx, gates);
+    hipLaunchKernelGGL((topk_gates_kernel<8>), grid, block, 0, s, logits, sel_bias, T, N, K, idx, gates);
   } else if (J <= 16) {
-    hipLaunchKernelGGL((topk_gates_kernel<16>), grid, block, 0, s, logits, T, N, K, idx, gates);
+    hipLaunchKernelGGL((topk_gates_kernel<16>), grid, block, 0, s, logits, sel_bias, T, N, K, idx, gates);
   } else {
     return hipErrorInvalidValue;
   }

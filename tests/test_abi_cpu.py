@@ -124,3 +124,19 @@ def test_grouped_ffn_split_workspace_size(B):
     f32 = B.config(64, 128, 8, 2, 0, 256, "f32")
     assert B.grouped_ffn_workspace_size(f32, 8, 128) == 0
     assert B.grouped_ffn_workspace_size(bf, 0, 1024) == 0
+
+
+def test_bias_mode_is_validated(B):
+    L = B.lib()
+    bad = B.config(64, 128, 8, 2, 0, 256, "f32")
+    bad.bias_mode = 2
+    assert L.moe_route(ctypes.byref(bad), None, None, None, None, None, None, None) == -1
+    ok = B.config(64, 128, 8, 2, 0, 256, "f32", selection_only_bias=True)
+    assert ok.bias_mode == 1
+    # balance statistics: missing pointers and workspace
+    assert L.moe_balance_stats(ctypes.byref(ok), None, None, 0.01, None, None, None, None, 0,
+                               None) == -1
+    P = ctypes.c_void_p
+    assert L.moe_balance_stats(ctypes.byref(ok), P(16), P(16), 0.01, P(16), P(16), P(16), None, 0,
+                               None) == -3
+    assert B.balance_stats_workspace_size(ok) == 4 * 8   # one 64-token block x N floats

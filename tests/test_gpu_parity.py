@@ -122,6 +122,91 @@ def test_route_bit_exact(wl):
     assert np.abs(gates.cpu().numpy() - ref_g).max() <= 1e-6
 
 
+SEL_ONLY_CASES = [
+    W.custom_workload("sel_only_gauss", T=203, d_model=128, n_routed=64, top_k=6, n_shared=0,
+                      d_ff=64, dtype="bf16", router_bias="gauss", router_bias_var=0.5,
+                      selection_only_bias=True),
+    W.custom_workload("sel_only_zipf_decode", T=128, d_model=7168, n_routed=256, top_k=8,
+                      n_shared=1, d_ff=2048, dtype="bf16", router_bias="zipf", zipf_s=1.1,
+                      capacity_factor=1.25, selection_only_bias=True),
+    W.custom_workload("sel_only_f32", T=77, d_model=48, n_routed=10, top_k=3, n_shared=0,
+                      d_ff=16, dtype="f32", router_bias="gauss", router_bias_var=2.0,
+                      selection_only_bias=True),
+]
+
+
+@pytest.mark.parametrize("wl", SEL_ONLY_CASES, ids=lambda w: w.name)
+def test_route_selection_only_bias(wl):
+    b = B()
+    cfg = b.config(wl.T, wl.d_model, wl.n_routed, wl.top_k, wl.n_shared, wl.d_ff, wl.dtype,
+                   wl.capacity_factor, selection_only_bias=True)
+    x = wl.x("cuda")
+    wr = wl.w_router("cuda")
+    rb = wl.router_bias_values("cuda")
+    T, N, K = wl.T, wl.n_routed, wl.top_k
+    logits = torch.empty((T, N), dtype=torch.float32, device="cuda")
+    idx = torch.empty((T, K), dtype=torch.int32, device="cuda")
+    gates = torch.empty((T, K), dtype=torch.float32, device="cuda")
+    b.route(cfg, x, wr, rb, logits, idx, gates)
+    torch.cuda.synchronize()
+    ref_l, ref_i, ref_g = oracle.route(host(x), host(wr), bias_np(wl), K, selection_only_bias=True)
+    assert np.array_equal(logits.cpu().numpy().view(np.uint32), ref_l.view(np.uint32))
+    assert np.array_equal(idx.cpu().numpy(), ref_i)
+    assert np.abs(gates.cpu().numpy() - ref_g).max() <= 1e-6
+    # the bias changed the selection somewhere (the mode is not a no-op here)
+    plain = oracle.select_top_k(ref_l, K)
+    assert not np.array_equal(plain, ref_i)
+
+
+def test_layer_selection_only_bias():
+    wl = W.custom_workload("sel_only_layer", T=150, d_model=128, n_routed=16, top_k=4, n_shared=1,
+                           d_ff=128, dtype="bf16", router_bias="zipf", zipf_s=1.1,
+                           capacity_factor=1.25, selection_only_bias=True)
+    dl = W.device.DeviceLayer(wl)
+    dl.forward()
+    torch.cuda.synchronize()
+    routed, shared = providers_host(wl)
+    ref = oracle.layer_forward(host(dl.x), wl.w_router().numpy(), bias_np(wl), routed, shared,
+                               top_k=wl.top_k, n_shared=wl.n_shared,
+                               capacity_factor=wl.capacity_factor, selection_only_bias=True)
+    assert np.array_equal(dl.topk_idx.cpu().numpy(), ref["topk_idx"])
+    assert np.array_equal(dl.counts.cpu().numpy(), ref["counts"])
+    assert np.abs(dl.topk_gate.cpu().numpy() - ref["gates"]).max() <= 1e-6
+    assert rel_l2(host(dl.y), ref["y"]) <= TOL[wl.dtype]
+
+
+# ---------------------------------------------------------------------------
+# moe_balance_stats
+# ---------------------------------------------------------------------------
+
+BALANCE_CASES = [(64, 8, 2), (100, 64, 6), (4096, 256, 8), (333, 1000, 16), (1, 3, 1)]
+
+
+@pytest.mark.parametrize("T,N,K", BALANCE_CASES)
+def test_balance_stats_match_oracle(T, N, K):
+    b = B()
+    wl = W.custom_workload(f"bal_{T}_{N}_{K}", T=T, d_model=64, n_routed=N, top_k=K, n_shared=0,
+                           d_ff=64, dtype="bf16", router_bias="gauss", router_bias_var=0.5)
+    cfg = cfg_of(wl)
+    x, wr, rb = wl.x("cuda"), wl.w_router("cuda"), wl.router_bias_values("cuda")
+    logits = torch.empty((T, N), dtype=torch.float32, device="cuda")
+    idx = torch.empty((T, K), dtype=torch.int32, device="cuda")
+    gates = torch.empty((T, K), dtype=torch.float32, device="cuda")
+    b.route(cfg, x, wr, rb, logits, idx, gates)
+    ws = torch.empty(max(b.balance_stats_workspace_size(cfg), 1), dtype=torch.uint8, device="cuda")
+    f = torch.empty(N, dtype=torch.float32, device="cuda")
+    P = torch.empty(N, dtype=torch.float32, device="cuda")
+    loss = torch.empty(1, dtype=torch.float32, device="cuda")
+    b.balance_stats(cfg, logits, idx, 0.01, f, P, loss, ws)
+    torch.cuda.synchronize()
+    rf, rP, rL = oracle.balance_statistics(logits.cpu().numpy(), idx.cpu().numpy(), 0.01)
+    # counts are exact: f * T * K is an integer
+    assert np.array_equal(np.rint(f.cpu().numpy().astype(np.float64) * T * K), np.rint(rf * T * K))
+    assert np.allclose(f.cpu().numpy(), rf, rtol=1e-6, atol=0)
+    assert np.abs(P.cpu().numpy() - rP).max() <= 1e-5 * max(rP.max(), 1e-30)
+    assert abs(float(loss.item()) - rL) <= 1e-5 * abs(rL)
+
+
 def test_route_all_ties_pick_lowest_ids():
     b = B()
     wl = W.custom_workload("ties", T=67, d_model=64, n_routed=40, top_k=7, n_shared=0, d_ff=64,

@@ -181,6 +181,8 @@ class Workload:
     ``router_bias`` is "none", "gauss" (variance ``router_bias_var``) or
     "zipf" (deterministic, bias[e] = -s*ln(e+1)).
     ``capacity_factor <= 0`` means no per-expert limit.
+    ``selection_only_bias`` marks a router bias that enters the selection key
+    only (the gates then use the unbiased logits).
     """
     name: str
     T: int
@@ -195,6 +197,7 @@ class Workload:
     router_bias: str = "none"
     router_bias_var: float = 0.0
     zipf_s: float = 0.0
+    selection_only_bias: bool = False
     seed: int = 0
     description: str = field(default="", compare=False)
 

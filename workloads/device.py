@@ -22,7 +22,8 @@ class DeviceLayer:
         dev = self.dev
         self.act = torch.bfloat16 if wl.dtype == "bf16" else torch.float32
         self.cfg = B.config(wl.T, wl.d_model, wl.n_routed, wl.top_k, wl.n_shared, wl.d_ff,
-                            wl.dtype, wl.capacity_factor)
+                            wl.dtype, wl.capacity_factor,
+                            selection_only_bias=wl.selection_only_bias)
         self.x = wl.x(dev)
         self.w_router = wl.w_router(dev)
         self.router_bias = wl.router_bias_values(dev)
