@@ -15,20 +15,24 @@
 // per group in LDS from those offsets, so the launch is sized from a host
 // upper bound and the work list lives entirely on the device.
 //
-// Scheduling: persistent workgroups; the tile range is split into eight equal
+// Scheduling: persistent workgroups; the work list is split into eight equal
 // contiguous parts, one per XCD (workgroups are dealt to the eight XCDs
-// round-robin by id), and within a part tiles are visited in bands of GM
-// m-tiles so that the workgroups running together on one XCD share weight
-// tiles and activation tiles in that XCD's L2.
+// round-robin by id), so the workgroups running together on one XCD share
+// weight and activation tiles in that XCD's L2.
 //
-// bf16 path: MFMA v_mfma_f32_32x32x16_bf16, fp32 accumulate.  Tiles go from
-// HBM straight into LDS (global_load_lds, 16 bytes per lane, no staging
-// registers), double buffered, with an XOR swizzle of the 16-byte chunks so
-// the fragment reads of 32 rows hit distinct banks.  The weight tile is the MFMA's first operand,
-// so each lane ends up holding four consecutive output features of one row
-// and the epilogue writes 8-byte packed bf16 stores.
-//
-// fp32 path: a plain LDS-tiled VALU kernel (4x4 register tile per thread).
+// Kernels, chosen by operand type and group size (rows per expert):
+//   * 256x256 tiles (groups above 256 rows): MFMA v_mfma_f32_32x32x16_bf16 with
+//     fp32 accumulators, operands staged global -> registers -> swizzled LDS
+//     one K-step ahead, a hand-interleaved schedule, and a K split of the last
+//     partial round of tiles;
+//   * a stream kernel (groups of up to 256 rows, bound by the weight stream):
+//     weights and activations copied straight into a ring of LDS stages
+//     several chunks ahead, non-temporal for weights read once, and a K split
+//     when a product has too few units to fill the chip (decode);
+//   * fp32 operands: a plain LDS-tiled VALU kernel (4x4 register tile).
+// The weight tile is the MFMA's first operand, so each lane ends up holding
+// four consecutive output features of one row and the epilogues store packed
+// bf16 pairs.
 #include "moe_common.h"
 
 namespace moe {
@@ -180,220 +184,6 @@ __device__ __forceinline__ void decode_tile(int L, int total_m, int n_nt, int *m
   const int r = L - band * GM * n_nt;
   *mt = first + r % gm;
   *nt = r / gm;
-}
-
-// ---------------------------------------------------------------------------
-// bf16 MFMA kernel
-// ---------------------------------------------------------------------------
-// One wave instruction moves 8 tile rows x 128 bytes straight from global
-// memory into LDS: lane L lands at byte 16*L of the 1 KB block, i.e. row L/8,
-// chunk position L%8.  Position p of row r must hold logical chunk p ^ (r%8)
-// (the XOR swizzle the fragment reads expect), so lane L fetches chunk
-// (L%8) ^ (L/8) of its row; the 128-byte row segment stays fully used.
-__device__ __forceinline__ void load_rows_to_lds(const uint16_t *src, uint16_t *lds_block) {
-  __builtin_amdgcn_global_load_lds(src, lds_block, 16, 0, 0);
-}
-
-// Issue the global->LDS loads of K-step kb into one stage.
-template <int A_INS, int B_INS, int NW, int BM, int BK>
-__device__ __forceinline__ void issue_stage(uint16_t *sa, const uint16_t *const (&a_src)[A_INS],
-                                            const uint16_t *const (&b_src)[B_INS], int kb,
-                                            int wave) {
-  uint16_t *sb = sa + BM * BK;
-#pragma unroll
-  for (int j = 0; j < A_INS; ++j) load_rows_to_lds(a_src[j] + kb * BK, sa + (j * NW + wave) * 8 * BK);
-#pragma unroll
-  for (int j = 0; j < B_INS; ++j) load_rows_to_lds(b_src[j] + kb * BK, sb + (j * NW + wave) * 8 * BK);
-}
-
-// Fragments of one 16-wide K slice: lane l holds 8 consecutive k of row l%32
-// (k offset 8*(l/32)) for each 32-row block of the wave's rows.
-template <int TM, int TN, int BM, int BK, int WTM, int WTN>
-__device__ __forceinline__ void load_frags(const uint16_t *sa, bf16x8_t (&fa)[TM],
-                                           bf16x8_t (&fb)[TN], int ks, int wm, int wn,
-                                           int lane) {
-  const uint16_t *sb = sa + BM * BK;
-  const int c = ks * 2 + (lane >> 5);
-#pragma unroll
-  for (int mi = 0; mi < TM; ++mi) {
-    const int row = wm * WTM + mi * 32 + (lane & 31);
-    fa[mi] = *reinterpret_cast<const bf16x8_t *>(sa + row * BK + ((c ^ (row & 7)) << 3));
-  }
-#pragma unroll
-  for (int ni = 0; ni < TN; ++ni) {
-    const int row = wn * WTN + ni * 32 + (lane & 31);
-    fb[ni] = *reinterpret_cast<const bf16x8_t *>(sb + row * BK + ((c ^ (row & 7)) << 3));
-  }
-}
-
-// Multiply one staged K-step into the wave's accumulators.  The fragments of
-// slice ks+1 are read while the MFMAs of slice ks run (two register sets).
-template <int TM, int TN, int BM, int BK, int WTM, int WTN>
-__device__ __forceinline__ void mma_stage(const uint16_t *sa, f32x16_t (&acc)[TN][TM], int wm,
-                                          int wn, int lane) {
-  constexpr int NS = BK / 16;
-  bf16x8_t fa[2][TM], fb[2][TN];
-  load_frags<TM, TN, BM, BK, WTM, WTN>(sa, fa[0], fb[0], 0, wm, wn, lane);
-#pragma unroll
-  for (int ks = 0; ks < NS; ++ks) {
-    if (ks + 1 < NS)
-      load_frags<TM, TN, BM, BK, WTM, WTN>(sa, fa[(ks + 1) & 1], fb[(ks + 1) & 1], ks + 1, wm, wn,
-                                           lane);
-#pragma unroll
-    for (int ni = 0; ni < TN; ++ni)
-#pragma unroll
-      for (int mi = 0; mi < TM; ++mi)
-        acc[ni][mi] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[ks & 1][ni], fa[ks & 1][mi],
-                                                              acc[ni][mi], 0, 0, 0);
-  }
-}
-
-template <int BM, int BN, int WAVES_M, int WAVES_N, int EPI, int GM>
-__global__ __launch_bounds__(WAVES_M *WAVES_N * 64) void grouped_gemm_bf16_kernel(GemmArgs a) {
-  constexpr int NT = WAVES_M * WAVES_N * 64;
-  constexpr int BK = 64;                 // 8 chunks of 16 B per row
-  constexpr int WTM = BM / WAVES_M;      // rows (tokens) per wave
-  constexpr int WTN = BN / WAVES_N;      // output features per wave
-  constexpr int TM = WTM / 32;
-  constexpr int TN = WTN / 32;
-  constexpr int NW = NT / 64;
-  constexpr int A_INS = BM / 8 / NW;     // 8-row global->LDS loads per wave per stage
-  constexpr int B_INS = BN / 8 / NW;
-  constexpr int STAGE = (BM + BN) * BK;  // bf16 elements per stage
-  static_assert(WTM % 32 == 0 && WTN % 32 == 0, "wave tile must be MFMA-aligned");
-  static_assert((BM / 8) % NW == 0 && (BN / 8) % NW == 0, "row blocks must divide evenly");
-
-  // Two stages as distinct objects, so the compiler can tell the loads into
-  // one from the reads of the other and need not wait between them.
-  __shared__ __attribute__((aligned(16))) uint16_t s_st0[STAGE];
-  __shared__ __attribute__((aligned(16))) uint16_t s_st1[STAGE];
-  __shared__ int s_pref[kMaxGroups + 1];
-  __shared__ int s_tmp[NT / 64];
-
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = uniform(tid >> 6);
-  const int wm = wave % WAVES_M, wn = wave / WAVES_M;
-  const int n_groups = a.n_routed + a.n_shared;
-
-  const int total_m = build_tile_prefix<NT, BM>(a, s_pref, s_tmp);
-  const int n_nt = (a.Nout + BN - 1) / BN;
-  const int total = total_m * n_nt;
-  const int xcd = blockIdx.x % kXcds;
-  const int slot = blockIdx.x / kXcds;
-  const int nslots = gridDim.x / kXcds;
-  const int part = (total + kXcds - 1) / kXcds;
-  const int begin = xcd * part;
-  const int end = min(total, begin + part);
-  const int nk = a.K / BK;
-  const int lrow = lane >> 3;                       // row within an 8-row block
-  const int lchunk = (lane & 7) ^ lrow;             // logical chunk this lane fetches
-
-  for (int L = begin + slot; L < end; L += nslots) {
-    int mt, nt;
-    decode_tile<GM>(L, total_m, n_nt, &mt, &nt);
-    const int g = find_group(s_pref, n_groups, mt);
-    const TileView<uint16_t> v = tile_view<uint16_t>(a, g, mt - s_pref[g], BM);
-    const int n0 = nt * BN;
-
-    const uint16_t *a_src[A_INS];
-    const uint16_t *b_src[B_INS];
-#pragma unroll
-    for (int j = 0; j < A_INS; ++j) {
-      const int row = (j * NW + wave) * 8 + lrow;
-      a_src[j] = a_row_ptr(a, v, v.row0 + row) + lchunk * 8;
-    }
-#pragma unroll
-    for (int j = 0; j < B_INS; ++j) {
-      int n = n0 + (j * NW + wave) * 8 + lrow;
-      if (n >= a.Nout) n = a.Nout - 1;
-      b_src[j] = v.W + static_cast<int64_t>(n) * a.K + lchunk * 8;
-    }
-    f32x16_t acc[TN][TM];
-#pragma unroll
-    for (int i = 0; i < TN; ++i)
-#pragma unroll
-      for (int j = 0; j < TM; ++j)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
-
-    // Two LDS stages: the loads of step kb+1 land in one while step kb is
-    // multiplied out of the other; the barrier at the end of each step both
-    // publishes the new stage and frees the old one.
-    issue_stage<A_INS, B_INS, NW, BM, BK>(s_st0, a_src, b_src, 0, wave);
-    __syncthreads();
-    int kb = 0;
-    for (; kb + 1 < nk; kb += 2) {
-      issue_stage<A_INS, B_INS, NW, BM, BK>(s_st1, a_src, b_src, kb + 1, wave);
-      mma_stage<TM, TN, BM, BK, WTM, WTN>(s_st0, acc, wm, wn, lane);
-      __syncthreads();
-      if (kb + 2 < nk) issue_stage<A_INS, B_INS, NW, BM, BK>(s_st0, a_src, b_src, kb + 2, wave);
-      mma_stage<TM, TN, BM, BK, WTM, WTN>(s_st1, acc, wm, wn, lane);
-      __syncthreads();
-    }
-    if (kb < nk) {   // odd number of K-steps: the last one sits in stage 0
-      mma_stage<TM, TN, BM, BK, WTM, WTN>(s_st0, acc, wm, wn, lane);
-      __syncthreads();
-    }
-
-    // Epilogue through LDS: bias, SiLU and bf16 rounding per accumulator,
-    // into a [BM][BN] bf16 tile whose 16-byte chunks are XOR-swizzled by row
-    // (acc[ni][mi][q*4 + j] holds feature wn*WTN + ni*32 + q*8 + (lane/32)*4 + j
-    // of row wm*WTM + mi*32 + lane%32); then whole rows leave in 16-byte stores.
-    // Opaque copies of the lane coordinates keep the epilogue's address
-    // arithmetic below the K loop instead of live across it.
-    int el = lane, ewm = wm, ewn = wn, etid = tid;
-    asm volatile("" : "+v"(el), "+v"(etid), "+s"(ewm), "+s"(ewn));
-    constexpr int CH = BN / 8;                       // 16-byte chunks per tile row
-    constexpr int XM = (CH < 32 ? CH : 32) - 1;      // swizzle mask
-    // the C tile takes stage 0, spilling its second half of rows into stage 1
-    constexpr bool kSplitC = BM * BN > STAGE;
-    static_assert(!kSplitC || (BM * BN) / 2 <= STAGE, "C tile must fit in the LDS stages");
-#define MOE_CROW(r) ((kSplitC && (r) >= BM / 2) ? s_st1 + ((r) - BM / 2) * BN : s_st0 + (r) * BN)
-#pragma unroll
-    for (int ni = 0; ni < TN; ++ni) {
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int nl = ewn * WTN + ni * 32 + q * 8 + (el >> 5) * 4;
-        const int n = n0 + nl;
-        float bv[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-        if (v.bias && n < a.Nout) {
-          const uint2 bq = *reinterpret_cast<const uint2 *>(v.bias + n);
-          bv[0] = __uint_as_float(bq.x << 16);
-          bv[1] = __uint_as_float(bq.x & 0xFFFF0000u);
-          bv[2] = __uint_as_float(bq.y << 16);
-          bv[3] = __uint_as_float(bq.y & 0xFFFF0000u);
-        }
-#pragma unroll
-        for (int mi = 0; mi < TM; ++mi) {
-          const int ml = ewm * WTM + mi * 32 + (el & 31);
-          float o[4];
-#pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            o[j] = acc[ni][mi][q * 4 + j] + bv[j];
-            if (EPI == kEpiBiasSilu) o[j] = silu(o[j]);
-          }
-          uint2 packed;
-          packed.x = f32_to_bf16(o[0]) | (static_cast<uint32_t>(f32_to_bf16(o[1])) << 16);
-          packed.y = f32_to_bf16(o[2]) | (static_cast<uint32_t>(f32_to_bf16(o[3])) << 16);
-          const int pos = (nl >> 3) ^ (ml & XM);
-          *reinterpret_cast<uint2 *>(MOE_CROW(ml) + pos * 8 + ((nl >> 2) & 1) * 4) = packed;
-        }
-      }
-    }
-    __syncthreads();
-    for (int i = etid; i < BM * CH; i += NT) {
-      const int r = i / CH, c = i % CH;
-      const int64_t row = v.row0 + r;
-      const int n = n0 + c * 8;
-      if (row < v.rows && n < a.Nout) {
-        const u32x4_t val = *reinterpret_cast<const u32x4_t *>(MOE_CROW(r) + ((c ^ (r & XM)) << 3));
-        *reinterpret_cast<u32x4_t *>(v.C + (v.out_base + row) * a.Nout + n) = val;
-      }
-    }
-#undef MOE_CROW
-    __syncthreads();
-  }
 }
 
 // ---------------------------------------------------------------------------
@@ -931,8 +721,14 @@ __device__ __forceinline__ void stream_store(const f32x16_t (&acc)[MB][NTB], con
   }
 }
 
+// One unit of the stream kernel (unit index L of the k-split ks, kc_per
+// chunks per part); `stage` is the ring position of the next chunk, carried
+// from unit to unit of one workgroup.
 template <int MB, int NTB, int S, int EPI>
-__global__ __launch_bounds__(256) void grouped_gemm_bf16_stream_kernel(GemmArgs a, StreamSplit sp) {
+__device__ __forceinline__ void stream_unit(const GemmArgs &a, const StreamSplit &sp,
+                                            const int *s_pref, int L, int ks, int kc_per,
+                                            uint16_t *s_ring, uint32_t ring0, int &stage,
+                                            int lane, int wave) {
   using namespace st;
   constexpr int MR = 32 * NTB;                   // rows per unit
   constexpr int NB = 4 * 32 * MB;                // features per unit
@@ -941,14 +737,112 @@ __global__ __launch_bounds__(256) void grouped_gemm_bf16_stream_kernel(GemmArgs 
   constexpr int LPS = W_INS + X_INS;
   constexpr int STAGE = (NB + MR) * KCH;         // bf16 elements
   static_assert((S - 2) * LPS <= 63, "vmcnt range");
+  const int r32 = lane & 31, h = lane >> 5;
+  const int n_groups = a.n_routed + a.n_shared;
+  const int n_nb = (a.Nout + NB - 1) / NB;
+  const int nkc = a.K / KCH;
+  // lane's place in a copy: row lane/8 of an 8-row block, LDS piece lane%8
+  const int crow = lane >> 3, cpos = lane & 7;
+
+  // unit order: part fastest, then row block, then feature block, so the
+  // workgroups running together share a weight block in L2
+  const int kp = L % ks;
+  const int u = L / ks;
+  const int g = find_group(s_pref, n_groups, u / n_nb);
+  const int mg = s_pref[g + 1] - s_pref[g];
+  const int uu = u - s_pref[g] * n_nb;
+  const int nb = uu / mg, rb = uu % mg;
+  const TileView<uint16_t> v = tile_view<uint16_t>(a, g, rb, MR);
+  const int n0 = nb * NB;
+  const int kc0 = kp * kc_per;
+  const int nch = min(nkc, kc0 + kc_per) - kc0;
+
+  // sources of this wave's copies (chunk 0 of the part)
+  const uint16_t *w_src[W_INS];
+  const uint16_t *x_src[X_INS];
+#pragma unroll
+  for (int i = 0; i < W_INS; ++i) {
+    const int r = (i * NW + wave) * 8 + crow;
+    const int n = min(n0 + r, a.Nout - 1);
+    w_src[i] = v.W + static_cast<int64_t>(n) * a.K + kc0 * KCH + swz(r, cpos) * 8;
+  }
+#pragma unroll
+  for (int i = 0; i < X_INS; ++i) {
+    const int r = (i * NW + wave) * 8 + crow;
+    x_src[i] = a_row_ptr(a, v, v.row0 + r) + kc0 * KCH + swz(r, cpos) * 8;
+  }
+  // weights of a group with one row block are read once: stream them
+  const bool w_once = mg == 1;
+  auto issue = [&](int c, int st_idx) {
+    const uint32_t base = ring0 + static_cast<uint32_t>(st_idx) * (STAGE * 2);
+    if (w_once) {
+#pragma unroll
+      for (int i = 0; i < W_INS; ++i) dma16_nt(w_src[i] + c * KCH, base + (i * NW + wave) * 1024);
+    } else {
+#pragma unroll
+      for (int i = 0; i < W_INS; ++i) dma16(w_src[i] + c * KCH, base + (i * NW + wave) * 1024);
+    }
+#pragma unroll
+    for (int i = 0; i < X_INS; ++i)
+      dma16(x_src[i] + c * KCH, base + NB * KCH * 2 + (i * NW + wave) * 1024);
+  };
+
+  f32x16_t acc[MB][NTB];
+#pragma unroll
+  for (int i = 0; i < MB; ++i)
+#pragma unroll
+    for (int j = 0; j < NTB; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+
+  const int pro = min(S - 1, nch);
+  for (int c = 0; c < pro; ++c) issue(c, (stage + c) % S);
+  for (int c = 0; c < nch; ++c) {
+    // copies of chunks c+1 .. min(c+S-2, nch-1) may stay in flight
+    const int later = min(S - 2, nch - 1 - c);
+    if (later == S - 2) wait_and_barrier<(S - 2) * LPS>();
+    else wait_chunks<LPS, S - 3>(later);
+    const int cur = (stage + c) % S;
+    if (c + S - 1 < nch) issue(c + S - 1, (stage + c + S - 1) % S);
+    const uint16_t *sw = s_ring + cur * STAGE;
+    const uint16_t *sx = sw + NB * KCH;
+#pragma unroll
+    for (int kst = 0; kst < 4; ++kst) {
+      const int p = 2 * kst + h;
+      bf16x8_t fw[MB], fx[NTB];
+#pragma unroll
+      for (int i = 0; i < MB; ++i) {
+        const int r = wave * 32 * MB + 32 * i + r32;
+        fw[i] = *reinterpret_cast<const bf16x8_t *>(sw + r * KCH + swz(r, p) * 8);
+      }
+#pragma unroll
+      for (int j = 0; j < NTB; ++j) {
+        const int r = 32 * j + r32;
+        fx[j] = *reinterpret_cast<const bf16x8_t *>(sx + r * KCH + swz(r, p) * 8);
+      }
+#pragma unroll
+      for (int i = 0; i < MB; ++i)
+#pragma unroll
+        for (int j = 0; j < NTB; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fw[i], fx[j], acc[i][j], 0, 0, 0);
+    }
+  }
+  stage = (stage + nch) % S;
+  stream_store<MB, NTB, EPI>(acc, a, v, g, n0 + wave * 32 * MB, kp, ks, sp, r32, h);
+}
+
+template <int MB, int NTB, int S, int EPI>
+__global__ __launch_bounds__(256) void grouped_gemm_bf16_stream_kernel(GemmArgs a, StreamSplit sp) {
+  using namespace st;
+  constexpr int MR = 32 * NTB;
+  constexpr int NB = 4 * 32 * MB;
+  constexpr int STAGE = (NB + MR) * KCH;
   __shared__ __attribute__((aligned(16))) uint16_t s_ring[S * STAGE];
   __shared__ int s_pref[kMaxGroups + 1];
   __shared__ int s_tmp[NT / 64];
 
   const int lane = threadIdx.x & 63;
   const int wave = uniform(threadIdx.x >> 6);
-  const int r32 = lane & 31, h = lane >> 5;
-  const int n_groups = a.n_routed + a.n_shared;
   const int total_m = build_tile_prefix<NT, MR>(a, s_pref, s_tmp);
   const int n_nb = (a.Nout + NB - 1) / NB;
   const int nkc = a.K / KCH;
@@ -963,271 +857,9 @@ __global__ __launch_bounds__(256) void grouped_gemm_bf16_stream_kernel(GemmArgs 
   const int begin = xcd * part;
   const int end = min(total, begin + part);
   const uint32_t ring0 = uniform(static_cast<int>(lds_addr(s_ring)));
-  // lane's place in a copy: row lane/8 of an 8-row block, LDS piece lane%8
-  const int crow = lane >> 3, cpos = lane & 7;
-  int stage = 0;                                 // ring position of the next chunk
-
-  for (int L = begin + slot; L < end; L += nslots) {
-    // unit order: part fastest, then row block, then feature block, so the
-    // workgroups running together share a weight block in L2
-    const int kp = L % ks;
-    const int u = L / ks;
-    const int g = find_group(s_pref, n_groups, u / n_nb);
-    const int mg = s_pref[g + 1] - s_pref[g];
-    const int uu = u - s_pref[g] * n_nb;
-    const int nb = uu / mg, rb = uu % mg;
-    const TileView<uint16_t> v = tile_view<uint16_t>(a, g, rb, MR);
-    const int n0 = nb * NB;
-    const int kc0 = kp * kc_per;
-    const int nch = min(nkc, kc0 + kc_per) - kc0;
-
-    // sources of this wave's copies (chunk 0 of the part)
-    const uint16_t *w_src[W_INS];
-    const uint16_t *x_src[X_INS];
-#pragma unroll
-    for (int i = 0; i < W_INS; ++i) {
-      const int r = (i * NW + wave) * 8 + crow;
-      const int n = min(n0 + r, a.Nout - 1);
-      w_src[i] = v.W + static_cast<int64_t>(n) * a.K + kc0 * KCH + swz(r, cpos) * 8;
-    }
-#pragma unroll
-    for (int i = 0; i < X_INS; ++i) {
-      const int r = (i * NW + wave) * 8 + crow;
-      x_src[i] = a_row_ptr(a, v, v.row0 + r) + kc0 * KCH + swz(r, cpos) * 8;
-    }
-    // weights of a group with one row block are read once: stream them
-    const bool w_once = mg == 1;
-    auto issue = [&](int c, int st_idx) {
-      const uint32_t base = ring0 + static_cast<uint32_t>(st_idx) * (STAGE * 2);
-      if (w_once) {
-#pragma unroll
-        for (int i = 0; i < W_INS; ++i) dma16_nt(w_src[i] + c * KCH, base + (i * NW + wave) * 1024);
-      } else {
-#pragma unroll
-        for (int i = 0; i < W_INS; ++i) dma16(w_src[i] + c * KCH, base + (i * NW + wave) * 1024);
-      }
-#pragma unroll
-      for (int i = 0; i < X_INS; ++i)
-        dma16(x_src[i] + c * KCH, base + NB * KCH * 2 + (i * NW + wave) * 1024);
-    };
-
-    f32x16_t acc[MB][NTB];
-#pragma unroll
-    for (int i = 0; i < MB; ++i)
-#pragma unroll
-      for (int j = 0; j < NTB; ++j)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
-
-    const int pro = min(S - 1, nch);
-    for (int c = 0; c < pro; ++c) issue(c, (stage + c) % S);
-    for (int c = 0; c < nch; ++c) {
-      // copies of chunks c+1 .. min(c+S-2, nch-1) may stay in flight
-      const int later = min(S - 2, nch - 1 - c);
-      if (later == S - 2) wait_and_barrier<(S - 2) * LPS>();
-      else wait_chunks<LPS, S - 3>(later);
-      const int cur = (stage + c) % S;
-      if (c + S - 1 < nch) issue(c + S - 1, (stage + c + S - 1) % S);
-      const uint16_t *sw = s_ring + cur * STAGE;
-      const uint16_t *sx = sw + NB * KCH;
-#pragma unroll
-      for (int kst = 0; kst < 4; ++kst) {
-        const int p = 2 * kst + h;
-        bf16x8_t fw[MB], fx[NTB];
-#pragma unroll
-        for (int i = 0; i < MB; ++i) {
-          const int r = wave * 32 * MB + 32 * i + r32;
-          fw[i] = *reinterpret_cast<const bf16x8_t *>(sw + r * KCH + swz(r, p) * 8);
-        }
-#pragma unroll
-        for (int j = 0; j < NTB; ++j) {
-          const int r = 32 * j + r32;
-          fx[j] = *reinterpret_cast<const bf16x8_t *>(sx + r * KCH + swz(r, p) * 8);
-        }
-#pragma unroll
-        for (int i = 0; i < MB; ++i)
-#pragma unroll
-          for (int j = 0; j < NTB; ++j)
-            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fw[i], fx[j], acc[i][j], 0, 0, 0);
-      }
-    }
-    stage = (stage + nch) % S;
-
-    stream_store<MB, NTB, EPI>(acc, a, v, g, n0 + wave * 32 * MB, kp, ks, sp, r32, h);
-  }
-}
-
-// Register-ring variant of the stream kernel: the same units and operand
-// layout, but every thread prefetches its share of R 64-wide k-chunks into
-// registers with coalesced 16-byte loads (8 lanes per 128-byte row segment),
-// so R chunks (about 200 KB per CU) are in flight instead of the two or three
-// an LDS ring of this size holds.  Each step writes the next chunk from
-// registers into the other half of a double-buffered, swizzled LDS tile and
-// runs the MFMAs of the current one.  Weights of groups with one row block
-// are loaded with the non-temporal policy.
-namespace rst {
-template <int WCH, int XCH>
-struct Chunk {
-  u32x4_t w[WCH];
-  u32x4_t x[XCH];
-};
-
-template <bool NTW, int WCH, int XCH>
-__device__ __forceinline__ void gload(Chunk<WCH, XCH> &r, const uint16_t *const (&wp)[WCH],
-                                      const uint16_t *const (&xp)[XCH], int c) {
-#pragma unroll
-  for (int i = 0; i < WCH; ++i) {
-    const u32x4_t *src = reinterpret_cast<const u32x4_t *>(wp[i] + c * st::KCH);
-    r.w[i] = NTW ? __builtin_nontemporal_load(src) : *src;
-  }
-#pragma unroll
-  for (int i = 0; i < XCH; ++i) r.x[i] = *reinterpret_cast<const u32x4_t *>(xp[i] + c * st::KCH);
-}
-}  // namespace rst
-
-template <int MB, int NTB, int R, bool NTW, int EPI>
-__device__ __forceinline__ void rstream_unit(const GemmArgs &a, const StreamSplit &sp,
-                                             const TileView<uint16_t> &v, int g, int n0, int kp,
-                                             int ks, int kc0, int nch, uint16_t *s_tile, int tid,
-                                             int lane, int wave) {
-  using namespace rst;
-  constexpr int MR = 32 * NTB, NB = 4 * 32 * MB, KCH = st::KCH;
-  constexpr int WCH = NB * 8 / st::NT, XCH = MR * 8 / st::NT;
-  constexpr int HALF = (NB + MR) * KCH;          // bf16 elements per LDS buffer
-  const int r32 = lane & 31, h = lane >> 5;
-  const int crow = tid >> 3, cpc = tid & 7;
-  const uint16_t *wp[WCH];
-  const uint16_t *xp[XCH];
-#pragma unroll
-  for (int i = 0; i < WCH; ++i) {
-    const int n = min(n0 + crow + 32 * i, a.Nout - 1);
-    wp[i] = v.W + static_cast<int64_t>(n) * a.K + kc0 * KCH + cpc * 8;
-  }
-#pragma unroll
-  for (int i = 0; i < XCH; ++i) xp[i] = a_row_ptr(a, v, v.row0 + crow + 32 * i) + kc0 * KCH + cpc * 8;
-
-  f32x16_t acc[MB][NTB];
-#pragma unroll
-  for (int i = 0; i < MB; ++i)
-#pragma unroll
-    for (int j = 0; j < NTB; ++j)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
-
-  auto lstore = [&](const Chunk<WCH, XCH> &ck, int buf) {
-    uint16_t *tw = s_tile + buf * HALF;
-    uint16_t *tx = tw + NB * KCH;
-#pragma unroll
-    for (int i = 0; i < WCH; ++i) {
-      const int r = crow + 32 * i;
-      *reinterpret_cast<u32x4_t *>(tw + r * KCH + (st::swz(r, cpc) << 3)) = ck.w[i];
-    }
-#pragma unroll
-    for (int i = 0; i < XCH; ++i) {
-      const int r = crow + 32 * i;
-      *reinterpret_cast<u32x4_t *>(tx + r * KCH + (st::swz(r, cpc) << 3)) = ck.x[i];
-    }
-  };
-  auto mma = [&](int buf) {
-    const uint16_t *tw = s_tile + buf * HALF;
-    const uint16_t *tx = tw + NB * KCH;
-#pragma unroll
-    for (int kst = 0; kst < 4; ++kst) {
-      const int p = 2 * kst + h;
-      bf16x8_t fw[MB], fx[NTB];
-#pragma unroll
-      for (int i = 0; i < MB; ++i) {
-        const int r = wave * 32 * MB + 32 * i + r32;
-        fw[i] = *reinterpret_cast<const bf16x8_t *>(tw + r * KCH + (st::swz(r, p) << 3));
-      }
-#pragma unroll
-      for (int j = 0; j < NTB; ++j) {
-        const int r = 32 * j + r32;
-        fx[j] = *reinterpret_cast<const bf16x8_t *>(tx + r * KCH + (st::swz(r, p) << 3));
-      }
-#pragma unroll
-      for (int i = 0; i < MB; ++i)
-#pragma unroll
-        for (int j = 0; j < NTB; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fw[i], fx[j], acc[i][j], 0, 0, 0);
-    }
-  };
-
-  // Ring slot r holds chunk c with c % R == r (R is even, so LDS buffer c & 1
-  // is r & 1); loads past the end re-read the last chunk (cache hits), so the
-  // steady-state steps have no branches.  Step c: write chunk c+1 from its
-  // slot into the other LDS buffer, refill the slot with chunk c+1+R, run the
-  // MFMAs of chunk c, barrier.
-  static_assert(R % 2 == 0, "even ring");
-  Chunk<WCH, XCH> ring[R];
-#pragma unroll
-  for (int r = 0; r < R; ++r) gload<NTW>(ring[r], wp, xp, min(r, nch - 1));
-  lstore(ring[0], 0);
-  gload<NTW>(ring[0], wp, xp, min(R, nch - 1));
-  __syncthreads();
-  int c0 = 0;
-  for (; c0 + R < nch; c0 += R) {
-#pragma unroll
-    for (int r = 0; r < R; ++r) {
-      const int nr = (r + 1) % R;
-      lstore(ring[nr], (r + 1) & 1);
-      gload<NTW>(ring[nr], wp, xp, min(c0 + r + 1 + R, nch - 1));
-      mma(r & 1);
-      __syncthreads();
-    }
-  }
-#pragma unroll
-  for (int r = 0; r < R; ++r) {                // the last chunks: no refills
-    const int c = c0 + r;
-    if (c < nch) {
-      if (c + 1 < nch) lstore(ring[(r + 1) % R], (r + 1) & 1);
-      mma(r & 1);
-      __syncthreads();
-    }
-  }
-  stream_store<MB, NTB, EPI>(acc, a, v, g, n0 + wave * 32 * MB, kp, ks, sp, r32, h);
-}
-
-template <int MB, int NTB, int R, int EPI>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
-void grouped_gemm_bf16_rstream_kernel(GemmArgs a, StreamSplit sp) {
-  using namespace st;
-  constexpr int MR = 32 * NTB, NB = 4 * 32 * MB;
-  __shared__ __attribute__((aligned(16))) uint16_t s_tile[2 * (NB + MR) * KCH];
-  __shared__ int s_pref[kMaxGroups + 1];
-  __shared__ int s_tmp[NT / 64];
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = uniform(tid >> 6);
-  const int n_groups = a.n_routed + a.n_shared;
-  const int total_m = build_tile_prefix<NT, MR>(a, s_pref, s_tmp);
-  const int n_nb = (a.Nout + NB - 1) / NB;
-  const int nkc = a.K / KCH;
-  int kc_per;
-  const int ks = stream_split(total_m * n_nb, nkc, sp.ks_cap, gridDim.x, &kc_per);
-  if (blockIdx.x == 0 && threadIdx.x == 0 && sp.ks_used) *sp.ks_used = ks;
-  const int total = total_m * n_nb * ks;
-  const int xcd = blockIdx.x % kXcds;
-  const int slot = blockIdx.x / kXcds;
-  const int nslots = gridDim.x / kXcds;
-  const int part = (total + kXcds - 1) / kXcds;
-  const int begin = xcd * part;
-  const int end = min(total, begin + part);
-  for (int L = begin + slot; L < end; L += nslots) {
-    const int kp = L % ks;
-    const int u = L / ks;
-    const int g = find_group(s_pref, n_groups, u / n_nb);
-    const int mg = s_pref[g + 1] - s_pref[g];
-    const int uu = u - s_pref[g] * n_nb;
-    const int nb = uu / mg, rb = uu % mg;
-    const TileView<uint16_t> v = tile_view<uint16_t>(a, g, rb, MR);
-    const int kc0 = kp * kc_per;
-    const int nch = min(nkc, kc0 + kc_per) - kc0;
-    if (mg == 1)
-      rstream_unit<MB, NTB, R, true, EPI>(a, sp, v, g, nb * NB, kp, ks, kc0, nch, s_tile, tid, lane, wave);
-    else
-      rstream_unit<MB, NTB, R, false, EPI>(a, sp, v, g, nb * NB, kp, ks, kc0, nch, s_tile, tid, lane, wave);
-  }
+  int stage = 0;
+  for (int L = begin + slot; L < end; L += nslots)
+    stream_unit<MB, NTB, S, EPI>(a, sp, s_pref, L, ks, kc_per, s_ring, ring0, stage, lane, wave);
 }
 
 // Sum of the k-split partials in part order, bias, epilogue, bf16 store.
@@ -1416,20 +1048,6 @@ unsigned persistent_grid(int64_t tiles_ub, int per_cu) {
   return static_cast<unsigned>(g);
 }
 
-template <int BM, int BN, int WM, int WN, int GM>
-hipError_t launch_bf16(const GemmArgs &a, const GemmGroups &g, Epilogue epi, int per_cu,
-                       hipStream_t s) {
-  const unsigned grid = persistent_grid(tiles_upper_bound(g, BM, BN), per_cu);
-  const dim3 block(WM * WN * 64);
-  if (epi == kEpiBiasSilu)
-    hipLaunchKernelGGL((grouped_gemm_bf16_kernel<BM, BN, WM, WN, kEpiBiasSilu, GM>), dim3(grid),
-                       block, 0, s, a);
-  else
-    hipLaunchKernelGGL((grouped_gemm_bf16_kernel<BM, BN, WM, WN, kEpiBias, GM>), dim3(grid),
-                       block, 0, s, a);
-  return hipGetLastError();
-}
-
 constexpr int kSplitCap = 8;
 constexpr int64_t kSplitMaxRows = 4096;   // partial rows (reduce grid.y, scratch size)
 
@@ -1473,40 +1091,6 @@ hipError_t launch_bf16_stream(const GemmArgs &a, const GemmGroups &g, Epilogue e
 
 constexpr int64_t kRsPieceBytes = 256 * 256 * sizeof(float);
 constexpr int kRsMaxBlocks = 256;
-
-template <int MB, int NTB, int R>
-hipError_t launch_bf16_rstream(const GemmArgs &a, const GemmGroups &g, Epilogue epi,
-                               hipStream_t s) {
-  StreamSplit sp{};
-  sp.ks_cap = 1;
-  const int64_t prows = split_rows(g);
-  if (g.split_ws && prows <= kSplitMaxRows && g.split_bytes > 256) {
-    const int64_t per = prows * g.Nout * static_cast<int64_t>(sizeof(float));
-    const int64_t cap = (static_cast<int64_t>(g.split_bytes) - 256) / per;
-    if (cap > 1) {
-      sp.ks_used = static_cast<int *>(g.split_ws);
-      sp.partial = reinterpret_cast<float *>(static_cast<char *>(g.split_ws) + 256);
-      sp.part_rows = g.max_routed_rows;
-      sp.ks_cap = static_cast<int>(cap < kSplitCap ? cap : kSplitCap);
-    }
-  }
-  const unsigned grid =
-      persistent_grid(tiles_upper_bound(g, 32 * NTB, 128 * MB) * sp.ks_cap, 1);
-  if (epi == kEpiBiasSilu)
-    hipLaunchKernelGGL((grouped_gemm_bf16_rstream_kernel<MB, NTB, R, kEpiBiasSilu>),
-                       dim3(grid), dim3(256), 0, s, a, sp);
-  else
-    hipLaunchKernelGGL((grouped_gemm_bf16_rstream_kernel<MB, NTB, R, kEpiBias>), dim3(grid),
-                       dim3(256), 0, s, a, sp);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess || sp.ks_cap <= 1) return e;
-  const dim3 rgrid(static_cast<unsigned>((g.Nout / 4 + 255) / 256), static_cast<unsigned>(prows));
-  if (epi == kEpiBiasSilu)
-    hipLaunchKernelGGL((stream_reduce_kernel<kEpiBiasSilu>), rgrid, dim3(256), 0, s, a, sp);
-  else
-    hipLaunchKernelGGL((stream_reduce_kernel<kEpiBias>), rgrid, dim3(256), 0, s, a, sp);
-  return hipGetLastError();
-}
 
 template <int GM>
 hipError_t launch_bf16_rs(const GemmArgs &a, const GemmGroups &g, Epilogue epi, hipStream_t s) {
@@ -1562,12 +1146,12 @@ hipError_t launch_grouped_gemm(bool bf16, const GemmGroups &g, Epilogue epi, hip
     const bool any_small = (g.n_routed > 0 && mean_rows < 384) || (g.n_shared > 0 && g.T_sh <= kStreamRows);
     if (!any_big) return launch_bf16_stream<1, 1, 6>(a, g, epi, 1, s);
     if (!any_small) return launch_bf16_rs<8>(a, g, epi, s);
-    a.cls_lo = kStreamRows + 1;
-    hipError_t e = launch_bf16_rs<8>(a, g, epi, s);
+    GemmArgs ab = a, as = a;
+    ab.cls_lo = kStreamRows + 1;
+    as.cls_hi = kStreamRows;
+    hipError_t e = launch_bf16_rs<8>(ab, g, epi, s);
     if (e != hipSuccess) return e;
-    a.cls_lo = 0;
-    a.cls_hi = kStreamRows;
-    return launch_bf16_stream<2, 2, 3>(a, g, epi, 1, s);
+    return launch_bf16_stream<2, 2, 3>(as, g, epi, 1, s);
   }
   const unsigned grid = persistent_grid(tiles_upper_bound(g, 64, 64), 4);
   if (bf16) {
