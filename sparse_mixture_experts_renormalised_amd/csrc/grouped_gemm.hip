@@ -116,6 +116,25 @@ __device__ int build_tile_prefix(const GemmArgs &a, int *s_pref, int *s_tmp) {
   return total;
 }
 
+// Prefix over groups of count(g) tiles, built in LDS by every workgroup.
+template <int NT, typename F>
+__device__ int build_prefix(int n_groups, F count, int *s_pref, int *s_tmp) {
+  const int per = (n_groups + NT - 1) / NT;
+  const int g0 = threadIdx.x * per;
+  const int g1 = min(g0 + per, n_groups);
+  int local = 0;
+  for (int g = g0; g < g1; ++g) local += count(g);
+  int total;
+  int run = block_excl_scan<NT>(local, s_tmp, &total);
+  for (int g = g0; g < g1; ++g) {
+    s_pref[g] = run;
+    run += count(g);
+  }
+  if (threadIdx.x == 0) s_pref[n_groups] = total;
+  __syncthreads();
+  return total;
+}
+
 // Group of m-tile mt: largest g with s_pref[g] <= mt (never an empty group).
 __device__ __forceinline__ int find_group(const int *s_pref, int n_groups, int mt) {
   int lo = 0, hi = n_groups;   // invariant: s_pref[lo] <= mt < s_pref[hi]
@@ -289,6 +308,94 @@ __device__ __forceinline__ void lds_barrier() {
 }
 }  // namespace rs
 
+// Half-height tiles: the last m-tile of a group often holds 128 rows or
+// fewer (an expert of 1,052 rows leaves 28 in its fifth 256-row tile).  Such
+// a tile is computed as 128 x 256 by all four waves (2 x 2 waves of 64 x 128)
+// instead of leaving half the waves to multiply padding rows: same operand
+// path and swizzle, half the A rows and MFMAs.
+namespace rh {
+constexpr int BM = 128, BN = 256, BK = 64, NT = 256, WTM = 64, WTN = 128;
+constexpr int TM = WTM / 32, TN = WTN / 32, NS = BK / 16;
+constexpr int A_CH = BM * 8 / NT, B_CH = BN * 8 / NT;
+using rs::swz;
+
+struct Frags {
+  bf16x8_t a[NS][TM];
+  bf16x8_t b[NS][TN];
+};
+
+__device__ __forceinline__ void gload(u32x4_t (&ra)[A_CH], u32x4_t (&rb)[B_CH],
+                                      const uint16_t *const (&a_src)[A_CH],
+                                      const uint16_t *const (&b_src)[B_CH], int kb) {
+#pragma unroll
+  for (int i = 0; i < A_CH; ++i) ra[i] = *reinterpret_cast<const u32x4_t *>(a_src[i] + kb * BK);
+#pragma unroll
+  for (int i = 0; i < B_CH; ++i) rb[i] = *reinterpret_cast<const u32x4_t *>(b_src[i] + kb * BK);
+}
+
+__device__ __forceinline__ void lstore(uint16_t *tile, const u32x4_t (&ra)[A_CH],
+                                       const u32x4_t (&rb)[B_CH], int tid) {
+  const int kc = tid & 7;
+#pragma unroll
+  for (int i = 0; i < A_CH; ++i) {
+    const int row = (tid >> 3) + i * (NT / 8);
+    *reinterpret_cast<u32x4_t *>(tile + row * BK + (swz(row, kc) << 3)) = ra[i];
+  }
+#pragma unroll
+  for (int i = 0; i < B_CH; ++i) {
+    const int row = (tid >> 3) + i * (NT / 8);
+    *reinterpret_cast<u32x4_t *>(tile + BM * BK + row * BK + (swz(row, kc) << 3)) = rb[i];
+  }
+}
+
+__device__ __forceinline__ void read_frags(const uint16_t *tile, Frags &f, int wm, int wn,
+                                           int lane) {
+#pragma unroll
+  for (int ks = 0; ks < NS; ++ks) {
+    const int c = ks * 2 + (lane >> 5);
+#pragma unroll
+    for (int mi = 0; mi < TM; ++mi) {
+      const int row = wm * WTM + mi * 32 + (lane & 31);
+      f.a[ks][mi] = *reinterpret_cast<const bf16x8_t *>(tile + row * BK + (swz(row, c) << 3));
+    }
+#pragma unroll
+    for (int ni = 0; ni < TN; ++ni) {
+      const int row = wn * WTN + ni * 32 + (lane & 31);
+      f.b[ks][ni] =
+          *reinterpret_cast<const bf16x8_t *>(tile + BM * BK + row * BK + (swz(row, c) << 3));
+    }
+  }
+}
+
+__device__ __forceinline__ void mfma_all(const Frags &f, f32x16_t (&acc)[TN][TM]) {
+#pragma unroll
+  for (int ks = 0; ks < NS; ++ks)
+#pragma unroll
+    for (int ni = 0; ni < TN; ++ni)
+#pragma unroll
+      for (int mi = 0; mi < TM; ++mi)
+        acc[ni][mi] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.b[ks][ni], f.a[ks][mi], acc[ni][mi],
+                                                              0, 0, 0);
+}
+
+// One step: 32 MFMAs; each of the 12 global loads / LDS writes shares a slot
+// with two MFMAs, then three fragment reads precede each of the last eight.
+__device__ __forceinline__ void schedule_step() {
+#pragma unroll
+  for (int i = 0; i < A_CH + B_CH; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);   // DS write
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA
+    __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);   // VMEM read
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA
+  }
+#pragma unroll
+  for (int i = 0; i < NS * (TM + TN) / 3; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x100, 3, 0);   // DS read
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA
+  }
+}
+}  // namespace rh
+
 // Epilogue of a 256x256 tile through LDS in two passes of 128 rows (the tile
 // buffer holds 128 x 256 bf16): in pass p every wave stores its row blocks
 // mi = 2p, 2p+1, so all four waves work in both passes.
@@ -364,15 +471,13 @@ struct RsSplit {
 };
 
 struct RsPlan {
-  int begin, full, end, rem, P, kper;
+  int full, rem, P, kper;
 };
 
-__device__ __forceinline__ RsPlan rs_plan(int total, int xcd, int nslots, int nk, bool can_split) {
+// cnt work items of one XCD over its nslots workgroups: full rounds, then a
+// remainder of rem items, cut into P K-pieces when rem fills at most half.
+__device__ __forceinline__ RsPlan rs_plan(int cnt, int nslots, int nk, bool can_split) {
   RsPlan p;
-  const int part = (total + kXcds - 1) / kXcds;
-  p.begin = xcd * part;
-  p.end = min(total, p.begin + part);
-  const int cnt = max(0, p.end - p.begin);
   p.full = (cnt / nslots) * nslots;
   p.rem = cnt - p.full;
   int P = 1;
@@ -381,6 +486,59 @@ __device__ __forceinline__ RsPlan rs_plan(int total, int xcd, int nslots, int nk
   p.kper = (nk + P - 1) / P;
   p.P = (nk + p.kper - 1) / p.kper;   // no empty pieces
   return p;
+}
+
+// The 256-row m-tiles in two lists: tiles of 129..256 rows, and the last
+// tiles of groups that end with 1..128 rows (computed at half height).  Each
+// XCD takes an equal contiguous share of both lists, full tiles first, so
+// that its last, partly filled round is made of the cheap tail tiles.
+__device__ __forceinline__ bool rs_half_tail(int64_t rows) {
+  const int64_t r = rows % rs::BM;
+  return r != 0 && r <= rh::BM;
+}
+
+struct RsTiles {
+  int total_mf, total_mh, n_nt;   // m-tiles per list, n-tiles
+  int begin_f, cnt_f, begin_h, cnt_h;
+};
+
+__device__ __forceinline__ RsTiles rs_tiles(const GemmArgs &a, int *s_pref_f, int *s_pref_h,
+                                            int *s_tmp, int xcd) {
+  RsTiles t;
+  const int n_groups = a.n_routed + a.n_shared;
+  t.total_mf = build_prefix<rs::NT>(n_groups, [&](int g) {
+    const int64_t rows = group_rows(a, g);
+    return static_cast<int>((rows + rs::BM - 1) / rs::BM) - (rs_half_tail(rows) ? 1 : 0);
+  }, s_pref_f, s_tmp);
+  t.total_mh = build_prefix<rs::NT>(n_groups, [&](int g) {
+    return rs_half_tail(group_rows(a, g)) ? 1 : 0;
+  }, s_pref_h, s_tmp);
+  t.n_nt = (a.Nout + rs::BN - 1) / rs::BN;
+  const int tot_f = t.total_mf * t.n_nt, tot_h = t.total_mh * t.n_nt;
+  const int part_f = (tot_f + kXcds - 1) / kXcds, part_h = (tot_h + kXcds - 1) / kXcds;
+  t.begin_f = xcd * part_f;
+  t.cnt_f = max(0, min(tot_f, t.begin_f + part_f) - t.begin_f);
+  t.begin_h = xcd * part_h;
+  t.cnt_h = max(0, min(tot_h, t.begin_h + part_h) - t.begin_h);
+  return t;
+}
+
+// Item i of this XCD's list: group, m-tile within the group, n-tile.
+template <int GM>
+__device__ __forceinline__ void rs_tile_at(const GemmArgs &a, const RsTiles &t,
+                                           const int *s_pref_f, const int *s_pref_h, int i,
+                                           int *g, int *lm, int *nt) {
+  const int n_groups = a.n_routed + a.n_shared;
+  int mt;
+  if (i < t.cnt_f) {
+    decode_tile<GM>(t.begin_f + i, t.total_mf, t.n_nt, &mt, nt);
+    *g = find_group(s_pref_f, n_groups, mt);
+    *lm = mt - s_pref_f[*g];
+  } else {
+    decode_tile<GM>(t.begin_h + (i - t.cnt_f), t.total_mh, t.n_nt, &mt, nt);
+    *g = find_group(s_pref_h, n_groups, mt);
+    *lm = static_cast<int>((group_rows(a, *g) + rs::BM - 1) / rs::BM) - 1;
+  }
 }
 
 // Accumulators of one 256x256 tile over K-steps k0 .. k0+nk-1.
@@ -438,6 +596,114 @@ __device__ __forceinline__ void rs_tile(const GemmArgs &a, const TileView<uint16
   __syncthreads();
 }
 
+// Accumulators of one 128 x 256 tile (the half-height tail of a group).
+__device__ __forceinline__ void rh_tile(const GemmArgs &a, const TileView<uint16_t> &v, int n0,
+                                        int nk, uint16_t *s_tile, int tid, int lane, int wm,
+                                        int wn, f32x16_t (&acc)[rh::TN][rh::TM]) {
+  using namespace rh;
+  const int kc = tid & 7;
+  const uint16_t *a_src[A_CH];
+  const uint16_t *b_src[B_CH];
+#pragma unroll
+  for (int i = 0; i < A_CH; ++i)
+    a_src[i] = a_row_ptr(a, v, v.row0 + (tid >> 3) + i * (NT / 8)) + kc * 8;
+#pragma unroll
+  for (int i = 0; i < B_CH; ++i) {
+    int n = n0 + (tid >> 3) + i * (NT / 8);
+    if (n >= a.Nout) n = a.Nout - 1;
+    b_src[i] = v.W + static_cast<int64_t>(n) * a.K + kc * 8;
+  }
+#pragma unroll
+  for (int i = 0; i < TN; ++i)
+#pragma unroll
+    for (int j = 0; j < TM; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+
+  u32x4_t ra[A_CH], rb[B_CH];
+  Frags f;
+  gload(ra, rb, a_src, b_src, 0);
+  lstore(s_tile, ra, rb, tid);
+  if (nk > 1) gload(ra, rb, a_src, b_src, 1);
+  __syncthreads();
+  read_frags(s_tile, f, wm, wn, lane);
+  __builtin_amdgcn_sched_barrier(0);
+  int kb = 0;
+  for (; kb + 2 < nk; ++kb) {
+    rs::lds_barrier();
+    lstore(s_tile, ra, rb, tid);
+    gload(ra, rb, a_src, b_src, kb + 2);
+    mfma_all(f, acc);
+    rs::lds_barrier();
+    read_frags(s_tile, f, wm, wn, lane);
+    schedule_step();
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  if (kb + 1 < nk) {
+    rs::lds_barrier();
+    lstore(s_tile, ra, rb, tid);
+    mfma_all(f, acc);
+    rs::lds_barrier();
+    read_frags(s_tile, f, wm, wn, lane);
+  }
+  mfma_all(f, acc);
+  __syncthreads();
+}
+
+// Epilogue of a 128 x 256 tile: one pass through the LDS staging rows.
+template <int EPI>
+__device__ __forceinline__ void rh_epilogue(const f32x16_t (&acc)[rh::TN][rh::TM],
+                                            const GemmArgs &a, const TileView<uint16_t> &v,
+                                            int n0, uint16_t *s_tile, int lane, int wm, int wn,
+                                            int tid) {
+  using namespace rh;
+  int el = lane, ewm = wm, ewn = wn, etid = tid;
+  asm volatile("" : "+v"(el), "+v"(etid), "+s"(ewm), "+s"(ewn));
+  constexpr int CH = BN / 8;
+#pragma unroll
+  for (int ni = 0; ni < TN; ++ni) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int nl = ewn * WTN + ni * 32 + q * 8 + (el >> 5) * 4;
+      const int n = n0 + nl;
+      float bv[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+      if (v.bias && n < a.Nout) {
+        const uint2 bq = *reinterpret_cast<const uint2 *>(v.bias + n);
+        bv[0] = __uint_as_float(bq.x << 16);
+        bv[1] = __uint_as_float(bq.x & 0xFFFF0000u);
+        bv[2] = __uint_as_float(bq.y << 16);
+        bv[3] = __uint_as_float(bq.y & 0xFFFF0000u);
+      }
+#pragma unroll
+      for (int mi = 0; mi < TM; ++mi) {
+        const int ml = ewm * WTM + mi * 32 + (el & 31);
+        float o[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          o[j] = acc[ni][mi][q * 4 + j] + bv[j];
+          if (EPI == kEpiBiasSilu) o[j] = silu_fast(o[j]);
+        }
+        uint2 packed;
+        packed.x = f32_to_bf16(o[0]) | (static_cast<uint32_t>(f32_to_bf16(o[1])) << 16);
+        packed.y = f32_to_bf16(o[2]) | (static_cast<uint32_t>(f32_to_bf16(o[3])) << 16);
+        const int p = (nl >> 3) ^ (ml & 31);
+        *reinterpret_cast<uint2 *>(s_tile + ml * BN + p * 8 + ((nl >> 2) & 1) * 4) = packed;
+      }
+    }
+  }
+  __syncthreads();
+  for (int i = etid; i < BM * CH; i += NT) {
+    const int r = i / CH, c = i % CH;
+    const int64_t row = v.row0 + r;
+    const int n = n0 + c * 8;
+    if (row < v.rows && n < a.Nout) {
+      const u32x4_t val = *reinterpret_cast<const u32x4_t *>(s_tile + r * BN + ((c ^ (r & 31)) << 3));
+      *reinterpret_cast<u32x4_t *>(v.C + (v.out_base + row) * a.Nout + n) = val;
+    }
+  }
+  __syncthreads();
+}
+
 // PIECE = false: whole tiles of the full rounds (of every round when there is
 // no split).  PIECE = true: the K pieces of the remainder tiles, one per
 // workgroup, stored as float32 partial tiles (launched right after, with the
@@ -447,29 +713,27 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void grouped_gemm_bf16_rs_kernel(GemmArgs a, RsSplit sp) {
   using namespace rs;
   __shared__ __attribute__((aligned(16))) uint16_t s_tile[TILE];
-  __shared__ int s_pref[kMaxGroups + 1];
+  __shared__ int s_pref_f[kMaxGroups + 1];
+  __shared__ int s_pref_h[kMaxGroups + 1];
   __shared__ int s_tmp[NT / 64];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = uniform(tid >> 6);
   const int wm = wave & 1, wn = wave >> 1;
-  const int n_groups = a.n_routed + a.n_shared;
-  const int total_m = build_tile_prefix<NT, BM>(a, s_pref, s_tmp);
-  const int n_nt = (a.Nout + BN - 1) / BN;
   const int xcd = blockIdx.x % kXcds;
   const int slot = blockIdx.x / kXcds;
   const int nslots = gridDim.x / kXcds;
   const int nk = a.K / BK;
-  const RsPlan pl = rs_plan(total_m * n_nt, xcd, nslots, nk,
+  const RsTiles t = rs_tiles(a, s_pref_f, s_pref_h, s_tmp, xcd);
+  const RsPlan pl = rs_plan(t.cnt_f + t.cnt_h, nslots, nk,
                             sp.partial != nullptr && static_cast<int>(gridDim.x) <= sp.max_blocks);
   f32x16_t acc[TN][TM];
   if constexpr (PIECE) {
     if (pl.P <= 1 || slot >= pl.rem * pl.P) return;
-    int mt, nt;
-    decode_tile<GM>(pl.begin + pl.full + slot / pl.P, total_m, n_nt, &mt, &nt);
-    const int g = find_group(s_pref, n_groups, mt);
-    const TileView<uint16_t> v = tile_view<uint16_t>(a, g, mt - s_pref[g], BM);
+    int g, lm, nt;
+    rs_tile_at<GM>(a, t, s_pref_f, s_pref_h, pl.full + slot / pl.P, &g, &lm, &nt);
+    const TileView<uint16_t> v = tile_view<uint16_t>(a, g, lm, BM);
     const int k0 = (slot % pl.P) * pl.kper;
     rs_tile(a, v, nt * BN, k0, min(nk, k0 + pl.kper) - k0, s_tile, tid, lane, wm, wn, acc);
     float4 *dst = reinterpret_cast<float4 *>(sp.partial + static_cast<int64_t>(blockIdx.x) * (BM * BN));
@@ -483,14 +747,19 @@ void grouped_gemm_bf16_rs_kernel(GemmArgs a, RsSplit sp) {
               make_float4(acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2],
                           acc[i][j][4 * q + 3]);
   } else {
-    const int end = pl.P > 1 ? pl.begin + pl.full : pl.end;
-    for (int L = pl.begin + slot; L < end; L += nslots) {
-      int mt, nt;
-      decode_tile<GM>(L, total_m, n_nt, &mt, &nt);
-      const int g = find_group(s_pref, n_groups, mt);
-      const TileView<uint16_t> v = tile_view<uint16_t>(a, g, mt - s_pref[g], BM);
-      rs_tile(a, v, nt * BN, 0, nk, s_tile, tid, lane, wm, wn, acc);
-      rs_epilogue<EPI>(acc, a, v, nt * BN, s_tile, lane, wm, wn, tid);
+    const int end = pl.P > 1 ? pl.full : t.cnt_f + t.cnt_h;
+    for (int i = slot; i < end; i += nslots) {
+      int g, lm, nt;
+      rs_tile_at<GM>(a, t, s_pref_f, s_pref_h, i, &g, &lm, &nt);
+      const TileView<uint16_t> v = tile_view<uint16_t>(a, g, lm, BM);
+      if (i >= t.cnt_f) {                  // half-height tail tile
+        f32x16_t acch[rh::TN][rh::TM];
+        rh_tile(a, v, nt * BN, nk, s_tile, tid, lane, wm, wn, acch);
+        rh_epilogue<EPI>(acch, a, v, nt * BN, s_tile, lane, wm, wn, tid);
+      } else {
+        rs_tile(a, v, nt * BN, 0, nk, s_tile, tid, lane, wm, wn, acc);
+        rs_epilogue<EPI>(acc, a, v, nt * BN, s_tile, lane, wm, wn, tid);
+      }
     }
   }
 }
@@ -503,25 +772,23 @@ void grouped_gemm_bf16_rs_kernel(GemmArgs a, RsSplit sp) {
 template <int EPI, int GM>
 __global__ __launch_bounds__(256) void rs_fixup_kernel(GemmArgs a, RsSplit sp, int gemm_grid) {
   using namespace rs;
-  __shared__ int s_pref[kMaxGroups + 1];
+  __shared__ int s_pref_f[kMaxGroups + 1];
+  __shared__ int s_pref_h[kMaxGroups + 1];
   __shared__ int s_tmp[NT / 64];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
   const int wm = wave & 1, wn = wave >> 1;
-  const int n_groups = a.n_routed + a.n_shared;
-  const int total_m = build_tile_prefix<NT, BM>(a, s_pref, s_tmp);
-  const int n_nt = (a.Nout + BN - 1) / BN;
   const int xcd = blockIdx.x % kXcds;
   const int t = (blockIdx.x / kXcds) >> 2;
   const int quarter = (blockIdx.x / kXcds) & 3;
-  const RsPlan pl = rs_plan(total_m * n_nt, xcd, gemm_grid / kXcds, a.K / BK,
+  const RsTiles tl = rs_tiles(a, s_pref_f, s_pref_h, s_tmp, xcd);
+  const RsPlan pl = rs_plan(tl.cnt_f + tl.cnt_h, gemm_grid / kXcds, a.K / BK,
                             sp.partial != nullptr && gemm_grid <= sp.max_blocks);
   if (pl.P <= 1 || t >= pl.rem) return;
-  int mt, nt;
-  decode_tile<GM>(pl.begin + pl.full + t, total_m, n_nt, &mt, &nt);
-  const int g = find_group(s_pref, n_groups, mt);
-  const TileView<uint16_t> v = tile_view<uint16_t>(a, g, mt - s_pref[g], BM);
+  int g, lm, nt;
+  rs_tile_at<GM>(a, tl, s_pref_f, s_pref_h, pl.full + t, &g, &lm, &nt);
+  const TileView<uint16_t> v = tile_view<uint16_t>(a, g, lm, BM);
   const int n0 = nt * BN;
   const int64_t blk0 = static_cast<int64_t>(t * pl.P) * kXcds + xcd;   // piece 0's workgroup
   // all 16 chunks of one piece are loaded together, pieces are added in order

@@ -305,6 +305,9 @@ FFN_CASES = [
     ("bf16_large_groups", [385, 0, 700, 513], 192, 320, "bf16", True),
     # one and two k-steps of 64
     ("bf16_large_short_k", [400, 450], 64, 128, "bf16", False),
+    # last 256-row tiles of 1, 128 and 129 rows (half-height tail tiles for the
+    # first two), small groups beside them
+    ("bf16_half_tails", [1, 128, 129, 257, 384, 385, 640, 513], 512, 320, "bf16", True),
     # a loose row bound widens the grid so that every XCD's tiles form a
     # partial round, which is split along K and reassembled: the first Linear
     # in 2 pieces, then the second in 4
