@@ -16,7 +16,9 @@ from typing import Optional
 import torch
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(HERE, "_lib", "libmoe_mi355x.so")
+# MOE_MI355X_LIB names another build of the same library (for example a
+# second build kept for side-by-side timing); the default is the in-tree one.
+LIB_PATH = os.environ.get("MOE_MI355X_LIB") or os.path.join(HERE, "_lib", "libmoe_mi355x.so")
 
 MOE_F32, MOE_BF16 = 0, 1
 STATUS = {0: "ok", -1: "invalid argument", -2: "unsupported size", -3: "workspace", -4: "HIP error"}

@@ -398,8 +398,10 @@ __device__ __forceinline__ void schedule_step() {
 
 // Epilogue of a 256x256 tile through LDS in two passes of 128 rows (the tile
 // buffer holds 128 x 256 bf16): in pass p every wave stores its row blocks
-// mi = 2p, 2p+1, so all four waves work in both passes.
-template <int EPI>
+// mi = 2p, 2p+1, so all four waves work in both passes.  The barriers only
+// order LDS accesses, so global loads issued before the epilogue (the next
+// tile's first K-steps) stay in flight across it.
+template <int EPI, bool BIAS>
 __device__ __forceinline__ void rs_epilogue(const f32x16_t (&acc)[rs::TN][rs::TM],
                                             const GemmArgs &a, const TileView<uint16_t> &v,
                                             int n0, uint16_t *s_tile, int lane, int wm, int wn,
@@ -418,7 +420,7 @@ __device__ __forceinline__ void rs_epilogue(const f32x16_t (&acc)[rs::TN][rs::TM
         const int nl = ewn * WTN + ni * 32 + q * 8 + (el >> 5) * 4;
         const int n = n0 + nl;
         float bv[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-        if (v.bias && n < a.Nout) {
+        if (BIAS && n < a.Nout) {
           const uint2 bq = *reinterpret_cast<const uint2 *>(v.bias + n);
           bv[0] = __uint_as_float(bq.x << 16);
           bv[1] = __uint_as_float(bq.x & 0xFFFF0000u);
@@ -432,18 +434,19 @@ __device__ __forceinline__ void rs_epilogue(const f32x16_t (&acc)[rs::TN][rs::TM
           float o[4];
 #pragma unroll
           for (int j = 0; j < 4; ++j) {
-            o[j] = acc[ni][mi][q * 4 + j] + bv[j];
+            o[j] = acc[ni][mi][q * 4 + j];
+            if (BIAS) o[j] += bv[j];
             if (EPI == kEpiBiasSilu) o[j] = silu_fast(o[j]);
           }
           uint2 packed;
-          packed.x = f32_to_bf16(o[0]) | (static_cast<uint32_t>(f32_to_bf16(o[1])) << 16);
-          packed.y = f32_to_bf16(o[2]) | (static_cast<uint32_t>(f32_to_bf16(o[3])) << 16);
+          packed.x = pack_bf16x2(o[0], o[1]);
+          packed.y = pack_bf16x2(o[2], o[3]);
           const int p = (nl >> 3) ^ (ml & 31);
           *reinterpret_cast<uint2 *>(s_tile + ml * BN + p * 8 + ((nl >> 2) & 1) * 4) = packed;
         }
       }
     }
-    __syncthreads();
+    rs::lds_barrier();
     // LDS row ml of the pass is tile row (ml/64)*128 + pass*64 + ml%64
     for (int i = etid; i < 128 * CH; i += NT) {
       const int r = i / CH, c = i % CH;
@@ -454,8 +457,19 @@ __device__ __forceinline__ void rs_epilogue(const f32x16_t (&acc)[rs::TN][rs::TM
         *reinterpret_cast<u32x4_t *>(v.C + (v.out_base + row) * a.Nout + n) = val;
       }
     }
-    __syncthreads();
+    rs::lds_barrier();
   }
+}
+
+template <int EPI>
+__device__ __forceinline__ void rs_epilogue(const f32x16_t (&acc)[rs::TN][rs::TM],
+                                            const GemmArgs &a, const TileView<uint16_t> &v,
+                                            int n0, uint16_t *s_tile, int lane, int wm, int wn,
+                                            int tid) {
+  if (v.bias)
+    rs_epilogue<EPI, true>(acc, a, v, n0, s_tile, lane, wm, wn, tid);
+  else
+    rs_epilogue<EPI, false>(acc, a, v, n0, s_tile, lane, wm, wn, tid);
 }
 
 // Splitting the last, partly filled round of tiles along K.  Per XCD the
@@ -541,23 +555,46 @@ __device__ __forceinline__ void rs_tile_at(const GemmArgs &a, const RsTiles &t,
   }
 }
 
-// Accumulators of one 256x256 tile over K-steps k0 .. k0+nk-1.
-__device__ __forceinline__ void rs_tile(const GemmArgs &a, const TileView<uint16_t> &v, int n0,
-                                        int k0, int nk, uint16_t *s_tile, int tid, int lane,
-                                        int wm, int wn, f32x16_t (&acc)[rs::TN][rs::TM]) {
+// Source addresses of this thread's 16-byte chunks of a 256x256 tile, from
+// K-step k0 on.
+struct RsSrc {
+  const uint16_t *a[rs::A_CH];
+  const uint16_t *b[rs::B_CH];
+};
+
+// The first K-step of a tile in registers: issued before the previous
+// tile's epilogue, so its latency overlaps that epilogue.
+struct RsHead {
+  u32x4_t ra0[rs::A_CH], rb0[rs::B_CH];
+};
+
+__device__ __forceinline__ void rs_src(const GemmArgs &a, const TileView<uint16_t> &v, int n0,
+                                       int k0, int tid, RsSrc &src) {
   using namespace rs;
   const int kc = tid & 7;
-  const uint16_t *a_src[A_CH];
-  const uint16_t *b_src[B_CH];
 #pragma unroll
   for (int i = 0; i < A_CH; ++i)
-    a_src[i] = a_row_ptr(a, v, v.row0 + (tid >> 3) + i * (NT / 8)) + kc * 8 + k0 * BK;
+    src.a[i] = a_row_ptr(a, v, v.row0 + (tid >> 3) + i * (NT / 8)) + kc * 8 + k0 * BK;
 #pragma unroll
   for (int i = 0; i < B_CH; ++i) {
     int n = n0 + (tid >> 3) + i * (NT / 8);
     if (n >= a.Nout) n = a.Nout - 1;
-    b_src[i] = v.W + static_cast<int64_t>(n) * a.K + kc * 8 + k0 * BK;
+    src.b[i] = v.W + static_cast<int64_t>(n) * a.K + kc * 8 + k0 * BK;
   }
+}
+
+__device__ __forceinline__ void rs_head(const RsSrc &src, RsHead &h) {
+  rs::gload(h.ra0, h.rb0, src.a, src.b, 0);
+}
+
+// Accumulators of one 256x256 tile over the nk K-steps that src points at,
+// the first of them already in h.  Returns once the last step's MFMAs
+// are issued; the caller passes an LDS barrier before reusing the tile
+// buffer.
+__device__ __forceinline__ void rs_body(const RsSrc &src, int nk, const RsHead &h,
+                                        uint16_t *s_tile, int tid, int lane, int wm, int wn,
+                                        f32x16_t (&acc)[rs::TN][rs::TM]) {
+  using namespace rs;
 #pragma unroll
   for (int i = 0; i < TN; ++i)
 #pragma unroll
@@ -567,33 +604,43 @@ __device__ __forceinline__ void rs_tile(const GemmArgs &a, const TileView<uint16
 
   u32x4_t ra[A_CH], rb[B_CH];
   Frags f;
-  gload(ra, rb, a_src, b_src, 0);
-  lstore(s_tile, ra, rb, tid);
-  if (nk > 1) gload(ra, rb, a_src, b_src, 1);
-  __syncthreads();
+  lstore(s_tile, h.ra0, h.rb0, tid);
+  if (nk > 1) gload(ra, rb, src.a, src.b, 1);
+  lds_barrier();
   read_frags(s_tile, f, wm, wn, lane);
   __builtin_amdgcn_sched_barrier(0);
   // steady state (no branches, so each step is one scheduling region)
   int kb = 0;
   for (; kb + 2 < nk; ++kb) {
-    lds_barrier();                        // every wave has its fragments of step kb
-    lstore(s_tile, ra, rb, tid);          // step kb+1 into LDS
-    gload(ra, rb, a_src, b_src, kb + 2);  // step kb+2 into registers
-    mfma_all(f, acc);                     // step kb
-    lds_barrier();                        // step kb+1 is in LDS
+    lds_barrier();                          // every wave has its fragments of step kb
+    lstore(s_tile, ra, rb, tid);            // step kb+1 into LDS
+    gload(ra, rb, src.a, src.b, kb + 2);    // step kb+2 into registers
+    mfma_all(f, acc);                       // step kb
+    lds_barrier();                          // step kb+1 is in LDS
     read_frags(s_tile, f, wm, wn, lane);
     schedule_step();
     __builtin_amdgcn_sched_barrier(0);
   }
-  if (kb + 1 < nk) {                      // step nk-2: nothing left to load
+  if (kb + 1 < nk) {                        // step nk-2: nothing left to load
     lds_barrier();
     lstore(s_tile, ra, rb, tid);
     mfma_all(f, acc);
     lds_barrier();
     read_frags(s_tile, f, wm, wn, lane);
   }
-  mfma_all(f, acc);                       // last step
-  __syncthreads();
+  mfma_all(f, acc);                         // last step
+}
+
+// Accumulators of one 256x256 tile over K-steps k0 .. k0+nk-1.
+__device__ __forceinline__ void rs_tile(const GemmArgs &a, const TileView<uint16_t> &v, int n0,
+                                        int k0, int nk, uint16_t *s_tile, int tid, int lane,
+                                        int wm, int wn, f32x16_t (&acc)[rs::TN][rs::TM]) {
+  RsSrc src;
+  RsHead h;
+  rs_src(a, v, n0, k0, tid, src);
+  rs_head(src, h);
+  rs_body(src, nk, h, s_tile, tid, lane, wm, wn, acc);
+  rs::lds_barrier();
 }
 
 // Accumulators of one 128 x 256 tile (the half-height tail of a group).
@@ -684,8 +731,8 @@ __device__ __forceinline__ void rh_epilogue(const f32x16_t (&acc)[rh::TN][rh::TM
           if (EPI == kEpiBiasSilu) o[j] = silu_fast(o[j]);
         }
         uint2 packed;
-        packed.x = f32_to_bf16(o[0]) | (static_cast<uint32_t>(f32_to_bf16(o[1])) << 16);
-        packed.y = f32_to_bf16(o[2]) | (static_cast<uint32_t>(f32_to_bf16(o[3])) << 16);
+        packed.x = pack_bf16x2(o[0], o[1]);
+        packed.y = pack_bf16x2(o[2], o[3]);
         const int p = (nl >> 3) ^ (ml & 31);
         *reinterpret_cast<uint2 *>(s_tile + ml * BN + p * 8 + ((nl >> 2) & 1) * 4) = packed;
       }
@@ -748,18 +795,21 @@ void grouped_gemm_bf16_rs_kernel(GemmArgs a, RsSplit sp) {
                           acc[i][j][4 * q + 3]);
   } else {
     const int end = pl.P > 1 ? pl.full : t.cnt_f + t.cnt_h;
-    for (int i = slot; i < end; i += nslots) {
-      int g, lm, nt;
+    const int end_f = min(end, t.cnt_f);
+    int g, lm, nt;
+    int i = slot;
+    for (; i < end_f; i += nslots) {       // full-cost tiles
       rs_tile_at<GM>(a, t, s_pref_f, s_pref_h, i, &g, &lm, &nt);
       const TileView<uint16_t> v = tile_view<uint16_t>(a, g, lm, BM);
-      if (i >= t.cnt_f) {                  // half-height tail tile
-        f32x16_t acch[rh::TN][rh::TM];
-        rh_tile(a, v, nt * BN, nk, s_tile, tid, lane, wm, wn, acch);
-        rh_epilogue<EPI>(acch, a, v, nt * BN, s_tile, lane, wm, wn, tid);
-      } else {
-        rs_tile(a, v, nt * BN, 0, nk, s_tile, tid, lane, wm, wn, acc);
-        rs_epilogue<EPI>(acc, a, v, nt * BN, s_tile, lane, wm, wn, tid);
-      }
+      rs_tile(a, v, nt * BN, 0, nk, s_tile, tid, lane, wm, wn, acc);
+      rs_epilogue<EPI>(acc, a, v, nt * BN, s_tile, lane, wm, wn, tid);
+    }
+    for (; i < end; i += nslots) {         // half-height tail tiles
+      rs_tile_at<GM>(a, t, s_pref_f, s_pref_h, i, &g, &lm, &nt);
+      const TileView<uint16_t> v = tile_view<uint16_t>(a, g, lm, BM);
+      f32x16_t acch[rh::TN][rh::TM];
+      rh_tile(a, v, nt * BN, nk, s_tile, tid, lane, wm, wn, acch);
+      rh_epilogue<EPI>(acch, a, v, nt * BN, s_tile, lane, wm, wn, tid);
     }
   }
 }
@@ -830,8 +880,8 @@ __global__ __launch_bounds__(256) void rs_fixup_kernel(GemmArgs a, RsSplit sp, i
 #pragma unroll
       for (int e = 0; e < 4; ++e) o[e] = silu_fast(o[e]);
     uint2 packed;
-    packed.x = f32_to_bf16(o[0]) | (static_cast<uint32_t>(f32_to_bf16(o[1])) << 16);
-    packed.y = f32_to_bf16(o[2]) | (static_cast<uint32_t>(f32_to_bf16(o[3])) << 16);
+    packed.x = pack_bf16x2(o[0], o[1]);
+    packed.y = pack_bf16x2(o[2], o[3]);
     *reinterpret_cast<uint2 *>(v.C + (v.out_base + row) * a.Nout + n) = packed;
   }
 }
@@ -979,8 +1029,8 @@ __device__ __forceinline__ void stream_store(const f32x16_t (&acc)[MB][NTB], con
               if (EPI == kEpiBiasSilu) o[e] = silu_fast(o[e]);
             }
             uint2 packed;
-            packed.x = f32_to_bf16(o[0]) | (static_cast<uint32_t>(f32_to_bf16(o[1])) << 16);
-            packed.y = f32_to_bf16(o[2]) | (static_cast<uint32_t>(f32_to_bf16(o[3])) << 16);
+            packed.x = pack_bf16x2(o[0], o[1]);
+            packed.y = pack_bf16x2(o[2], o[3]);
             *reinterpret_cast<uint2 *>(dst + n) = packed;
           }
         }
@@ -988,12 +1038,13 @@ __device__ __forceinline__ void stream_store(const f32x16_t (&acc)[MB][NTB], con
   }
 }
 
-// One unit of the stream kernel (unit index L of the k-split ks, kc_per
-// chunks per part); `stage` is the ring position of the next chunk, carried
-// from unit to unit of one workgroup.
-template <int MB, int NTB, int S, int EPI>
-__device__ __forceinline__ void stream_unit(const GemmArgs &a, const StreamSplit &sp,
-                                            const int *s_pref, int L, int ks, int kc_per,
+// One unit of the stream kernel: rows rb*32*NTB .. of group g (mg row blocks),
+// features nb*128*MB .., K part kp of kc_per chunks.  Ring stages are STRIDE
+// bf16 elements apart; `stage` is the ring position of the next chunk,
+// carried from unit to unit of one workgroup.
+template <int MB, int NTB, int S, int STRIDE, int EPI>
+__device__ __forceinline__ void stream_unit(const GemmArgs &a, const StreamSplit &sp, int g,
+                                            int mg, int nb, int rb, int kp, int ks, int kc_per,
                                             uint16_t *s_ring, uint32_t ring0, int &stage,
                                             int lane, int wave) {
   using namespace st;
@@ -1002,23 +1053,12 @@ __device__ __forceinline__ void stream_unit(const GemmArgs &a, const StreamSplit
   constexpr int W_INS = NB / 8 / NW;             // weight copies per wave per chunk
   constexpr int X_INS = MR / 8 / NW;             // activation copies per wave per chunk
   constexpr int LPS = W_INS + X_INS;
-  constexpr int STAGE = (NB + MR) * KCH;         // bf16 elements
+  static_assert((NB + MR) * KCH <= STRIDE, "stage fits its ring slot");
   static_assert((S - 2) * LPS <= 63, "vmcnt range");
   const int r32 = lane & 31, h = lane >> 5;
-  const int n_groups = a.n_routed + a.n_shared;
-  const int n_nb = (a.Nout + NB - 1) / NB;
   const int nkc = a.K / KCH;
   // lane's place in a copy: row lane/8 of an 8-row block, LDS piece lane%8
   const int crow = lane >> 3, cpos = lane & 7;
-
-  // unit order: part fastest, then row block, then feature block, so the
-  // workgroups running together share a weight block in L2
-  const int kp = L % ks;
-  const int u = L / ks;
-  const int g = find_group(s_pref, n_groups, u / n_nb);
-  const int mg = s_pref[g + 1] - s_pref[g];
-  const int uu = u - s_pref[g] * n_nb;
-  const int nb = uu / mg, rb = uu % mg;
   const TileView<uint16_t> v = tile_view<uint16_t>(a, g, rb, MR);
   const int n0 = nb * NB;
   const int kc0 = kp * kc_per;
@@ -1041,7 +1081,7 @@ __device__ __forceinline__ void stream_unit(const GemmArgs &a, const StreamSplit
   // weights of a group with one row block are read once: stream them
   const bool w_once = mg == 1;
   auto issue = [&](int c, int st_idx) {
-    const uint32_t base = ring0 + static_cast<uint32_t>(st_idx) * (STAGE * 2);
+    const uint32_t base = ring0 + static_cast<uint32_t>(st_idx) * (STRIDE * 2);
     if (w_once) {
 #pragma unroll
       for (int i = 0; i < W_INS; ++i) dma16_nt(w_src[i] + c * KCH, base + (i * NW + wave) * 1024);
@@ -1071,7 +1111,7 @@ __device__ __forceinline__ void stream_unit(const GemmArgs &a, const StreamSplit
     else wait_chunks<LPS, S - 3>(later);
     const int cur = (stage + c) % S;
     if (c + S - 1 < nch) issue(c + S - 1, (stage + c + S - 1) % S);
-    const uint16_t *sw = s_ring + cur * STAGE;
+    const uint16_t *sw = s_ring + cur * STRIDE;
     const uint16_t *sx = sw + NB * KCH;
 #pragma unroll
     for (int kst = 0; kst < 4; ++kst) {
@@ -1098,19 +1138,28 @@ __device__ __forceinline__ void stream_unit(const GemmArgs &a, const StreamSplit
   stream_store<MB, NTB, EPI>(acc, a, v, g, n0 + wave * 32 * MB, kp, ks, sp, r32, h);
 }
 
-template <int MB, int NTB, int S, int EPI>
+// NTB2 > NTB gives the kernel a second unit height: groups of more than
+// 32*NTB rows take units of 32*NTB2 rows, so a group of up to 32*NTB2 rows
+// reads each weight block once.  Both shapes share the ring (slots sized
+// for the larger stage) and its position.
+template <int MB, int NTB, int NTB2, int S, int EPI>
 __global__ __launch_bounds__(256) void grouped_gemm_bf16_stream_kernel(GemmArgs a, StreamSplit sp) {
   using namespace st;
-  constexpr int MR = 32 * NTB;
+  constexpr int MR1 = 32 * NTB, MR2 = 32 * (NTB2 > NTB ? NTB2 : NTB);
   constexpr int NB = 4 * 32 * MB;
-  constexpr int STAGE = (NB + MR) * KCH;
-  __shared__ __attribute__((aligned(16))) uint16_t s_ring[S * STAGE];
+  constexpr int STRIDE = (NB + MR2) * KCH;
+  __shared__ __attribute__((aligned(16))) uint16_t s_ring[S * STRIDE];
   __shared__ int s_pref[kMaxGroups + 1];
   __shared__ int s_tmp[NT / 64];
 
   const int lane = threadIdx.x & 63;
   const int wave = uniform(threadIdx.x >> 6);
-  const int total_m = build_tile_prefix<NT, MR>(a, s_pref, s_tmp);
+  const int n_groups = a.n_routed + a.n_shared;
+  const int total_m = build_prefix<NT>(n_groups, [&](int g) {
+    const int64_t rows = group_rows(a, g);
+    const int mr = rows <= MR1 ? MR1 : MR2;
+    return static_cast<int>((rows + mr - 1) / mr);
+  }, s_pref, s_tmp);
   const int n_nb = (a.Nout + NB - 1) / NB;
   const int nkc = a.K / KCH;
   int kc_per;
@@ -1125,8 +1174,23 @@ __global__ __launch_bounds__(256) void grouped_gemm_bf16_stream_kernel(GemmArgs 
   const int end = min(total, begin + part);
   const uint32_t ring0 = uniform(static_cast<int>(lds_addr(s_ring)));
   int stage = 0;
-  for (int L = begin + slot; L < end; L += nslots)
-    stream_unit<MB, NTB, S, EPI>(a, sp, s_pref, L, ks, kc_per, s_ring, ring0, stage, lane, wave);
+  for (int L = begin + slot; L < end; L += nslots) {
+    // unit order: part fastest, then row block, then feature block, so the
+    // workgroups running together share a weight block in L2
+    const int kp = L % ks;
+    const int u = L / ks;
+    const int g = find_group(s_pref, n_groups, u / n_nb);
+    const int mg = s_pref[g + 1] - s_pref[g];
+    const int uu = u - s_pref[g] * n_nb;
+    const int nb = uu / mg, rb = uu % mg;
+    if (NTB2 <= NTB || group_rows(a, g) <= MR1)
+      stream_unit<MB, NTB, S, STRIDE, EPI>(a, sp, g, mg, nb, rb, kp, ks, kc_per, s_ring, ring0,
+                                           stage, lane, wave);
+    else
+      stream_unit<MB, (NTB2 > NTB ? NTB2 : NTB), S, STRIDE, EPI>(a, sp, g, mg, nb, rb, kp, ks,
+                                                                 kc_per, s_ring, ring0, stage,
+                                                                 lane, wave);
+  }
 }
 
 // Sum of the k-split partials in part order, bias, epilogue, bf16 store.
@@ -1179,8 +1243,8 @@ __global__ __launch_bounds__(256) void stream_reduce_kernel(GemmArgs a, StreamSp
 #pragma unroll
     for (int e = 0; e < 4; ++e) o[e] = silu_fast(o[e]);
   uint2 packed;
-  packed.x = f32_to_bf16(o[0]) | (static_cast<uint32_t>(f32_to_bf16(o[1])) << 16);
-  packed.y = f32_to_bf16(o[2]) | (static_cast<uint32_t>(f32_to_bf16(o[3])) << 16);
+  packed.x = pack_bf16x2(o[0], o[1]);
+  packed.y = pack_bf16x2(o[2], o[3]);
   *reinterpret_cast<uint2 *>(dst + n) = packed;
 }
 
@@ -1322,7 +1386,7 @@ int64_t split_rows(const GemmGroups &g) {
   return g.max_routed_rows + static_cast<int64_t>(g.n_shared) * g.T_sh;
 }
 
-template <int MB, int NTB, int S>
+template <int MB, int NTB, int S, int NTB2 = 0>
 hipError_t launch_bf16_stream(const GemmArgs &a, const GemmGroups &g, Epilogue epi, int per_cu,
                               hipStream_t s) {
   StreamSplit sp{};
@@ -1341,10 +1405,10 @@ hipError_t launch_bf16_stream(const GemmArgs &a, const GemmGroups &g, Epilogue e
   const unsigned grid =
       persistent_grid(tiles_upper_bound(g, 32 * NTB, 128 * MB) * sp.ks_cap, per_cu);
   if (epi == kEpiBiasSilu)
-    hipLaunchKernelGGL((grouped_gemm_bf16_stream_kernel<MB, NTB, S, kEpiBiasSilu>),
+    hipLaunchKernelGGL((grouped_gemm_bf16_stream_kernel<MB, NTB, NTB2, S, kEpiBiasSilu>),
                        dim3(grid), dim3(256), 0, s, a, sp);
   else
-    hipLaunchKernelGGL((grouped_gemm_bf16_stream_kernel<MB, NTB, S, kEpiBias>), dim3(grid),
+    hipLaunchKernelGGL((grouped_gemm_bf16_stream_kernel<MB, NTB, NTB2, S, kEpiBias>), dim3(grid),
                        dim3(256), 0, s, a, sp);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || sp.ks_cap <= 1) return e;
@@ -1403,22 +1467,29 @@ hipError_t launch_grouped_gemm(bool bf16, const GemmGroups &g, Epilogue epi, hip
   if (g.n_routed + g.n_shared <= 0 || g.Nout <= 0) return hipSuccess;
   if (bf16 && g.K % 64 == 0 && g.Nout % 4 == 0) {
     // Groups of up to kStreamRows rows are bound by their weight stream and
-    // go to the stream kernel; larger groups reuse each weight tile across
-    // 256 rows in the 256x256 kernel.  Each kernel takes its own size class.
-    constexpr int64_t kStreamRows = 256;
+    // go to the stream kernel (units of 64 rows up to 64 rows, else 128, so
+    // each weight block is read once); larger groups reuse each weight tile
+    // across up to 256 rows in the 256x256 kernel, which measures faster
+    // from about 130 rows on.  Each kernel takes its own size class.
+    // Batches of at most 32 rows per group (decode) use the deep-ring
+    // 32-row shape.
+    constexpr int64_t kStreamRows = 128;
     const int64_t groups = g.n_routed > 0 ? g.n_routed : 1;
     const int64_t mean_rows = g.max_routed_rows / groups;
     const int64_t max_rows = g.n_routed > 0 ? g.max_group_rows : 0;
     const bool any_big = max_rows > kStreamRows || (g.n_shared > 0 && g.T_sh > kStreamRows);
     const bool any_small = (g.n_routed > 0 && mean_rows < 384) || (g.n_shared > 0 && g.T_sh <= kStreamRows);
-    if (!any_big) return launch_bf16_stream<1, 1, 6>(a, g, epi, 1, s);
+    if (!any_big) {
+      if (max_rows <= 32) return launch_bf16_stream<1, 1, 6>(a, g, epi, 1, s);
+      return launch_bf16_stream<2, 2, 3, 4>(a, g, epi, 1, s);
+    }
     if (!any_small) return launch_bf16_rs<8>(a, g, epi, s);
     GemmArgs ab = a, as = a;
     ab.cls_lo = kStreamRows + 1;
     as.cls_hi = kStreamRows;
     hipError_t e = launch_bf16_rs<8>(ab, g, epi, s);
     if (e != hipSuccess) return e;
-    return launch_bf16_stream<2, 2, 3>(as, g, epi, 1, s);
+    return launch_bf16_stream<2, 2, 3, 4>(as, g, epi, 1, s);
   }
   const unsigned grid = persistent_grid(tiles_upper_bound(g, 64, 64), 4);
   if (bf16) {

@@ -33,6 +33,14 @@ template <> struct Act<uint16_t> {
   static __device__ __forceinline__ uint16_t from_f32(float v) { return f32_to_bf16(v); }
 };
 
+// Two floats to packed bfloat16 (lo in bits 0..15), round to nearest even:
+// one v_cvt_pk_bf16_f32 on gfx950, the same bits as f32_to_bf16 on each.
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2_hw_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2_t){lo, hi}, bf16x2_hw_t));
+}
+
 __device__ __forceinline__ float silu(float z) { return z / (1.0f + __expf(-z)); }
 
 // SiLU with the hardware exp2 and reciprocal (about 1 ulp each in float32),

@@ -300,6 +300,9 @@ FFN_CASES = [
     ("bf16_bias", [3, 200, 64], 64, 128, "bf16", True),
     ("bf16_decode_tile", [1, 5, 0, 3, 5, 2, 4, 5, 5, 1], 256, 320, "bf16", False),
     ("bf16_ntail", [40, 90], 320, 704, "bf16", False),
+    # at most 128 rows per group: the stream kernel alone, with 64-row units
+    # for groups of up to 64 rows and 128-row units above
+    ("bf16_stream_two_heights", [3, 40, 70, 0, 15], 256, 320, "bf16", True),
     # mean rows >= 384: the 256x256 large-group kernel, with partial m and n
     # tiles, an empty group and 3 / 5 k-steps of 64
     ("bf16_large_groups", [385, 0, 700, 513], 192, 320, "bf16", True),
