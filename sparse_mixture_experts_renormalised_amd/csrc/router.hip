@@ -22,9 +22,10 @@ namespace {
 // Logits as a register-tiled product: a workgroup covers BT tokens x BE
 // experts, each thread MT tokens x ME experts; K advances in chunks of KC
 // staged through LDS (x converted to float32 exactly, layout [k][token] and
-// [k][expert] so each thread reads its MT / ME values as one vector).  Every
-// accumulator still sees its terms one at a time in ascending k.
-template <int BT, int BE, int MT, int ME, int KC, bool BF16>
+// [k][expert] so each thread reads its MT / ME values as one vector).  Global
+// loads run PF chunks ahead (PF = 2: two register sets).  Every accumulator
+// still sees its terms one at a time in ascending k.
+template <int BT, int BE, int MT, int ME, int KC, bool BF16, int PF = 1>
 __global__ __launch_bounds__(256) void router_logits_kernel(
     const void *__restrict__ xv, const float *__restrict__ w, const float *__restrict__ bias,
     float *__restrict__ logits, int64_t T, int d, int N) {
@@ -43,9 +44,14 @@ __global__ __launch_bounds__(256) void router_logits_kernel(
   const int e0 = blockIdx.y * BE;
   const int tm = tid % NTT, te = tid / NTT;
 
-  uint4 rx[XPT];
-  float4 rw[WPT];
-  auto gload = [&](int k0) {
+  float acc[MT][ME];
+#pragma unroll
+  for (int i = 0; i < MT; ++i)
+#pragma unroll
+    for (int j = 0; j < ME; ++j) acc[i][j] = 0.0f;
+  uint4 rx[2][XPT];
+  float4 rw[2][WPT];
+  auto gload_set = [&](uint4 (&rxs)[XPT], float4 (&rws)[WPT], int k0) {
 #pragma unroll
     for (int i = 0; i < XPT; ++i) {
       const int id = tid + i * 256;
@@ -54,9 +60,9 @@ __global__ __launch_bounds__(256) void router_logits_kernel(
         int64_t t = t0 + r;
         if (t >= T) t = T - 1;
         if constexpr (BF16)
-          rx[i] = *reinterpret_cast<const uint4 *>(static_cast<const uint16_t *>(xv) + t * d + k0 + c * XV);
+          rxs[i] = *reinterpret_cast<const uint4 *>(static_cast<const uint16_t *>(xv) + t * d + k0 + c * XV);
         else
-          rx[i] = *reinterpret_cast<const uint4 *>(static_cast<const float *>(xv) + t * d + k0 + c * XV);
+          rxs[i] = *reinterpret_cast<const uint4 *>(static_cast<const float *>(xv) + t * d + k0 + c * XV);
       }
     }
 #pragma unroll
@@ -66,28 +72,28 @@ __global__ __launch_bounds__(256) void router_logits_kernel(
         const int r = id / (KC / 4), c = id % (KC / 4);
         int e = e0 + r;
         if (e >= N) e = N - 1;
-        rw[i] = *reinterpret_cast<const float4 *>(w + static_cast<int64_t>(e) * d + k0 + c * 4);
+        rws[i] = *reinterpret_cast<const float4 *>(w + static_cast<int64_t>(e) * d + k0 + c * 4);
       }
     }
   };
-  auto lstore = [&](int buf) {
+  auto lstore_set = [&](int buf, const uint4 (&rxs)[XPT], const float4 (&rws)[WPT]) {
 #pragma unroll
     for (int i = 0; i < XPT; ++i) {
       const int id = tid + i * 256;
       if (id < X_LOADS) {
         const int r = id / (KC / XV), c = id % (KC / XV);
         if constexpr (BF16) {
-          const uint32_t q[4] = {rx[i].x, rx[i].y, rx[i].z, rx[i].w};
+          const uint32_t q[4] = {rxs[i].x, rxs[i].y, rxs[i].z, rxs[i].w};
 #pragma unroll
           for (int j = 0; j < 4; ++j) {
             s_x[buf][c * 8 + 2 * j][r] = __uint_as_float(q[j] << 16);
             s_x[buf][c * 8 + 2 * j + 1][r] = __uint_as_float(q[j] & 0xFFFF0000u);
           }
         } else {
-          s_x[buf][c * 4 + 0][r] = __uint_as_float(rx[i].x);
-          s_x[buf][c * 4 + 1][r] = __uint_as_float(rx[i].y);
-          s_x[buf][c * 4 + 2][r] = __uint_as_float(rx[i].z);
-          s_x[buf][c * 4 + 3][r] = __uint_as_float(rx[i].w);
+          s_x[buf][c * 4 + 0][r] = __uint_as_float(rxs[i].x);
+          s_x[buf][c * 4 + 1][r] = __uint_as_float(rxs[i].y);
+          s_x[buf][c * 4 + 2][r] = __uint_as_float(rxs[i].z);
+          s_x[buf][c * 4 + 3][r] = __uint_as_float(rxs[i].w);
         }
       }
     }
@@ -96,27 +102,17 @@ __global__ __launch_bounds__(256) void router_logits_kernel(
       const int id = tid + i * 256;
       if (id < W_LOADS) {
         const int r = id / (KC / 4), c = id % (KC / 4);
-        s_w[buf][c * 4 + 0][r] = rw[i].x;
-        s_w[buf][c * 4 + 1][r] = rw[i].y;
-        s_w[buf][c * 4 + 2][r] = rw[i].z;
-        s_w[buf][c * 4 + 3][r] = rw[i].w;
+        s_w[buf][c * 4 + 0][r] = rws[i].x;
+        s_w[buf][c * 4 + 1][r] = rws[i].y;
+        s_w[buf][c * 4 + 2][r] = rws[i].z;
+        s_w[buf][c * 4 + 3][r] = rws[i].w;
       }
     }
   };
 
-  float acc[MT][ME];
-#pragma unroll
-  for (int i = 0; i < MT; ++i)
-#pragma unroll
-    for (int j = 0; j < ME; ++j) acc[i][j] = 0.0f;
-
-  const int nchunks = d / KC;
-  gload(0);
-  lstore(0);
-  __syncthreads();
-  for (int ch = 0; ch < nchunks; ++ch) {
-    const int buf = ch & 1;
-    if (ch + 1 < nchunks) gload((ch + 1) * KC);
+  auto gload = [&](int k0) { gload_set(rx[0], rw[0], k0); };
+  auto lstore = [&](int buf) { lstore_set(buf, rx[0], rw[0]); };
+  auto compute = [&](int buf) {
 #pragma unroll
     for (int k = 0; k < KC; ++k) {
       float xs[MT], ws[ME];
@@ -129,8 +125,38 @@ __global__ __launch_bounds__(256) void router_logits_kernel(
 #pragma unroll
         for (int j = 0; j < ME; ++j) acc[i][j] = __builtin_fmaf(xs[i], ws[j], acc[i][j]);
     }
-    if (ch + 1 < nchunks) lstore(buf ^ 1);
+  };
+
+  const int nchunks = d / KC;
+  if constexpr (PF == 1) {
+    gload(0);
+    lstore(0);
     __syncthreads();
+    for (int ch = 0; ch < nchunks; ++ch) {
+      const int buf = ch & 1;
+      if (ch + 1 < nchunks) gload((ch + 1) * KC);
+      compute(buf);
+      if (ch + 1 < nchunks) lstore(buf ^ 1);
+      __syncthreads();
+    }
+  } else {
+    // loads run two chunks ahead in two register sets: chunk c+2 is loaded
+    // while chunk c is multiplied and stored to LDS at the end of chunk c+1
+    gload_set(rx[0], rw[0], 0);
+    if (nchunks > 1) gload_set(rx[1], rw[1], KC);
+    lstore_set(0, rx[0], rw[0]);
+    __syncthreads();
+    for (int ch = 0; ch < nchunks; ch += 2) {
+      if (ch + 2 < nchunks) gload_set(rx[0], rw[0], (ch + 2) * KC);
+      compute(0);
+      if (ch + 1 < nchunks) lstore_set(1, rx[1], rw[1]);
+      __syncthreads();
+      if (ch + 1 >= nchunks) break;
+      if (ch + 3 < nchunks) gload_set(rx[1], rw[1], (ch + 3) * KC);
+      compute(1);
+      if (ch + 2 < nchunks) lstore_set(0, rx[0], rw[0]);
+      __syncthreads();
+    }
   }
 #pragma unroll
   for (int i = 0; i < MT; ++i) {
@@ -327,20 +353,21 @@ hipError_t launch_router_logits(bool bf16, const void *x, const float *w, const 
   if (T <= 0) return hipSuccess;
   // Shapes measured on MI355X: few logits in all (a decode batch, a narrow
   // router) go to the LDS-ring kernel, one logit per thread; otherwise wide
-  // routers over many tokens use 32x64 blocks with 2x4 logits per thread,
-  // mid-sized ones 32x32 with 2x2, and the rest 64x8 with 2x1.
+  // routers over many tokens use 64x32 blocks with 4x2 logits per thread,
+  // mid-sized ones 32x32 with 2x2 (both loading two chunks ahead), and the
+  // rest 64x8 with 2x1.
   const int64_t TN = T * static_cast<int64_t>(N);
   const int kc32 = d % 32 == 0;
-#define MOE_ROUTER_LAUNCH(BT, BE, MT, ME, KC)                                                   \
+#define MOE_ROUTER_LAUNCH(BT, BE, MT, ME, KC, PF)                                               \
   {                                                                                             \
     const dim3 grid(static_cast<unsigned>((T + BT - 1) / BT),                                   \
                     static_cast<unsigned>((N + BE - 1) / BE));                                  \
     if (bf16)                                                                                   \
-      hipLaunchKernelGGL((router_logits_kernel<BT, BE, MT, ME, KC, true>), grid, dim3(256), 0, \
-                         s, x, w, bias, logits, T, d, N);                                       \
+      hipLaunchKernelGGL((router_logits_kernel<BT, BE, MT, ME, KC, true, PF>), grid, dim3(256),\
+                         0, s, x, w, bias, logits, T, d, N);                                    \
     else                                                                                        \
-      hipLaunchKernelGGL((router_logits_kernel<BT, BE, MT, ME, KC, false>), grid, dim3(256), 0,\
-                         s, x, w, bias, logits, T, d, N);                                       \
+      hipLaunchKernelGGL((router_logits_kernel<BT, BE, MT, ME, KC, false, PF>), grid,          \
+                         dim3(256), 0, s, x, w, bias, logits, T, d, N);                         \
   }
   if (bf16 && d % 64 == 0 && TN < (int64_t(1) << 17)) {
     const dim3 grid(static_cast<unsigned>((T + ring::BT - 1) / ring::BT),
@@ -350,11 +377,11 @@ hipError_t launch_router_logits(bool bf16, const void *x, const float *w, const 
     return hipGetLastError();
   }
   if (N >= 64 && TN >= (int64_t(1) << 19)) {
-    if (kc32) MOE_ROUTER_LAUNCH(32, 64, 2, 4, 32) else MOE_ROUTER_LAUNCH(32, 64, 2, 4, 16)
+    if (kc32) MOE_ROUTER_LAUNCH(64, 32, 4, 2, 32, 2) else MOE_ROUTER_LAUNCH(64, 32, 4, 2, 16, 2)
   } else if (N >= 32 && TN >= (int64_t(1) << 17)) {
-    if (kc32) MOE_ROUTER_LAUNCH(32, 32, 2, 2, 32) else MOE_ROUTER_LAUNCH(32, 32, 2, 2, 16)
+    if (kc32) MOE_ROUTER_LAUNCH(32, 32, 2, 2, 32, 2) else MOE_ROUTER_LAUNCH(32, 32, 2, 2, 16, 2)
   } else {
-    if (kc32) MOE_ROUTER_LAUNCH(64, 8, 2, 1, 32) else MOE_ROUTER_LAUNCH(64, 8, 2, 1, 16)
+    if (kc32) MOE_ROUTER_LAUNCH(64, 8, 2, 1, 32, 1) else MOE_ROUTER_LAUNCH(64, 8, 2, 1, 16, 1)
   }
 #undef MOE_ROUTER_LAUNCH
   return hipGetLastError();
