@@ -250,30 +250,46 @@ __global__ __launch_bounds__(128) void router_logits_ring_kernel(
 
   const int nch = d / KC;
   float acc = 0.0f;
-  const int pro = min(S - 1, nch);
-  for (int c = 0; c < pro; ++c) issue(c, c % S);
-  for (int c = 0; c < nch; ++c) {
-    const int later = min(S - 2, nch - 1 - c);
-    if (later == S - 2) wait_and_barrier<(S - 2) * LPS>();
-    else wait_chunks<LPS, S - 3>(later);
-    if (c + S - 1 < nch) issue(c + S - 1, (c + S - 1) % S);
+  // a chunk's operands are read from LDS into registers before its chain of
+  // multiply-adds, so the LDS latency is paid once per chunk
+  uint4 xa[KC / 8];
+  float4 wa[KC / 4];
+  auto read = [&](int c, uint4 (&xq)[KC / 8], float4 (&wv)[KC / 4]) {
     const uint8_t *st = s_ring + (c % S) * STAGE;
     const uint16_t *xs = reinterpret_cast<const uint16_t *>(st) + tt * KC;
     const float *ws = reinterpret_cast<const float *>(st + XB) + te * KC;
 #pragma unroll
     for (int pc = 0; pc < KC / 8; ++pc) {
-      const uint4 xq = *reinterpret_cast<const uint4 *>(xs + ((pc ^ ((tt >> 1) & 7)) << 3));
-      const float4 wa = *reinterpret_cast<const float4 *>(ws + pc * 8);
-      const float4 wb = *reinterpret_cast<const float4 *>(ws + pc * 8 + 4);
-      acc = __builtin_fmaf(__uint_as_float(xq.x << 16), wa.x, acc);
-      acc = __builtin_fmaf(__uint_as_float(xq.x & 0xFFFF0000u), wa.y, acc);
-      acc = __builtin_fmaf(__uint_as_float(xq.y << 16), wa.z, acc);
-      acc = __builtin_fmaf(__uint_as_float(xq.y & 0xFFFF0000u), wa.w, acc);
-      acc = __builtin_fmaf(__uint_as_float(xq.z << 16), wb.x, acc);
-      acc = __builtin_fmaf(__uint_as_float(xq.z & 0xFFFF0000u), wb.y, acc);
-      acc = __builtin_fmaf(__uint_as_float(xq.w << 16), wb.z, acc);
-      acc = __builtin_fmaf(__uint_as_float(xq.w & 0xFFFF0000u), wb.w, acc);
+      xq[pc] = *reinterpret_cast<const uint4 *>(xs + ((pc ^ ((tt >> 1) & 7)) << 3));
+      wv[2 * pc] = *reinterpret_cast<const float4 *>(ws + pc * 8);
+      wv[2 * pc + 1] = *reinterpret_cast<const float4 *>(ws + pc * 8 + 4);
     }
+  };
+  auto chain = [&](const uint4 (&xq)[KC / 8], const float4 (&wv)[KC / 4]) {
+#pragma unroll
+    for (int pc = 0; pc < KC / 8; ++pc) {
+      const uint4 q = xq[pc];
+      const float4 u = wv[2 * pc], v = wv[2 * pc + 1];
+      acc = __builtin_fmaf(__uint_as_float(q.x << 16), u.x, acc);
+      acc = __builtin_fmaf(__uint_as_float(q.x & 0xFFFF0000u), u.y, acc);
+      acc = __builtin_fmaf(__uint_as_float(q.y << 16), u.z, acc);
+      acc = __builtin_fmaf(__uint_as_float(q.y & 0xFFFF0000u), u.w, acc);
+      acc = __builtin_fmaf(__uint_as_float(q.z << 16), v.x, acc);
+      acc = __builtin_fmaf(__uint_as_float(q.z & 0xFFFF0000u), v.y, acc);
+      acc = __builtin_fmaf(__uint_as_float(q.w << 16), v.z, acc);
+      acc = __builtin_fmaf(__uint_as_float(q.w & 0xFFFF0000u), v.w, acc);
+    }
+  };
+  const int pro = min(S - 1, nch);
+  for (int c = 0; c < pro; ++c) issue(c, c % S);
+  for (int c = 0; c < nch; ++c) {
+    // copies of chunks c+1 .. min(c+S-2, nch-1) may stay in flight
+    const int later = min(S - 2, nch - 1 - c);
+    if (later == S - 2) wait_and_barrier<(S - 2) * LPS>();
+    else wait_chunks<LPS, S - 3>(later);
+    if (c + S - 1 < nch) issue(c + S - 1, (c + S - 1) % S);
+    read(c, xa, wa);
+    chain(xa, wa);
   }
   const int64_t t = t0 + tt;
   const int e = e0 + te;
