@@ -13,6 +13,15 @@
 namespace moe {
 namespace {
 
+typedef uint32_t nt4_t __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ uint4 load_nt(const uint4 *p) {
+  const nt4_t v = __builtin_nontemporal_load(reinterpret_cast<const nt4_t *>(p));
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+__device__ __forceinline__ void store_nt(uint4 *p, uint4 q) {
+  __builtin_nontemporal_store((nt4_t){q.x, q.y, q.z, q.w}, reinterpret_cast<nt4_t *>(p));
+}
+
 template <bool BF16>
 struct Chunk;   // 16 bytes of activations
 
@@ -86,13 +95,15 @@ __global__ __launch_bounds__(256) void combine_kernel(const uint4 *__restrict__ 
     float acc[C::kElems];
 #pragma unroll
     for (int j = 0; j < C::kElems; ++j) acc[j] = 0.0f;
+    // every input row is read once and the output is not read again here:
+    // non-temporal loads and stores keep them from displacing cached data
     for (int sh = 0; sh < n_shared; ++sh)
-      C::add1(acc, shared_out[(static_cast<int64_t>(sh) * T + t) * nvec + i]);
+      C::add1(acc, load_nt(&shared_out[(static_cast<int64_t>(sh) * T + t) * nvec + i]));
     for (int k = 0; k < K; ++k) {
       const int32_t r = s_row[k];
-      if (r >= 0) C::add(acc, y_rows[static_cast<int64_t>(r) * nvec + i], s_gate[k]);
+      if (r >= 0) C::add(acc, load_nt(&y_rows[static_cast<int64_t>(r) * nvec + i]), s_gate[k]);
     }
-    y[t * nvec + i] = C::pack(acc);
+    store_nt(&y[t * nvec + i], C::pack(acc));
   }
 }
 
