@@ -454,7 +454,7 @@ __device__ __forceinline__ void rs_epilogue(const f32x16_t (&acc)[rs::TN][rs::TM
       const int n = n0 + c * 8;
       if (row < v.rows && n < a.Nout) {
         const u32x4_t val = *reinterpret_cast<const u32x4_t *>(s_tile + r * BN + ((c ^ (r & 31)) << 3));
-        *reinterpret_cast<u32x4_t *>(v.C + (v.out_base + row) * a.Nout + n) = val;
+        store_nt(v.C + (v.out_base + row) * a.Nout + n, val);
       }
     }
     rs::lds_barrier();
@@ -745,7 +745,7 @@ __device__ __forceinline__ void rh_epilogue(const f32x16_t (&acc)[rh::TN][rh::TM
     const int n = n0 + c * 8;
     if (row < v.rows && n < a.Nout) {
       const u32x4_t val = *reinterpret_cast<const u32x4_t *>(s_tile + r * BN + ((c ^ (r & 31)) << 3));
-      *reinterpret_cast<u32x4_t *>(v.C + (v.out_base + row) * a.Nout + n) = val;
+      store_nt(v.C + (v.out_base + row) * a.Nout + n, val);
     }
   }
   __syncthreads();

@@ -41,6 +41,17 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2_t){lo, hi}, bf16x2_hw_t));
 }
 
+// 16-byte store of a layer output that the kernel does not read back, with
+// the non-temporal policy so that it does not displace operand data in the
+// caches.  (Measured: this helps full-line tile stores; partial-line 8-byte
+// stores lose their write combining and get slower.)
+typedef uint32_t u32x4_nt_t __attribute__((ext_vector_type(4)));
+template <typename V>
+__device__ __forceinline__ void store_nt(uint16_t *p, V v) {
+  static_assert(sizeof(V) == 16, "16-byte vectors");
+  __builtin_nontemporal_store(__builtin_bit_cast(u32x4_nt_t, v), reinterpret_cast<u32x4_nt_t *>(p));
+}
+
 __device__ __forceinline__ float silu(float z) { return z / (1.0f + __expf(-z)); }
 
 // SiLU with the hardware exp2 and reciprocal (about 1 ulp each in float32),
