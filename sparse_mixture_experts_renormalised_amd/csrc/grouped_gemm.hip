@@ -1483,11 +1483,11 @@ hipError_t launch_grouped_gemm(bool bf16, const GemmGroups &g, Epilogue epi, hip
       if (max_rows <= 32) return launch_bf16_stream<1, 1, 6>(a, g, epi, 1, s);
       return launch_bf16_stream<2, 2, 3, 4>(a, g, epi, 1, s);
     }
-    if (!any_small) return launch_bf16_rs<8>(a, g, epi, s);
+    if (!any_small) return launch_bf16_rs<4>(a, g, epi, s);
     GemmArgs ab = a, as = a;
     ab.cls_lo = kStreamRows + 1;
     as.cls_hi = kStreamRows;
-    hipError_t e = launch_bf16_rs<8>(ab, g, epi, s);
+    hipError_t e = launch_bf16_rs<4>(ab, g, epi, s);
     if (e != hipSuccess) return e;
     return launch_bf16_stream<2, 2, 3, 4>(as, g, epi, 1, s);
   }
