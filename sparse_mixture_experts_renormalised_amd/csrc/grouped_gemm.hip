@@ -643,22 +643,23 @@ __device__ __forceinline__ void rs_tile(const GemmArgs &a, const TileView<uint16
   rs::lds_barrier();
 }
 
-// Accumulators of one 128 x 256 tile (the half-height tail of a group).
+// Accumulators of one 128 x 256 tile (the half-height tail of a group) over
+// K-steps k0 .. k0+nk-1.
 __device__ __forceinline__ void rh_tile(const GemmArgs &a, const TileView<uint16_t> &v, int n0,
-                                        int nk, uint16_t *s_tile, int tid, int lane, int wm,
-                                        int wn, f32x16_t (&acc)[rh::TN][rh::TM]) {
+                                        int k0, int nk, uint16_t *s_tile, int tid, int lane,
+                                        int wm, int wn, f32x16_t (&acc)[rh::TN][rh::TM]) {
   using namespace rh;
   const int kc = tid & 7;
   const uint16_t *a_src[A_CH];
   const uint16_t *b_src[B_CH];
 #pragma unroll
   for (int i = 0; i < A_CH; ++i)
-    a_src[i] = a_row_ptr(a, v, v.row0 + (tid >> 3) + i * (NT / 8)) + kc * 8;
+    a_src[i] = a_row_ptr(a, v, v.row0 + (tid >> 3) + i * (NT / 8)) + kc * 8 + k0 * BK;
 #pragma unroll
   for (int i = 0; i < B_CH; ++i) {
     int n = n0 + (tid >> 3) + i * (NT / 8);
     if (n >= a.Nout) n = a.Nout - 1;
-    b_src[i] = v.W + static_cast<int64_t>(n) * a.K + kc * 8;
+    b_src[i] = v.W + static_cast<int64_t>(n) * a.K + kc * 8 + k0 * BK;
   }
 #pragma unroll
   for (int i = 0; i < TN; ++i)
@@ -782,17 +783,32 @@ void grouped_gemm_bf16_rs_kernel(GemmArgs a, RsSplit sp) {
     rs_tile_at<GM>(a, t, s_pref_f, s_pref_h, pl.full + slot / pl.P, &g, &lm, &nt);
     const TileView<uint16_t> v = tile_view<uint16_t>(a, g, lm, BM);
     const int k0 = (slot % pl.P) * pl.kper;
-    rs_tile(a, v, nt * BN, k0, min(nk, k0 + pl.kper) - k0, s_tile, tid, lane, wm, wn, acc);
+    const int kn = min(nk, k0 + pl.kper) - k0;
     float4 *dst = reinterpret_cast<float4 *>(sp.partial + static_cast<int64_t>(blockIdx.x) * (BM * BN));
+    if (pl.full + slot / pl.P >= t.cnt_f) {   // a half-height tail: its own register layout
+      f32x16_t acch[rh::TN][rh::TM];
+      rh_tile(a, v, nt * BN, k0, kn, s_tile, tid, lane, wm, wn, acch);
 #pragma unroll
-    for (int i = 0; i < TN; ++i)
+      for (int i = 0; i < rh::TN; ++i)
 #pragma unroll
-      for (int j = 0; j < TM; ++j)
+        for (int j = 0; j < rh::TM; ++j)
 #pragma unroll
-        for (int q = 0; q < 4; ++q)
-          dst[((i * TM + j) * 4 + q) * NT + tid] =
-              make_float4(acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2],
-                          acc[i][j][4 * q + 3]);
+          for (int q = 0; q < 4; ++q)
+            dst[((i * rh::TM + j) * 4 + q) * NT + tid] =
+                make_float4(acch[i][j][4 * q], acch[i][j][4 * q + 1], acch[i][j][4 * q + 2],
+                            acch[i][j][4 * q + 3]);
+    } else {
+      rs_tile(a, v, nt * BN, k0, kn, s_tile, tid, lane, wm, wn, acc);
+#pragma unroll
+      for (int i = 0; i < TN; ++i)
+#pragma unroll
+        for (int j = 0; j < TM; ++j)
+#pragma unroll
+          for (int q = 0; q < 4; ++q)
+            dst[((i * TM + j) * 4 + q) * NT + tid] =
+                make_float4(acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2],
+                            acc[i][j][4 * q + 3]);
+    }
   } else {
     const int end = pl.P > 1 ? pl.full : t.cnt_f + t.cnt_h;
     const int end_f = min(end, t.cnt_f);
@@ -808,7 +824,7 @@ void grouped_gemm_bf16_rs_kernel(GemmArgs a, RsSplit sp) {
       rs_tile_at<GM>(a, t, s_pref_f, s_pref_h, i, &g, &lm, &nt);
       const TileView<uint16_t> v = tile_view<uint16_t>(a, g, lm, BM);
       f32x16_t acch[rh::TN][rh::TM];
-      rh_tile(a, v, nt * BN, nk, s_tile, tid, lane, wm, wn, acch);
+      rh_tile(a, v, nt * BN, 0, nk, s_tile, tid, lane, wm, wn, acch);
       rh_epilogue<EPI>(acch, a, v, nt * BN, s_tile, lane, wm, wn, tid);
     }
   }
@@ -841,16 +857,22 @@ __global__ __launch_bounds__(256) void rs_fixup_kernel(GemmArgs a, RsSplit sp, i
   const TileView<uint16_t> v = tile_view<uint16_t>(a, g, lm, BM);
   const int n0 = nt * BN;
   const int64_t blk0 = static_cast<int64_t>(t * pl.P) * kXcds + xcd;   // piece 0's workgroup
-  // all 16 chunks of one piece are loaded together, pieces are added in order
+  // a half-height tail holds 32 register chunks per thread (rh layout), a
+  // full tile 64; this workgroup takes a quarter of them
+  const bool half = pl.full + t >= tl.cnt_f;
+  const int per = half ? 8 : 16;
+  // all chunks of one piece are loaded together, pieces are added in order
   float4 acc[16];
   for (int pc = 0; pc < pl.P; ++pc) {
     const float4 *src = reinterpret_cast<const float4 *>(
         sp.partial + (blk0 + static_cast<int64_t>(pc) * kXcds) * (BM * BN));
     float4 p[16];
 #pragma unroll
-    for (int cc = 0; cc < 16; ++cc) p[cc] = src[(quarter * 16 + cc) * NT + tid];
+    for (int cc = 0; cc < 16; ++cc)
+      if (cc < per) p[cc] = src[(quarter * per + cc) * NT + tid];
 #pragma unroll
     for (int cc = 0; cc < 16; ++cc) {
+      if (cc >= per) continue;
       if (pc == 0) {
         acc[cc] = p[cc];
       } else {
@@ -863,9 +885,17 @@ __global__ __launch_bounds__(256) void rs_fixup_kernel(GemmArgs a, RsSplit sp, i
   }
 #pragma unroll
   for (int cc = 0; cc < 16; ++cc) {
-    const int c = quarter * 16 + cc;          // (ni * TM + mi) * 4 + q
-    const int ni = c >> 4, mi = (c >> 2) & 3, q = c & 3;
-    const int64_t row = v.row0 + wm * WTM + mi * 32 + (lane & 31);
+    if (cc >= per) continue;
+    const int c = quarter * per + cc;         // (ni * tm + mi) * 4 + q
+    int ni, mi, q;
+    int64_t row;
+    if (half) {
+      ni = c >> 3, mi = (c >> 2) & 1, q = c & 3;
+      row = v.row0 + wm * rh::WTM + mi * 32 + (lane & 31);
+    } else {
+      ni = c >> 4, mi = (c >> 2) & 3, q = c & 3;
+      row = v.row0 + wm * WTM + mi * 32 + (lane & 31);
+    }
     const int n = n0 + wn * WTN + ni * 32 + q * 8 + (lane >> 5) * 4;
     if (row >= v.rows || n >= a.Nout) continue;
     float o[4] = {acc[cc].x, acc[cc].y, acc[cc].z, acc[cc].w};
