@@ -810,7 +810,13 @@ void grouped_gemm_bf16_rs_kernel(GemmArgs a, RsSplit sp) {
                             acc[i][j][4 * q + 3]);
     }
   } else {
-    const int end = pl.P > 1 ? pl.full : t.cnt_f + t.cnt_h;
+    // A last, partly filled round that is not split along K (too few K-steps)
+    // is split along M instead when it fits: each full-cost tile of that
+    // round becomes two half-height tiles on two workgroups.
+    const int cnt = t.cnt_f + t.cnt_h;
+    const int rem_f = max(0, t.cnt_f - pl.full);
+    const bool msplit = pl.P <= 1 && pl.rem > 0 && 2 * rem_f + (pl.rem - rem_f) <= nslots;
+    const int end = pl.P > 1 || msplit ? pl.full : cnt;
     const int end_f = min(end, t.cnt_f);
     int g, lm, nt;
     int i = slot;
@@ -823,6 +829,22 @@ void grouped_gemm_bf16_rs_kernel(GemmArgs a, RsSplit sp) {
     for (; i < end; i += nslots) {         // half-height tail tiles
       rs_tile_at<GM>(a, t, s_pref_f, s_pref_h, i, &g, &lm, &nt);
       const TileView<uint16_t> v = tile_view<uint16_t>(a, g, lm, BM);
+      f32x16_t acch[rh::TN][rh::TM];
+      rh_tile(a, v, nt * BN, 0, nk, s_tile, tid, lane, wm, wn, acch);
+      rh_epilogue<EPI>(acch, a, v, nt * BN, s_tile, lane, wm, wn, tid);
+    }
+    if (msplit && slot < 2 * rem_f + (pl.rem - rem_f)) {
+      int item, upper = 0;
+      if (slot < 2 * rem_f) {
+        item = pl.full + slot / 2;
+        upper = slot & 1;
+      } else {
+        item = pl.full + rem_f + (slot - 2 * rem_f);
+      }
+      rs_tile_at<GM>(a, t, s_pref_f, s_pref_h, item, &g, &lm, &nt);
+      // rows 128*(2*lm + upper) .. +127 of the group: the upper or lower half
+      // of a full-cost tile, or a tail tile (upper = 0)
+      const TileView<uint16_t> v = tile_view<uint16_t>(a, g, 2 * lm + upper, rh::BM);
       f32x16_t acch[rh::TN][rh::TM];
       rh_tile(a, v, nt * BN, 0, nk, s_tile, tid, lane, wm, wn, acch);
       rh_epilogue<EPI>(acch, a, v, nt * BN, s_tile, lane, wm, wn, tid);

@@ -316,6 +316,9 @@ FFN_CASES = [
     # in 2 pieces, then the second in 4
     ("bf16_ksplit_up", [700, 300, 520], 4096, 2048, "bf16", True, 8192),
     ("bf16_ksplit_down", [700, 300, 520], 1024, 8192, "bf16", True, 8192),
+    # the same partial rounds with too few K-steps to split along K: their
+    # full-cost tiles are split along M into half-height tiles instead
+    ("bf16_msplit", [700, 300, 520], 512, 1024, "bf16", True, 8192),
 ]
 
 
