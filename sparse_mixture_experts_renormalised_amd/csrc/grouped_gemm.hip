@@ -206,12 +206,46 @@ __device__ __forceinline__ void decode_tile(int L, int total_m, int n_nt, int *m
 }
 
 // ---------------------------------------------------------------------------
-// bf16 MFMA kernel, register-staged pipeline: 256x256 tiles, four 128x128
-// wave tiles, one LDS buffer of one 64-wide K-step.  Global loads run two
-// K-steps ahead into registers; each step's fragments (all four 16-wide
-// slices) are read from LDS into registers once, so the MFMAs of step kb
-// overlap the LDS writes and global loads of the following steps and the
-// fragment reads of step kb+1.
+// Global-to-LDS copies shared by the MFMA kernels.
+// ---------------------------------------------------------------------------
+namespace dma {
+// LDS byte address of a __shared__ object (wave-uniform).
+__device__ __forceinline__ uint32_t lds_addr(const void *p) {
+  return static_cast<uint32_t>(
+      reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) const void *)p));
+}
+
+// One wave-wide LDS DMA (64 lanes x 16 B into the 1 KB block at LDS byte
+// address m0), written as inline assembly so the compiler does not drain
+// every load in flight before later LDS reads; the explicit waits cover it.
+// The s_nop separates the compiler's write of M0 from the copy that reads it.
+__device__ __forceinline__ void dma16(const uint16_t *src, uint32_t m0) {
+  asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, off" : : "v"(src), "{m0}"(m0) : "memory");
+}
+// The same copy with the non-temporal policy, for data read exactly once (a
+// weight block used by a single row block): streaming it past the caches
+// raises the sustained read rate from about 6.1 to 7.2 TB/s on MI355X.
+__device__ __forceinline__ void dma16_nt(const uint16_t *src, uint32_t m0) {
+  asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, off nt" : : "v"(src), "{m0}"(m0) : "memory");
+}
+
+// Wait until at most N of this wave's copies are in flight and its LDS reads
+// are done, then meet the other waves.
+template <int N>
+__device__ __forceinline__ void wait_and_barrier() {
+  asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)" ::"n"(N) : "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+}  // namespace dma
+
+// ---------------------------------------------------------------------------
+// bf16 MFMA kernel: 256x256 tiles, four 128x128 wave tiles, two LDS buffers
+// of one 64-wide K-step each, filled by global-to-LDS copies two K-steps
+// ahead.  Each step's fragments (all four 16-wide slices) are read from LDS
+// into registers once; the copies of step kb+2 are spread one per three
+// MFMAs over the first three slices of step kb, and the fragment reads of
+// step kb+1 over its last slice.
 // ---------------------------------------------------------------------------
 namespace rs {
 constexpr int BM = 256, BN = 256, BK = 64, NT = 256, WTM = 128, WTN = 128;
@@ -224,34 +258,10 @@ struct Frags {
   bf16x8_t b[NS][TN];
 };
 
-__device__ __forceinline__ void gload(u32x4_t (&ra)[A_CH], u32x4_t (&rb)[B_CH],
-                                      const uint16_t *const (&a_src)[A_CH],
-                                      const uint16_t *const (&b_src)[B_CH], int kb) {
-#pragma unroll
-  for (int i = 0; i < A_CH; ++i) ra[i] = *reinterpret_cast<const u32x4_t *>(a_src[i] + kb * BK);
-#pragma unroll
-  for (int i = 0; i < B_CH; ++i) rb[i] = *reinterpret_cast<const u32x4_t *>(b_src[i] + kb * BK);
-}
-
 // chunk kc of tile row r at chunk position kc ^ ((r / 2) % 8) of its 128-byte
 // row: with 64 four-byte banks serving 16 lanes of 16 bytes at a time, the
 // 16 rows read together (same logical chunk) then cover all banks once.
 __device__ __forceinline__ int swz(int r, int c) { return c ^ ((r >> 1) & 7); }
-
-__device__ __forceinline__ void lstore(uint16_t *tile, const u32x4_t (&ra)[A_CH],
-                                       const u32x4_t (&rb)[B_CH], int tid) {
-  const int kc = tid & 7;
-#pragma unroll
-  for (int i = 0; i < A_CH; ++i) {
-    const int row = (tid >> 3) + i * (NT / 8);
-    *reinterpret_cast<u32x4_t *>(tile + row * BK + (swz(row, kc) << 3)) = ra[i];
-  }
-#pragma unroll
-  for (int i = 0; i < B_CH; ++i) {
-    const int row = (tid >> 3) + i * (NT / 8);
-    *reinterpret_cast<u32x4_t *>(tile + BM * BK + row * BK + (swz(row, kc) << 3)) = rb[i];
-  }
-}
 
 __device__ __forceinline__ void read_frags(const uint16_t *tile, Frags &f, int wm, int wn,
                                            int lane) {
@@ -283,17 +293,20 @@ __device__ __forceinline__ void mfma_all(const Frags &f, f32x16_t (&acc)[TN][TM]
                                                               0, 0, 0);
 }
 
-// Instruction order of one steady-state step (64 MFMAs): each global load
-// and LDS write shares a slot with three MFMAs, then two fragment reads
-// precede each of the last sixteen MFMAs.
-__device__ __forceinline__ void schedule_step() {
+// MFMAs number M0 .. M1-1 of a step, in mfma_all's (slice, ni, mi) order.
+template <int M0, int M1>
+__device__ __forceinline__ void mfma_range(const Frags &f, f32x16_t (&acc)[TN][TM]) {
 #pragma unroll
-  for (int i = 0; i < A_CH + B_CH; ++i) {
-    __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);   // DS write
-    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA
-    __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);   // VMEM read
-    __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);   // MFMA
+  for (int m = M0; m < M1; ++m) {
+    const int ks = m / (TN * TM), ni = (m / TM) % TN, mi = m % TM;
+    acc[ni][mi] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.b[ks][ni], f.a[ks][mi], acc[ni][mi],
+                                                          0, 0, 0);
   }
+}
+
+// Instruction order of a step's last slice: two fragment reads of the next
+// step before each of its sixteen MFMAs.
+__device__ __forceinline__ void schedule_last_slice() {
 #pragma unroll
   for (int i = 0; i < NS * (TM + TN) / 2; ++i) {
     __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);   // DS read
@@ -556,77 +569,103 @@ __device__ __forceinline__ void rs_tile_at(const GemmArgs &a, const RsTiles &t,
 }
 
 // Source addresses of this thread's 16-byte chunks of a 256x256 tile, from
-// K-step k0 on.
+// K-step k0 on.  Copy i of wave w fills rows 8*(4i+w) .. +7 of the 512-row
+// tile (A rows, then B rows) at LDS bytes (4i+w)*1024 .. +1023: lane l writes
+// row 8*(4i+w) + l/8 at 16-byte position l%8, so it fetches the chunk that
+// the swizzle puts there, c = (l%8) ^ ((row/2)%8).
 struct RsSrc {
   const uint16_t *a[rs::A_CH];
   const uint16_t *b[rs::B_CH];
 };
 
-// The first K-step of a tile in registers: issued before the previous
-// tile's epilogue, so its latency overlaps that epilogue.
-struct RsHead {
-  u32x4_t ra0[rs::A_CH], rb0[rs::B_CH];
-};
-
 __device__ __forceinline__ void rs_src(const GemmArgs &a, const TileView<uint16_t> &v, int n0,
                                        int k0, int tid, RsSrc &src) {
   using namespace rs;
-  const int kc = tid & 7;
+  const int c = (tid & 7) ^ ((tid >> 4) & 7);   // row = tid/8 + 32i, so (row/2)%8 = (tid/16)%8
 #pragma unroll
   for (int i = 0; i < A_CH; ++i)
-    src.a[i] = a_row_ptr(a, v, v.row0 + (tid >> 3) + i * (NT / 8)) + kc * 8 + k0 * BK;
+    src.a[i] = a_row_ptr(a, v, v.row0 + (tid >> 3) + i * (NT / 8)) + c * 8 + k0 * BK;
 #pragma unroll
   for (int i = 0; i < B_CH; ++i) {
     int n = n0 + (tid >> 3) + i * (NT / 8);
     if (n >= a.Nout) n = a.Nout - 1;
-    src.b[i] = v.W + static_cast<int64_t>(n) * a.K + kc * 8 + k0 * BK;
+    src.b[i] = v.W + static_cast<int64_t>(n) * a.K + c * 8 + k0 * BK;
   }
 }
 
-__device__ __forceinline__ void rs_head(const RsSrc &src, RsHead &h) {
-  rs::gload(h.ra0, h.rb0, src.a, src.b, 0);
+// Copy I of K-step kb into the tile buffer at LDS byte address base.
+__device__ __forceinline__ void rs_copy(const RsSrc &src, int i, int kb, uint32_t base,
+                                        int wave) {
+  using namespace rs;
+  if (i < A_CH)
+    dma::dma16(src.a[i] + kb * BK, base + (4 * i + wave) * 1024);
+  else
+    dma::dma16(src.b[i - A_CH] + kb * BK, base + (4 * i + wave) * 1024);
 }
 
-// Accumulators of one 256x256 tile over the nk K-steps that src points at,
-// the first of them already in h.  Returns once the last step's MFMAs
-// are issued; the caller passes an LDS barrier before reusing the tile
-// buffer.
-__device__ __forceinline__ void rs_body(const RsSrc &src, int nk, const RsHead &h,
-                                        uint16_t *s_tile, int tid, int lane, int wm, int wn,
+// Copies I.. of step kb, one before each group of three MFMAs of the first
+// three slices (48 MFMAs for 16 copies); each group is its own scheduling
+// region so the copies stay spread out.
+template <int I>
+__device__ __forceinline__ void rs_copies_mfmas(const RsSrc &src, int kb, uint32_t base,
+                                                int wave, const rs::Frags &f,
+                                                f32x16_t (&acc)[rs::TN][rs::TM]) {
+  if constexpr (I < rs::A_CH + rs::B_CH) {
+    rs_copy(src, I, kb, base, wave);
+    rs::mfma_range<3 * I, 3 * I + 3>(f, acc);
+    __builtin_amdgcn_sched_barrier(0);
+    rs_copies_mfmas<I + 1>(src, kb, base, wave, f, acc);
+  }
+}
+
+// Accumulators of one 256x256 tile over the nk K-steps that src points at.
+// s_tile holds two tile buffers; step kb lives in buffer kb % 2.  Returns
+// once the last step's MFMAs are issued; the caller passes an LDS barrier
+// before reusing the buffers.
+__device__ __forceinline__ void rs_body(const RsSrc &src, int nk, uint16_t *s_tile, int tid,
+                                        int lane, int wm, int wn,
                                         f32x16_t (&acc)[rs::TN][rs::TM]) {
   using namespace rs;
+  constexpr int NCP = A_CH + B_CH;   // copies per wave per step
+  const int wave = uniform(tid >> 6);
 #pragma unroll
   for (int i = 0; i < TN; ++i)
 #pragma unroll
     for (int j = 0; j < TM; ++j)
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
-
-  u32x4_t ra[A_CH], rb[B_CH];
+  const uint32_t b0 = uniform(static_cast<int>(dma::lds_addr(s_tile)));
+  const uint32_t b1 = b0 + TILE * 2;
   Frags f;
-  lstore(s_tile, h.ra0, h.rb0, tid);
-  if (nk > 1) gload(ra, rb, src.a, src.b, 1);
-  lds_barrier();
+#pragma unroll
+  for (int i = 0; i < NCP; ++i) rs_copy(src, i, 0, b0, wave);
+  if (nk > 1) {
+#pragma unroll
+    for (int i = 0; i < NCP; ++i) rs_copy(src, i, 1, b1, wave);
+    dma::wait_and_barrier<NCP>();           // step 0 landed for every wave
+  } else {
+    dma::wait_and_barrier<0>();
+  }
   read_frags(s_tile, f, wm, wn, lane);
   __builtin_amdgcn_sched_barrier(0);
   // steady state (no branches, so each step is one scheduling region)
   int kb = 0;
   for (; kb + 2 < nk; ++kb) {
+    const int cur = kb & 1;
     lds_barrier();                          // every wave has its fragments of step kb
-    lstore(s_tile, ra, rb, tid);            // step kb+1 into LDS
-    gload(ra, rb, src.a, src.b, kb + 2);    // step kb+2 into registers
-    mfma_all(f, acc);                       // step kb
-    lds_barrier();                          // step kb+1 is in LDS
-    read_frags(s_tile, f, wm, wn, lane);
-    schedule_step();
+    __builtin_amdgcn_sched_barrier(0);
+    rs_copies_mfmas<0>(src, kb + 2, cur ? b1 : b0, wave, f, acc);   // step kb+2 into buffer cur
+    dma::wait_and_barrier<NCP>();           // step kb+1 landed for every wave
+    mfma_range<48, 64>(f, acc);             // last slice of step kb
+    read_frags(s_tile + (cur ? 0 : TILE), f, wm, wn, lane);          // step kb+1
+    schedule_last_slice();
     __builtin_amdgcn_sched_barrier(0);
   }
-  if (kb + 1 < nk) {                        // step nk-2: nothing left to load
-    lds_barrier();
-    lstore(s_tile, ra, rb, tid);
+  if (kb + 1 < nk) {                        // step nk-2: nothing left to copy
+    const int cur = kb & 1;
     mfma_all(f, acc);
-    lds_barrier();
-    read_frags(s_tile, f, wm, wn, lane);
+    dma::wait_and_barrier<0>();
+    read_frags(s_tile + (cur ? 0 : TILE), f, wm, wn, lane);
   }
   mfma_all(f, acc);                         // last step
 }
@@ -636,10 +675,8 @@ __device__ __forceinline__ void rs_tile(const GemmArgs &a, const TileView<uint16
                                         int k0, int nk, uint16_t *s_tile, int tid, int lane,
                                         int wm, int wn, f32x16_t (&acc)[rs::TN][rs::TM]) {
   RsSrc src;
-  RsHead h;
   rs_src(a, v, n0, k0, tid, src);
-  rs_head(src, h);
-  rs_body(src, nk, h, s_tile, tid, lane, wm, wn, acc);
+  rs_body(src, nk, s_tile, tid, lane, wm, wn, acc);
   rs::lds_barrier();
 }
 
@@ -760,7 +797,7 @@ template <int EPI, int GM, bool PIECE>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void grouped_gemm_bf16_rs_kernel(GemmArgs a, RsSplit sp) {
   using namespace rs;
-  __shared__ __attribute__((aligned(16))) uint16_t s_tile[TILE];
+  __shared__ __attribute__((aligned(16))) uint16_t s_tile[2 * TILE];
   __shared__ int s_pref_f[kMaxGroups + 1];
   __shared__ int s_pref_h[kMaxGroups + 1];
   __shared__ int s_tmp[NT / 64];
@@ -969,35 +1006,10 @@ struct StreamSplit {
 
 namespace st {
 constexpr int NT = 256, NW = 4, KCH = 64;
-
-// LDS byte address of a __shared__ object (wave-uniform).
-__device__ __forceinline__ uint32_t lds_addr(const void *p) {
-  return static_cast<uint32_t>(
-      reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) const void *)p));
-}
-
-// One wave-wide LDS DMA (64 lanes x 16 B into the 1 KB block at LDS byte
-// address m0), written as inline assembly so the compiler does not drain
-// every load in flight before later LDS reads; the explicit waits cover it.
-// The s_nop separates the compiler's write of M0 from the copy that reads it.
-__device__ __forceinline__ void dma16(const uint16_t *src, uint32_t m0) {
-  asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, off" : : "v"(src), "{m0}"(m0) : "memory");
-}
-// The same copy with the non-temporal policy, for data read exactly once (a
-// weight block used by a single row block): streaming it past the caches
-// raises the sustained read rate from about 6.1 to 7.2 TB/s on MI355X.
-__device__ __forceinline__ void dma16_nt(const uint16_t *src, uint32_t m0) {
-  asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, off nt" : : "v"(src), "{m0}"(m0) : "memory");
-}
-
-// Wait until at most N of this wave's copies are in flight and its LDS reads
-// are done, then meet the other waves.
-template <int N>
-__device__ __forceinline__ void wait_and_barrier() {
-  asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)" ::"n"(N) : "memory");
-  __builtin_amdgcn_s_barrier();
-  asm volatile("" ::: "memory");
-}
+using dma::lds_addr;
+using dma::dma16;
+using dma::dma16_nt;
+using dma::wait_and_barrier;
 
 // wait_and_barrier<n * LPS> for a run-time n in [0, MAXN].
 template <int LPS, int MAXN>
