@@ -64,9 +64,17 @@ __global__ __launch_bounds__(1024) void dispatch_scan_kernel(
   __shared__ int32_t s_wave[16];
   for (int e = threadIdx.x; e < N; e += blockDim.x) {
     int32_t run = 0;
-    for (int64_t c = 0; c < n_chunks; ++c) {
-      base[c * N + e] = run;
-      run += hist[c * N + e];
+    // eight chunk counts are loaded before they are summed, so the loop waits
+    // for one memory latency per eight chunks rather than per chunk
+    for (int64_t c0 = 0; c0 < n_chunks; c0 += 8) {
+      int32_t hv[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) hv[j] = c0 + j < n_chunks ? hist[(c0 + j) * N + e] : 0;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        if (c0 + j < n_chunks) base[(c0 + j) * N + e] = run;
+        run += hv[j];
+      }
     }
     const int32_t kept = (capacity >= 0 && run > capacity) ? static_cast<int32_t>(capacity) : run;
     counts[e] = kept;
