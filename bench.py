@@ -28,7 +28,7 @@ PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
 PEAK_FP32_TFLOPS = 157.3       # MI355X fp32 vector
 PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
 DEFAULT_WORKLOAD = "mixtral_shape"
-CPU_SAMPLE = {"tiny_fp32": 64, "mixtral_shape": 1024, "deepseekmoe_fine": 512,
+CPU_SAMPLE = {"tiny_fp32": 64, "mixtral_shape": 4096, "deepseekmoe_fine": 512,
               "dsv3_prefill": 64, "dsv3_decode": 128}
 
 
