@@ -21,14 +21,16 @@
 // weight and activation tiles in that XCD's L2.
 //
 // Kernels, chosen by operand type and group size (rows per expert):
-//   * 256x256 tiles (groups above 256 rows): MFMA v_mfma_f32_32x32x16_bf16 with
-//     fp32 accumulators, operands staged global -> registers -> swizzled LDS
-//     one K-step ahead, a hand-interleaved schedule, and a K split of the last
+//   * 256x256 tiles (groups above 128 rows): MFMA v_mfma_f32_32x32x16_bf16
+//     with fp32 accumulators, operands copied global -> two swizzled LDS
+//     buffers two K-steps ahead with the copies spread among the MFMAs, tail
+//     tiles of 1..128 rows at half height, and a K (or M) split of the last
 //     partial round of tiles;
-//   * a stream kernel (groups of up to 256 rows, bound by the weight stream):
+//   * a stream kernel (groups of up to 128 rows, bound by the weight stream):
 //     weights and activations copied straight into a ring of LDS stages
-//     several chunks ahead, non-temporal for weights read once, and a K split
-//     when a product has too few units to fill the chip (decode);
+//     several chunks ahead, non-temporal for weights read once, units of one
+//     or two heights, and a K split when a product has too few units to fill
+//     the chip (decode);
 //   * fp32 operands: a plain LDS-tiled VALU kernel (4x4 register tile).
 // The weight tile is the MFMA's first operand, so each lane ends up holding
 // four consecutive output features of one row and the epilogues store packed
