@@ -6,9 +6,10 @@
 // optional per-expert bias that is part of the logit.
 //
 // Fixed float32 order: for every (t, e) one fused multiply-add chain over k
-// ascending from +0, then the bias with one rounding.  Each thread owns whole
-// logits, so no reduction tree is involved and the bits do not depend on the
-// launch shape.
+// ascending from +0, then the bias with one rounding.  Every kernel below
+// keeps each logit in one accumulator that sees its terms in that order (a
+// thread's register, or one output of a float32 matrix-core chain), so no
+// reduction tree is involved and the bits do not depend on the launch shape.
 //
 // Top-K: one wave per token, N logits spread over the lanes' registers, K
 // rounds of a wave-wide arg-max on the key (logit desc, expert id asc).  Gates
@@ -195,9 +196,16 @@ __device__ __forceinline__ void dma16(const void *src, uint32_t m0) {
   asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, off" : : "v"(src), "{m0}"(m0) : "memory");
 }
 
+// Leaves at most N copies in flight, drains the LDS queue and joins the
+// workgroup.  Written as the waitcnt builtin (encoding: vmcnt bits 3:0 and
+// 15:14, expcnt 6:4 = 7 for "no wait", lgkmcnt 11:8 = 0) so that the
+// compiler's own wait insertion knows every earlier LDS read has returned and
+// does not hold later multiplies on reads issued after this point.
 template <int N>
 __device__ __forceinline__ void wait_and_barrier() {
-  asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)" ::"n"(N) : "memory");
+  static_assert(N >= 0 && N <= 63, "vmcnt range");
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | ((N >> 4) << 14));
   __builtin_amdgcn_s_barrier();
   asm volatile("" ::: "memory");
 }
@@ -300,6 +308,194 @@ __global__ __launch_bounds__(128) void router_logits_ring_kernel(
   }
 }
 
+// Logits on the float32 matrix cores.  v_mfma_f32_16x16x4_f32 adds to each of
+// its 16 x 16 outputs the four products of one k-quad one at a time in
+// ascending k, each with one rounding: on MI355X its results equal, bit for
+// bit, four fused multiply-adds in that order (checked against a host fmaf
+// chain on normal, subnormal and signed-zero operands).  A chain of these
+// instructions over ascending k-quads is therefore the fixed order itself.
+//
+// Lane l of the instruction supplies A[l % 16][k0 + l / 16] (a token's x) and
+// B[k0 + l / 16][l % 16] (an expert's W row) and receives outputs
+// (4 * (l / 16) + r, l % 16), r = 0..3.  A workgroup of AT x AE waves covers
+// BT = 16 AT TT tokens x BE = 16 AE TE experts; each wave owns TT x TE tiles.
+// x (bf16, as stored) and W (float32) stream through an LDS ring of S stages
+// of 64 k each, filled by 1 KB global-to-LDS copies issued S-1 stages ahead:
+// a copy moves 8 token rows of 128 bytes or 4 expert rows of 256 bytes.  The
+// 16-byte piece p of row r sits at p ^ (r & 7), so the 16 rows that one
+// instruction's lanes read spread over the banks.
+namespace rmf {
+constexpr int KC = 64;
+constexpr int XROW = KC * 2;     // bytes of a token's stage row
+constexpr int WROW = KC * 4;     // bytes of an expert's stage row
+}  // namespace rmf
+
+// Scheduling pattern for one stage: each multiply followed by PER of the next
+// stage's LDS reads, so that the reads are in flight while the dependent
+// multiplies of a tile hold the wave's issue.
+template <int I, int NM, int NR, int PER>
+__device__ __forceinline__ void interleave_reads() {
+  if constexpr (I < NM) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);        // one MFMA
+    constexpr int r = NR - I * PER < PER ? NR - I * PER : PER;
+    if constexpr (r > 0) __builtin_amdgcn_sched_group_barrier(0x100, r, 0);   // LDS reads
+    interleave_reads<I + 1, NM, NR, PER>();
+  }
+}
+
+template <int AT, int AE, int TT, int TE, int S>
+__global__ __launch_bounds__(64 * AT * AE) void router_logits_mfma_kernel(
+    const uint16_t *__restrict__ x, const float *__restrict__ w, const float *__restrict__ bias,
+    float *__restrict__ logits, int64_t T, int d, int N) {
+  using namespace rmf;
+  typedef float f32x4 __attribute__((ext_vector_type(4)));
+  constexpr int NWAVE = AT * AE;
+  constexpr int BT = 16 * AT * TT, BE = 16 * AE * TE;
+  constexpr int XB = BT * XROW, WB = BE * WROW, STAGE = XB + WB;
+  constexpr int NX = XB / 1024, NW = WB / 1024;
+  constexpr int CPW = (NX + NW) / NWAVE;      // copies per wave per stage
+  static_assert(CPW * NWAVE == NX + NW, "copies split evenly over the waves");
+  static_assert((S - 2) * CPW <= 63, "vmcnt range");
+  static_assert(S >= 4, "one stage read ahead of the multiply, two in flight");
+  __shared__ __attribute__((aligned(16))) uint8_t s_ring[S * STAGE];
+
+  const int lane = threadIdx.x & 63;
+  const int wave = uniform(threadIdx.x >> 6);
+  const int64_t t0 = static_cast<int64_t>(blockIdx.x) * BT;
+  const int e0 = blockIdx.y * BE;
+  const uint32_t ring0 = uniform(static_cast<int>(ring::lds_addr(s_ring)));
+
+  // this wave's copies: source row pointers (lane's piece, swizzled), byte
+  // step per stage and LDS destination within a stage
+  const uint8_t *src[CPW];
+  int step[CPW], dst[CPW];
+#pragma unroll
+  for (int q = 0; q < CPW; ++q) {
+    const int c = wave * CPW + q;
+    if (c < NX) {
+      const int r = 8 * c + (lane >> 3);
+      const int64_t t = min(t0 + r, T - 1);
+      src[q] = reinterpret_cast<const uint8_t *>(x + t * d + (((lane & 7) ^ (r & 7)) << 3));
+      step[q] = XROW;
+      dst[q] = c * 1024;
+    } else {
+      const int r = 4 * (c - NX) + (lane >> 4);
+      const int e = min(e0 + r, N - 1);
+      src[q] = reinterpret_cast<const uint8_t *>(w + static_cast<int64_t>(e) * d + (((lane & 15) ^ (r & 7)) << 2));
+      step[q] = WROW;
+      dst[q] = XB + (c - NX) * 1024;
+    }
+  }
+  auto issue = [&](int ch, int slot) {
+    const uint32_t base = ring0 + static_cast<uint32_t>(slot * STAGE);
+#pragma unroll
+    for (int q = 0; q < CPW; ++q)
+      ring::dma16(src[q] + static_cast<int64_t>(ch) * step[q], base + dst[q]);
+  };
+
+  // fragment addresses: lane reads row i of each tile at k = 4j + g of the stage
+  const int i = lane & 15, g = lane >> 4, i7 = i & 7;
+  const int wt = wave % AT, we = wave / AT;
+  const int xrow = wt * TT * 16 + i, wrow = we * TE * 16 + i;
+  int xo[8], wo[8];
+#pragma unroll
+  for (int q = 0; q < 8; ++q) {
+    xo[q] = xrow * XROW + ((q ^ i7) << 4) + 2 * g;
+    wo[q] = XB + wrow * WROW + ((q ^ i7) << 4) + 4 * g;
+  }
+
+  f32x4 acc[TT][TE];
+#pragma unroll
+  for (int a = 0; a < TT; ++a)
+#pragma unroll
+    for (int b = 0; b < TE; ++b) acc[a][b] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+
+  // a stage's fragments are read into registers one stage ahead, while the
+  // matrix cores work through the previous stage; x stays as its 16 raw bits
+  // until the multiply, so nothing waits on the reads in flight
+  constexpr int NJ = KC / 4;
+  uint32_t fa0[NJ][TT], fa1[NJ][TT];
+  float fb0[NJ][TE], fb1[NJ][TE];
+  auto read_frags = [&](int c, uint32_t (&fa)[NJ][TT], float (&fb)[NJ][TE]) {
+    const uint8_t *sb = s_ring + (c % S) * STAGE;
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) {
+#pragma unroll
+      for (int a = 0; a < TT; ++a) {
+        fa[j][a] = *reinterpret_cast<const uint16_t *>(sb + xo[j >> 1] + (j & 1) * 8 + a * 16 * XROW);
+      }
+#pragma unroll
+      for (int b = 0; b < TE; ++b)
+        fb[j][b] = *reinterpret_cast<const float *>(sb + wo[j & 7] + ((j & 8) << 4) + b * 16 * WROW);
+    }
+  };
+  auto mfmas = [&](const uint32_t (&fa)[NJ][TT], const float (&fb)[NJ][TE]) {
+#pragma unroll
+    for (int j = 0; j < NJ; ++j)
+#pragma unroll
+      for (int a = 0; a < TT; ++a) {
+        const float xa = __uint_as_float(fa[j][a] << 16);   // bf16 -> float32, exact
+#pragma unroll
+        for (int b = 0; b < TE; ++b)
+          acc[a][b] = __builtin_amdgcn_mfma_f32_16x16x4f32(xa, fb[j][b], acc[a][b], 0, 0, 0);
+      }
+  };
+
+  const int nch = d / KC;
+  const int pro = min(S - 1, nch);
+  for (int c = 0; c < pro; ++c) issue(c, c);
+  // stage 0 landed; stages 1 .. pro-1 may stay in flight
+  if (pro - 1 == S - 2) ring::wait_and_barrier<(S - 2) * CPW>();
+  else ring::wait_chunks<CPW, S - 3>(pro - 1);
+  read_frags(0, fa0, fb0);
+  // step c: wait for stage c+1, refill the slot of stage c-1 (its fragments
+  // were consumed in step c-1), read stage c+1, multiply stage c
+  auto advance = [&](int c, const uint32_t (&fa)[NJ][TT], const float (&fb)[NJ][TE],
+                     uint32_t (&na)[NJ][TT], float (&nb)[NJ][TE]) {
+    if (c + 1 < nch) {
+      const int later = min(S - 3, nch - 2 - c);   // stages c+2 .. may stay in flight
+      if (later == S - 3) ring::wait_and_barrier<(S - 3) * CPW>();
+      else ring::wait_chunks<CPW, S - 4>(later);
+      if (c + S - 1 < nch) issue(c + S - 1, (c + S - 1) % S);
+    } else {
+      __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0): every path enters drained
+    }
+    // unconditional, so the next buffer is always freshly loaded (no merge of
+    // old and new values, which would make the compiler copy -- and wait on --
+    // the reads in flight); after the last stage it re-reads a landed slot
+    // and the values go unused
+    __builtin_amdgcn_sched_barrier(0);
+    read_frags(c + 1, na, nb);
+    mfmas(fa, fb);
+    // reads per stage: 16 per token tile (16-bit) and 8 per expert tile (the
+    // compiler pairs the float32 reads of k-quads j and j + 8)
+    constexpr int NM = NJ * TT * TE, NR = NJ * TT + NJ / 2 * TE;
+    interleave_reads<0, NM, NR, (NR + NM - 1) / NM>();
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  for (int c = 0; c < nch; c += 2) {
+    advance(c, fa0, fb0, fa1, fb1);
+    if (c + 1 >= nch) break;
+    advance(c + 1, fa1, fb1, fa0, fb0);
+  }
+#pragma unroll
+  for (int b = 0; b < TE; ++b) {
+    const int e = e0 + wrow + b * 16;
+    if (e >= N) continue;
+    const float be = bias ? bias[e] : 0.0f;
+#pragma unroll
+    for (int a = 0; a < TT; ++a)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int64_t t = t0 + wt * TT * 16 + a * 16 + 4 * g + r;
+        if (t >= T) continue;
+        float v = acc[a][b][r];
+        if (bias) v = v + be;
+        logits[t * N + e] = v;
+      }
+  }
+}
+
 // Key order: a beats b iff a.v > b.v, or equal values and a.i < b.i.
 __device__ __forceinline__ bool key_better(float va, int ia, float vb, int ib) {
   return va > vb || (va == vb && ia < ib);
@@ -367,11 +563,13 @@ __global__ __launch_bounds__(256) void topk_gates_kernel(const float *__restrict
 hipError_t launch_router_logits(bool bf16, const void *x, const float *w, const float *bias,
                                 float *logits, int64_t T, int d, int N, hipStream_t s) {
   if (T <= 0) return hipSuccess;
-  // Shapes measured on MI355X: few logits in all (a decode batch, a narrow
-  // router) go to the LDS-ring kernel, one logit per thread; otherwise wide
-  // routers over many tokens use 64x32 blocks with 4x2 logits per thread,
-  // mid-sized ones 32x32 with 2x2 (both loading two chunks ahead), and the
-  // rest 64x8 with 2x1.
+  // Shapes measured on MI355X.  bf16 tokens with d a multiple of 64: few
+  // 16 x 16 output tiles in all (a decode batch, a narrow router) go to the
+  // LDS-ring kernel, one logit per thread, the rest to the matrix cores.
+  // float32 tokens and other d use the register-tiled kernel: 64x32 blocks
+  // with 4x2 logits per thread for wide routers over many tokens, 32x32 with
+  // 2x2 for mid-sized ones (both loading two chunks ahead), 64x8 with 2x1
+  // otherwise.
   const int64_t TN = T * static_cast<int64_t>(N);
   const int kc32 = d % 32 == 0;
 #define MOE_ROUTER_LAUNCH(BT, BE, MT, ME, KC, PF)                                               \
@@ -385,11 +583,32 @@ hipError_t launch_router_logits(bool bf16, const void *x, const float *w, const 
       hipLaunchKernelGGL((router_logits_kernel<BT, BE, MT, ME, KC, false, PF>), grid,          \
                          dim3(256), 0, s, x, w, bias, logits, T, d, N);                         \
   }
-  if (bf16 && d % 64 == 0 && TN < (int64_t(1) << 17)) {
-    const dim3 grid(static_cast<unsigned>((T + ring::BT - 1) / ring::BT),
-                    static_cast<unsigned>((N + ring::BE - 1) / ring::BE));
-    hipLaunchKernelGGL((router_logits_ring_kernel<12>), grid, dim3(ring::NT), 0, s,
-                       static_cast<const uint16_t *>(x), w, bias, logits, T, d, N);
+  if (bf16 && d % 64 == 0) {
+    const int64_t tiles = ((T + 15) / 16) * ((N + 15) / 16);
+    if (tiles <= 512) {
+      // few 16 x 16 output tiles: a matrix-core chain per tile would be bound
+      // by the latency of its dependent multiplies, so one logit per thread
+      const dim3 grid(static_cast<unsigned>((T + ring::BT - 1) / ring::BT),
+                      static_cast<unsigned>((N + ring::BE - 1) / ring::BE));
+      hipLaunchKernelGGL((router_logits_ring_kernel<12>), grid, dim3(ring::NT), 0, s,
+                         static_cast<const uint16_t *>(x), w, bias, logits, T, d, N);
+      return hipGetLastError();
+    }
+#define MOE_ROUTER_MFMA(AT, AE, TT, TE, S)                                                      \
+  {                                                                                             \
+    constexpr int BT = 16 * AT * TT, BE = 16 * AE * TE;                                         \
+    const dim3 grid(static_cast<unsigned>((T + BT - 1) / BT),                                   \
+                    static_cast<unsigned>((N + BE - 1) / BE));                                  \
+    hipLaunchKernelGGL((router_logits_mfma_kernel<AT, AE, TT, TE, S>), grid, dim3(64 * AT * AE),\
+                       0, s, static_cast<const uint16_t *>(x), w, bias, logits, T, d, N);       \
+  }
+    // measured on MI355X: 64 x 64 per workgroup of 8 waves (two per SIMD, one
+    // token tile x two expert tiles each) for many tiles, 32 x 32 of 4 waves
+    // in between, 64 tokens x 16 experts for narrow routers
+    if (N <= 16) MOE_ROUTER_MFMA(4, 1, 1, 1, 8)
+    else if (tiles <= 2048) MOE_ROUTER_MFMA(2, 2, 1, 1, 8)
+    else MOE_ROUTER_MFMA(4, 2, 1, 2, 4)
+#undef MOE_ROUTER_MFMA
     return hipGetLastError();
   }
   if (N >= 64 && TN >= (int64_t(1) << 19)) {

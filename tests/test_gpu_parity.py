@@ -100,6 +100,18 @@ ROUTE_CASES = [W.get_workload(n) for n in W.WORKLOADS] + [
                       dtype="f32"),
     W.custom_workload("T1_K1", T=1, d_model=16, n_routed=3, top_k=1, n_shared=0, d_ff=16,
                       dtype="f32"),
+    # the LDS-ring logits kernel with ragged tails, then one case per launch
+    # shape of the matrix-core logits kernel, each with ragged token and
+    # expert tails: 32 x 32, 64 x 64 (ring of 4 stages wrapping over 5
+    # k-stages) and 64 tokens x 16 experts
+    W.custom_workload("ring_ragged", T=203, d_model=128, n_routed=40, top_k=6, n_shared=0,
+                      d_ff=64, dtype="bf16", router_bias="gauss", router_bias_var=0.5),
+    W.custom_workload("mfma_32x32", T=1500, d_model=192, n_routed=100, top_k=8, n_shared=0,
+                      d_ff=64, dtype="bf16"),
+    W.custom_workload("mfma_64x64", T=2100, d_model=320, n_routed=272, top_k=8, n_shared=0,
+                      d_ff=64, dtype="bf16", router_bias="gauss", router_bias_var=0.5),
+    W.custom_workload("mfma_64x16", T=9000, d_model=256, n_routed=12, top_k=2, n_shared=0,
+                      d_ff=64, dtype="bf16"),
 ]
 
 
@@ -117,6 +129,33 @@ def test_route_bit_exact(wl):
     b.route(cfg, x, wr, rb, logits, idx, gates)
     torch.cuda.synchronize()
     ref_l, ref_i, ref_g = oracle.route(host(x), host(wr), bias_np(wl), K)
+    assert np.array_equal(logits.cpu().numpy().view(np.uint32), ref_l.view(np.uint32))
+    assert np.array_equal(idx.cpu().numpy(), ref_i)
+    assert np.abs(gates.cpu().numpy() - ref_g).max() <= 1e-6
+
+
+@pytest.mark.parametrize("T,d,N,K", [(203, 128, 40, 6), (1500, 192, 100, 8)],
+                         ids=["ring", "matrix_cores"])
+def test_route_zero_rows_bit_exact(T, d, N, K):
+    # tokens whose x is all zeros and an expert whose router row is all zeros:
+    # every product is a signed zero, and the chain from +0 stays +0
+    b = B()
+    wl = W.custom_workload("zero_rows", T=T, d_model=d, n_routed=N, top_k=K, n_shared=0,
+                           d_ff=64, dtype="bf16")
+    cfg = cfg_of(wl)
+    x = wl.x("cuda").clone()
+    x[::5] = 0
+    x[1::7] = -0.0
+    wr = wl.w_router("cuda").clone()
+    wr[3] = 0
+    wr[17] = -0.0
+    T, N, K = wl.T, wl.n_routed, wl.top_k
+    logits = torch.empty((T, N), dtype=torch.float32, device="cuda")
+    idx = torch.empty((T, K), dtype=torch.int32, device="cuda")
+    gates = torch.empty((T, K), dtype=torch.float32, device="cuda")
+    b.route(cfg, x, wr, None, logits, idx, gates)
+    torch.cuda.synchronize()
+    ref_l, ref_i, ref_g = oracle.route(host(x), host(wr), None, K)
     assert np.array_equal(logits.cpu().numpy().view(np.uint32), ref_l.view(np.uint32))
     assert np.array_equal(idx.cpu().numpy(), ref_i)
     assert np.abs(gates.cpu().numpy() - ref_g).max() <= 1e-6
@@ -219,6 +258,7 @@ def test_route_all_ties_pick_lowest_ids():
     gates = torch.empty((67, 7), dtype=torch.float32, device="cuda")
     b.route(cfg, x, wr, None, logits, idx, gates)
     torch.cuda.synchronize()
+    assert np.array_equal(logits.cpu().numpy().view(np.uint32), np.zeros((67, 40), np.uint32))
     assert np.array_equal(idx.cpu().numpy(), np.tile(np.arange(7, dtype=np.int32), (67, 1)))
     assert np.abs(gates.cpu().numpy() - 1.0 / 7).max() <= 1e-7
 
