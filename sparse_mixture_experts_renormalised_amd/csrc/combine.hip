@@ -4,10 +4,11 @@
 // sum).  Accumulates in float32 in a fixed order: shared experts in index
 // order, then slots k ascending; a dropped slot (row -1) adds nothing.
 //
-// One workgroup per token; the K (row, gate) pairs are loaded once into LDS
-// and every thread walks 16-byte column chunks, so each row is read with
-// fully coalesced 16-byte loads.  Pure HBM traffic: K gathered rows plus the
-// shared rows in, one row out.
+// Workgroup (t, b) of B covers the 16-byte column chunks 256 b + 256 B j ..
+// of token t's row (B = 1 for many tokens, more for few); the K (row, gate)
+// pairs are loaded once into LDS, and each row is read with fully coalesced
+// 16-byte loads.  Pure HBM
+// traffic: K gathered rows plus the shared rows in, one row out.
 #include "moe_common.h"
 
 namespace moe {
@@ -75,7 +76,7 @@ struct Chunk<false> {
   }
 };
 
-template <bool BF16>
+template <bool BF16, int BATCH>
 __global__ __launch_bounds__(256) void combine_kernel(const uint4 *__restrict__ y_rows,
                                                       const int32_t *__restrict__ slot_row,
                                                       const float *__restrict__ gates,
@@ -91,7 +92,7 @@ __global__ __launch_bounds__(256) void combine_kernel(const uint4 *__restrict__ 
     s_gate[threadIdx.x] = gates[t * K + threadIdx.x];
   }
   __syncthreads();
-  for (int i = threadIdx.x; i < nvec; i += blockDim.x) {
+  for (int i = blockIdx.y * blockDim.x + threadIdx.x; i < nvec; i += gridDim.y * blockDim.x) {
     float acc[C::kElems];
 #pragma unroll
     for (int j = 0; j < C::kElems; ++j) acc[j] = 0.0f;
@@ -99,9 +100,27 @@ __global__ __launch_bounds__(256) void combine_kernel(const uint4 *__restrict__ 
     // non-temporal loads and stores keep them from displacing cached data
     for (int sh = 0; sh < n_shared; ++sh)
       C::add1(acc, load_nt(&shared_out[(static_cast<int64_t>(sh) * T + t) * nvec + i]));
-    for (int k = 0; k < K; ++k) {
-      const int32_t r = s_row[k];
-      if (r >= 0) C::add(acc, load_nt(&y_rows[static_cast<int64_t>(r) * nvec + i]), s_gate[k]);
+    if constexpr (BATCH == 1) {
+      for (int k = 0; k < K; ++k) {
+        const int32_t r = s_row[k];
+        if (r >= 0) C::add(acc, load_nt(&y_rows[static_cast<int64_t>(r) * nvec + i]), s_gate[k]);
+      }
+    } else {
+      // slots in batches of BATCH: a batch's loads are all issued before its
+      // first add, and the adds keep slot order
+      for (int k0 = 0; k0 < K; k0 += BATCH) {
+        uint4 q[BATCH];
+#pragma unroll
+        for (int j = 0; j < BATCH; ++j) {
+          const int32_t r = k0 + j < K ? s_row[k0 + j] : -1;
+          if (r >= 0) q[j] = load_nt(&y_rows[static_cast<int64_t>(r) * nvec + i]);
+        }
+#pragma unroll
+        for (int j = 0; j < BATCH; ++j) {
+          const int32_t r = k0 + j < K ? s_row[k0 + j] : -1;
+          if (r >= 0) C::add(acc, q[j], s_gate[k0 + j]);
+        }
+      }
     }
     store_nt(&y[t * nvec + i], C::pack(acc));
   }
@@ -114,18 +133,28 @@ hipError_t launch_combine(bool bf16, const void *y_rows, const int32_t *slot_row
                           int K, int d, void *y, hipStream_t s) {
   if (T <= 0) return hipSuccess;
   const int nvec = d * (bf16 ? 2 : 4) / 16;
-  const dim3 grid(static_cast<unsigned>(T)), block(256);
+  // few tokens (decode): one 16-byte column chunk per thread, a token's row
+  // spread over nvec / 256 workgroups; many tokens: one workgroup per token
+  // walks its row (measured on MI355X)
+  const unsigned split = T < 1024 ? static_cast<unsigned>((nvec + 255) / 256) : 1u;
+  const dim3 grid(static_cast<unsigned>(T), split), block(256);
   if (shared_out == nullptr) n_shared = 0;
-  if (bf16)
-    hipLaunchKernelGGL((combine_kernel<true>), grid, block, 0, s,
-                       static_cast<const uint4 *>(y_rows), slot_row, gates,
-                       static_cast<const uint4 *>(shared_out), n_shared, T, K, nvec,
-                       static_cast<uint4 *>(y));
-  else
-    hipLaunchKernelGGL((combine_kernel<false>), grid, block, 0, s,
-                       static_cast<const uint4 *>(y_rows), slot_row, gates,
-                       static_cast<const uint4 *>(shared_out), n_shared, T, K, nvec,
-                       static_cast<uint4 *>(y));
+  const uint4 *yr = static_cast<const uint4 *>(y_rows);
+  const uint4 *sh = static_cast<const uint4 *>(shared_out);
+  uint4 *yo = static_cast<uint4 *>(y);
+  // the split path also loads eight slot rows before adding them (decode);
+  // with many tokens in flight the plain loop measures faster
+  if (bf16) {
+    if (split > 1)
+      hipLaunchKernelGGL((combine_kernel<true, 8>), grid, block, 0, s, yr, slot_row, gates, sh, n_shared, T, K, nvec, yo);
+    else
+      hipLaunchKernelGGL((combine_kernel<true, 1>), grid, block, 0, s, yr, slot_row, gates, sh, n_shared, T, K, nvec, yo);
+  } else {
+    if (split > 1)
+      hipLaunchKernelGGL((combine_kernel<false, 8>), grid, block, 0, s, yr, slot_row, gates, sh, n_shared, T, K, nvec, yo);
+    else
+      hipLaunchKernelGGL((combine_kernel<false, 1>), grid, block, 0, s, yr, slot_row, gates, sh, n_shared, T, K, nvec, yo);
+  }
   return hipGetLastError();
 }
 

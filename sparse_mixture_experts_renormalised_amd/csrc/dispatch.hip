@@ -16,6 +16,7 @@
 //   3. per chunk, the rank of (t, k) in its expert is the chunk base plus the
 //      popcount of the mask bits below lane t; kept iff rank < C.
 // A token never picks one expert twice, so each mask bit is set at most once.
+// Small problems run the three passes in one workgroup (dispatch_fused_kernel).
 #include "moe_common.h"
 
 namespace moe {
@@ -133,6 +134,108 @@ __global__ __launch_bounds__(256) void dispatch_scatter_kernel(
   }
 }
 
+// The three passes above in one workgroup of 1024 threads, for problems whose
+// chunk masks and chunk base ranks fit in LDS (n_chunks * N small): the
+// launches and their gaps would otherwise dominate a decode batch.  Same
+// arithmetic, so the same outputs: wave w builds the masks of chunks
+// w, w+16, ..; thread e scans expert e over the chunks; the scan of the
+// clipped counts and the drop total are those of dispatch_scan_kernel; the
+// ranks are those of dispatch_scatter_kernel.
+constexpr int kFusedThreads = 1024;
+constexpr int kFusedWaves = kFusedThreads / kWave;
+
+__global__ __launch_bounds__(kFusedThreads) void dispatch_fused_kernel(
+    const int32_t *__restrict__ idx, int64_t T, int K, int N, int64_t capacity,
+    int32_t *__restrict__ counts, int32_t *__restrict__ offsets, int32_t *__restrict__ row_token,
+    int32_t *__restrict__ slot_row, int32_t *__restrict__ n_dropped) {
+  extern __shared__ uint64_t s_dyn[];
+  __shared__ int32_t s_cnt[kMaxRouted];
+  __shared__ int32_t s_drop[kMaxRouted];
+  __shared__ int32_t s_off[kMaxRouted];
+  __shared__ int32_t s_wave[kFusedWaves];
+  const int n_chunks = static_cast<int>((T + kChunk - 1) / kChunk);
+  uint64_t *s_mask = s_dyn;                                              // [n_chunks][N]
+  int32_t *s_base = reinterpret_cast<int32_t *>(s_dyn + static_cast<size_t>(n_chunks) * N);
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  for (int i = tid; i < n_chunks * N; i += kFusedThreads) s_mask[i] = 0;
+  __syncthreads();
+  // pass 1: per chunk, the lane mask of the tokens that chose each expert
+  for (int c = wave; c < n_chunks; c += kFusedWaves) {
+    const int64_t t = static_cast<int64_t>(c) * kChunk + lane;
+    if (t < T)
+      for (int k = 0; k < K; ++k)
+        atomicOr(reinterpret_cast<unsigned long long *>(&s_mask[c * N + idx[t * K + k]]),
+                 1ull << lane);
+  }
+  __syncthreads();
+  // pass 2: base rank of every chunk per expert, clipped totals, drops
+  for (int e = tid; e < N; e += kFusedThreads) {
+    int32_t run = 0;
+    for (int c = 0; c < n_chunks; ++c) {
+      s_base[c * N + e] = run;
+      run += __popcll(s_mask[c * N + e]);
+    }
+    const int32_t kept = (capacity >= 0 && run > capacity) ? static_cast<int32_t>(capacity) : run;
+    counts[e] = kept;
+    s_cnt[e] = kept;
+    s_drop[e] = run - kept;
+  }
+  __syncthreads();
+  // exclusive scan of the clipped counts (N <= 1024: one entry per thread)
+  {
+    const int e = tid;
+    const int32_t v = e < N ? s_cnt[e] : 0;
+    int32_t dr = e < N ? s_drop[e] : 0;
+    int32_t incl = v;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const int32_t o = __shfl_up(incl, off);
+      if (lane >= off) incl += o;
+    }
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) dr += __shfl_xor(dr, off);
+    if (lane == 63) s_wave[wave] = incl;
+    __syncthreads();
+    int32_t wave_base = 0;
+    for (int w = 0; w < wave; ++w) wave_base += s_wave[w];
+    if (e < N) {
+      offsets[e] = wave_base + incl - v;
+      s_off[e] = wave_base + incl - v;
+    }
+    if (e == N - 1) offsets[N] = wave_base + incl;
+    __syncthreads();
+    if (lane == 0) s_wave[wave] = dr;
+    __syncthreads();
+    if (tid == 0) {
+      int32_t tot = 0;
+      for (int w = 0; w < kFusedWaves; ++w) tot += s_wave[w];
+      *n_dropped = tot;
+    }
+  }
+  // pass 3: rank of (t, k) = chunk base + mask bits below the lane
+  const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+  for (int c = wave; c < n_chunks; c += kFusedWaves) {
+    const int64_t t = static_cast<int64_t>(c) * kChunk + lane;
+    if (t >= T) continue;
+    for (int k = 0; k < K; ++k) {
+      const int e = idx[t * K + k];
+      const int64_t rank = s_base[c * N + e] + __popcll(s_mask[c * N + e] & below);
+      int32_t r = -1;
+      if (capacity < 0 || rank < capacity) {
+        r = s_off[e] + static_cast<int32_t>(rank);
+        row_token[r] = static_cast<int32_t>(t);
+      }
+      slot_row[t * K + k] = r;
+    }
+  }
+}
+
+// Limits of the fused dispatch: dynamic LDS for the masks and base ranks of
+// every chunk, and assignments (measured on MI355X: at 8,192 one workgroup
+// beats the three launches, at 32,768 it takes twice as long).
+constexpr size_t kFusedMaxLds = 48 * 1024;
+constexpr int64_t kFusedMaxAssign = 8192;
+
 // out[r] = x[row_token[r]] for r < *total_rows; one workgroup per row.
 template <typename VEC>
 __global__ __launch_bounds__(256) void gather_rows_kernel(const VEC *__restrict__ x,
@@ -170,6 +273,12 @@ hipError_t launch_dispatch(const int32_t *idx, int64_t T, int K, int N, int64_t 
   p += align256(cells * sizeof(int32_t));
   int32_t *base = reinterpret_cast<int32_t *>(p);
 
+  const size_t fused_lds = cells * (sizeof(uint64_t) + sizeof(int32_t));
+  if (fused_lds <= kFusedMaxLds && T * K <= kFusedMaxAssign) {
+    hipLaunchKernelGGL(dispatch_fused_kernel, dim3(1), dim3(kFusedThreads), fused_lds, s, idx, T,
+                       K, N, capacity, counts, offsets, row_token, slot_row, n_dropped);
+    return hipGetLastError();
+  }
   const unsigned blocks = static_cast<unsigned>((n_chunks + kChunksPerBlock - 1) / kChunksPerBlock);
   if (n_chunks > 0) {
     hipLaunchKernelGGL(dispatch_masks_kernel, dim3(blocks), dim3(256),

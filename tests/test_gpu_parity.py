@@ -275,6 +275,9 @@ def random_idx(T, N, K, seed):
 PERMUTE_CASES = [
     (1, 4, 1, -1), (63, 8, 2, -1), (64, 8, 2, -1), (65, 8, 2, 3), (200, 33, 5, -1),
     (200, 33, 5, 0), (200, 33, 5, 7), (777, 256, 8, 5), (4097, 64, 8, -1), (300, 1000, 16, 2),
+    # either side of the single-workgroup dispatch's limits: 8,192 assignments,
+    # and 48 KB of chunk masks and ranks (chunks x N = 4,096)
+    (1024, 8, 8, -1), (1025, 8, 8, 4), (256, 1024, 4, 1), (257, 1024, 4, -1),
 ]
 
 
@@ -394,10 +397,16 @@ def test_grouped_ffn_matches_oracle(case):
 # moe_combine (fed oracle expert outputs and gates)
 # ---------------------------------------------------------------------------
 
-@pytest.mark.parametrize("dtype,Ks,C", [("f32", 0, -1), ("bf16", 2, -1), ("bf16", 1, 2)])
-def test_combine_matches_oracle(dtype, Ks, C):
+@pytest.mark.parametrize("dtype,Ks,C,T,N,K,d", [
+    ("f32", 0, -1, 97, 12, 3, 128), ("bf16", 2, -1, 97, 12, 3, 128), ("bf16", 1, 2, 97, 12, 3, 128),
+    # a row over two workgroups with a ragged second (288 chunks of 16 bytes),
+    # and eleven slots (a second, partial batch of loads)
+    ("bf16", 1, 3, 97, 24, 11, 2304),
+    # many tokens: one workgroup walks its row in three passes, the last ragged
+    ("bf16", 0, -1, 1100, 16, 2, 4224),
+])
+def test_combine_matches_oracle(dtype, Ks, C, T, N, K, d):
     b = B()
-    T, N, K, d = 97, 12, 3, 128
     wl = W.custom_workload("comb", T=T, d_model=d, n_routed=N, top_k=K, n_shared=Ks, d_ff=64,
                            dtype=dtype)
     idx_h = random_idx(T, N, K, 5)
