@@ -140,3 +140,37 @@ def test_bias_mode_is_validated(B):
     assert L.moe_balance_stats(ctypes.byref(ok), P(16), P(16), 0.01, P(16), P(16), P(16), None, 0,
                                None) == -3
     assert B.balance_stats_workspace_size(ok) == 4 * 8   # one 64-token block x N floats
+
+
+def test_missing_library_fails_loudly(tmp_path):
+    # the product path has no fallback: without the built library, loading raises
+    import subprocess
+    import sys
+    code = ("from sparse_mixture_experts_renormalised_amd import binding\n"
+            "try:\n"
+            "    binding.lib()\n"
+            "except RuntimeError as e:\n"
+            "    print('raised:', e)\n"
+            "else:\n"
+            "    print('loaded')\n")
+    env = dict(os.environ, MOE_MI355X_LIB=str(tmp_path / "absent.so"))
+    out = subprocess.run([sys.executable, "-c", code], cwd=ROOT, env=env, capture_output=True,
+                         text=True, timeout=300)
+    assert out.returncode == 0, out.stderr
+    assert out.stdout.startswith("raised:"), out.stdout
+
+
+def test_package_never_imports_the_oracle():
+    # the oracle is test infrastructure: no module of the package may reach it
+    import re
+    pkg = os.path.join(ROOT, "sparse_mixture_experts_renormalised_amd")
+    pat = re.compile(r"^\s*(import\s+oracle\b|from\s+oracle\b|from\s+\.\.\s*import\s+oracle)", re.M)
+    hits = []
+    for dirpath, _, files in os.walk(pkg):
+        for f in files:
+            if f.endswith(".py"):
+                path = os.path.join(dirpath, f)
+                with open(path) as fh:
+                    if pat.search(fh.read()):
+                        hits.append(path)
+    assert not hits, hits
