@@ -231,6 +231,13 @@ __device__ __forceinline__ void dma16_nt(const uint16_t *src, uint32_t m0) {
   asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, off nt" : : "v"(src), "{m0}"(m0) : "memory");
 }
 
+// The same copy addressed as a wave-uniform 64-bit base in SGPRs plus a 32-bit
+// per-lane byte offset (the instruction's SGPR-base form): advancing along K
+// then costs one scalar add per base instead of a 64-bit vector add per copy.
+__device__ __forceinline__ void dma16s(uint32_t voff, const uint16_t *sbase, uint32_t m0) {
+  asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" : : "v"(voff), "s"(sbase), "{m0}"(m0) : "memory");
+}
+
 // Wait until at most N of this wave's copies are in flight and its LDS reads
 // are done, then meet the other waves.
 template <int N>
@@ -574,49 +581,95 @@ __device__ __forceinline__ void rs_tile_at(const GemmArgs &a, const RsTiles &t,
 // K-step k0 on.  Copy i of wave w fills rows 8*(4i+w) .. +7 of the 512-row
 // tile (A rows, then B rows) at LDS bytes (4i+w)*1024 .. +1023: lane l writes
 // row 8*(4i+w) + l/8 at 16-byte position l%8, so it fetches the chunk that
-// the swizzle puts there, c = (l%8) ^ ((row/2)%8).
-struct RsSrc {
+// the swizzle puts there, c = (l%8) ^ ((row/2)%8).  With OFF32 the sources
+// are 32-bit byte offsets from two wave-uniform bases (A and the group's W),
+// which the host allows when every offset fits; otherwise 64-bit pointers.
+template <bool OFF32>
+struct RsSrc;
+template <>
+struct RsSrc<false> {
   const uint16_t *a[rs::A_CH];
   const uint16_t *b[rs::B_CH];
 };
+template <>
+struct RsSrc<true> {
+  uint32_t a[rs::A_CH];
+  uint32_t b[rs::B_CH];
+  const uint16_t *abase, *bbase;   // at K-step k0
+};
 
+__device__ __forceinline__ const uint16_t *uniform_ptr(const uint16_t *p) {
+  const uint64_t u = reinterpret_cast<uint64_t>(p);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(u));
+  const uint32_t hi = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(u >> 32));
+  return reinterpret_cast<const uint16_t *>((static_cast<uint64_t>(hi) << 32) | lo);
+}
+
+template <bool OFF32>
 __device__ __forceinline__ void rs_src(const GemmArgs &a, const TileView<uint16_t> &v, int n0,
-                                       int k0, int tid, RsSrc &src) {
+                                       int k0, int tid, RsSrc<OFF32> &src) {
   using namespace rs;
   const int c = (tid & 7) ^ ((tid >> 4) & 7);   // row = tid/8 + 32i, so (row/2)%8 = (tid/16)%8
+  if constexpr (OFF32) {
+    const uint16_t *ab = v.g < a.n_routed
+                             ? static_cast<const uint16_t *>(a.A)
+                             : static_cast<const uint16_t *>(a.A_sh) +
+                                   static_cast<int64_t>(v.g - a.n_routed) * a.a_sh_stride;
+    src.abase = uniform_ptr(ab + static_cast<int64_t>(k0) * BK);
+    src.bbase = uniform_ptr(v.W + static_cast<int64_t>(k0) * BK);
 #pragma unroll
-  for (int i = 0; i < A_CH; ++i)
-    src.a[i] = a_row_ptr(a, v, v.row0 + (tid >> 3) + i * (NT / 8)) + c * 8 + k0 * BK;
+    for (int i = 0; i < A_CH; ++i)
+      src.a[i] = static_cast<uint32_t>(
+          (a_row_ptr(a, v, v.row0 + (tid >> 3) + i * (NT / 8)) - ab) * 2 + c * 16);
 #pragma unroll
-  for (int i = 0; i < B_CH; ++i) {
-    int n = n0 + (tid >> 3) + i * (NT / 8);
-    if (n >= a.Nout) n = a.Nout - 1;
-    src.b[i] = v.W + static_cast<int64_t>(n) * a.K + c * 8 + k0 * BK;
+    for (int i = 0; i < B_CH; ++i) {
+      int n = n0 + (tid >> 3) + i * (NT / 8);
+      if (n >= a.Nout) n = a.Nout - 1;
+      src.b[i] = static_cast<uint32_t>(static_cast<int64_t>(n) * a.K * 2 + c * 16);
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < A_CH; ++i)
+      src.a[i] = a_row_ptr(a, v, v.row0 + (tid >> 3) + i * (NT / 8)) + c * 8 + k0 * BK;
+#pragma unroll
+    for (int i = 0; i < B_CH; ++i) {
+      int n = n0 + (tid >> 3) + i * (NT / 8);
+      if (n >= a.Nout) n = a.Nout - 1;
+      src.b[i] = v.W + static_cast<int64_t>(n) * a.K + c * 8 + k0 * BK;
+    }
   }
 }
 
 // Copy I of K-step kb into the tile buffer at LDS byte address base.
-__device__ __forceinline__ void rs_copy(const RsSrc &src, int i, int kb, uint32_t base,
+template <bool OFF32>
+__device__ __forceinline__ void rs_copy(const RsSrc<OFF32> &src, int i, int kb, uint32_t base,
                                         int wave) {
   using namespace rs;
-  if (i < A_CH)
-    dma::dma16(src.a[i] + kb * BK, base + (4 * i + wave) * 1024);
-  else
-    dma::dma16(src.b[i - A_CH] + kb * BK, base + (4 * i + wave) * 1024);
+  if constexpr (OFF32) {
+    if (i < A_CH)
+      dma::dma16s(src.a[i], src.abase + kb * BK, base + (4 * i + wave) * 1024);
+    else
+      dma::dma16s(src.b[i - A_CH], src.bbase + kb * BK, base + (4 * i + wave) * 1024);
+  } else {
+    if (i < A_CH)
+      dma::dma16(src.a[i] + kb * BK, base + (4 * i + wave) * 1024);
+    else
+      dma::dma16(src.b[i - A_CH] + kb * BK, base + (4 * i + wave) * 1024);
+  }
 }
 
 // Copies I.. of step kb, one before each group of three MFMAs of the first
 // three slices (48 MFMAs for 16 copies); each group is its own scheduling
 // region so the copies stay spread out.
-template <int I>
-__device__ __forceinline__ void rs_copies_mfmas(const RsSrc &src, int kb, uint32_t base,
+template <int I, bool OFF32>
+__device__ __forceinline__ void rs_copies_mfmas(const RsSrc<OFF32> &src, int kb, uint32_t base,
                                                 int wave, const rs::Frags &f,
                                                 f32x16_t (&acc)[rs::TN][rs::TM]) {
   if constexpr (I < rs::A_CH + rs::B_CH) {
     rs_copy(src, I, kb, base, wave);
     rs::mfma_range<3 * I, 3 * I + 3>(f, acc);
     __builtin_amdgcn_sched_barrier(0);
-    rs_copies_mfmas<I + 1>(src, kb, base, wave, f, acc);
+    rs_copies_mfmas<I + 1, OFF32>(src, kb, base, wave, f, acc);
   }
 }
 
@@ -624,7 +677,8 @@ __device__ __forceinline__ void rs_copies_mfmas(const RsSrc &src, int kb, uint32
 // s_tile holds two tile buffers; step kb lives in buffer kb % 2.  Returns
 // once the last step's MFMAs are issued; the caller passes an LDS barrier
 // before reusing the buffers.
-__device__ __forceinline__ void rs_body(const RsSrc &src, int nk, uint16_t *s_tile, int tid,
+template <bool OFF32>
+__device__ __forceinline__ void rs_body(const RsSrc<OFF32> &src, int nk, uint16_t *s_tile, int tid,
                                         int lane, int wm, int wn,
                                         f32x16_t (&acc)[rs::TN][rs::TM]) {
   using namespace rs;
@@ -656,7 +710,7 @@ __device__ __forceinline__ void rs_body(const RsSrc &src, int nk, uint16_t *s_ti
     const int cur = kb & 1;
     lds_barrier();                          // every wave has its fragments of step kb
     __builtin_amdgcn_sched_barrier(0);
-    rs_copies_mfmas<0>(src, kb + 2, cur ? b1 : b0, wave, f, acc);   // step kb+2 into buffer cur
+    rs_copies_mfmas<0, OFF32>(src, kb + 2, cur ? b1 : b0, wave, f, acc);   // step kb+2 into buffer cur
     dma::wait_and_barrier<NCP>();           // step kb+1 landed for every wave
     mfma_range<48, 64>(f, acc);             // last slice of step kb
     read_frags(s_tile + (cur ? 0 : TILE), f, wm, wn, lane);          // step kb+1
@@ -673,11 +727,12 @@ __device__ __forceinline__ void rs_body(const RsSrc &src, int nk, uint16_t *s_ti
 }
 
 // Accumulators of one 256x256 tile over K-steps k0 .. k0+nk-1.
+template <bool OFF32>
 __device__ __forceinline__ void rs_tile(const GemmArgs &a, const TileView<uint16_t> &v, int n0,
                                         int k0, int nk, uint16_t *s_tile, int tid, int lane,
                                         int wm, int wn, f32x16_t (&acc)[rs::TN][rs::TM]) {
-  RsSrc src;
-  rs_src(a, v, n0, k0, tid, src);
+  RsSrc<OFF32> src;
+  rs_src<OFF32>(a, v, n0, k0, tid, src);
   rs_body(src, nk, s_tile, tid, lane, wm, wn, acc);
   rs::lds_barrier();
 }
@@ -795,7 +850,7 @@ __device__ __forceinline__ void rh_epilogue(const f32x16_t (&acc)[rh::TN][rh::TM
 // no split).  PIECE = true: the K pieces of the remainder tiles, one per
 // workgroup, stored as float32 partial tiles (launched right after, with the
 // same grid, so both derive the same plan).
-template <int EPI, int GM, bool PIECE>
+template <int EPI, int GM, bool PIECE, bool OFF32>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void grouped_gemm_bf16_rs_kernel(GemmArgs a, RsSplit sp) {
   using namespace rs;
@@ -837,7 +892,7 @@ void grouped_gemm_bf16_rs_kernel(GemmArgs a, RsSplit sp) {
                 make_float4(acch[i][j][4 * q], acch[i][j][4 * q + 1], acch[i][j][4 * q + 2],
                             acch[i][j][4 * q + 3]);
     } else {
-      rs_tile(a, v, nt * BN, k0, kn, s_tile, tid, lane, wm, wn, acc);
+      rs_tile<OFF32>(a, v, nt * BN, k0, kn, s_tile, tid, lane, wm, wn, acc);
 #pragma unroll
       for (int i = 0; i < TN; ++i)
 #pragma unroll
@@ -862,7 +917,7 @@ void grouped_gemm_bf16_rs_kernel(GemmArgs a, RsSplit sp) {
     for (; i < end_f; i += nslots) {       // full-cost tiles
       rs_tile_at<GM>(a, t, s_pref_f, s_pref_h, i, &g, &lm, &nt);
       const TileView<uint16_t> v = tile_view<uint16_t>(a, g, lm, BM);
-      rs_tile(a, v, nt * BN, 0, nk, s_tile, tid, lane, wm, wn, acc);
+      rs_tile<OFF32>(a, v, nt * BN, 0, nk, s_tile, tid, lane, wm, wn, acc);
       rs_epilogue<EPI>(acc, a, v, nt * BN, s_tile, lane, wm, wn, tid);
     }
     for (; i < end; i += nslots) {         // half-height tail tiles
@@ -1489,6 +1544,17 @@ hipError_t launch_bf16_stream(const GemmArgs &a, const GemmGroups &g, Epilogue e
 constexpr int64_t kRsPieceBytes = 256 * 256 * sizeof(float);
 constexpr int kRsMaxBlocks = 256;
 
+// The 256x256 kernel's copies address their sources as 32-bit byte offsets
+// from wave-uniform bases when every offset fits: A rows lie below
+// max(max_routed_rows, T_sh) (gathered rows index the T_sh tokens), W rows
+// below Nout.  Larger operands take the 64-bit form.
+bool rs_off32(const GemmGroups &g) {
+  if (g.a_index && g.T_sh <= 0) return false;
+  const int64_t rows = g.max_routed_rows > g.T_sh ? g.max_routed_rows : g.T_sh;
+  const int64_t lim = (int64_t(1) << 32) - 4096;
+  return rows * g.K * 2 < lim && static_cast<int64_t>(g.Nout) * g.K * 2 < lim;
+}
+
 template <int GM>
 hipError_t launch_bf16_rs(const GemmArgs &a, const GemmGroups &g, Epilogue epi, hipStream_t s) {
   const unsigned grid = persistent_grid(tiles_upper_bound(g, 256, 256), 1);
@@ -1497,13 +1563,22 @@ hipError_t launch_bf16_rs(const GemmArgs &a, const GemmGroups &g, Epilogue epi, 
     sp.max_blocks = static_cast<int>(static_cast<int64_t>(g.split_bytes) / kRsPieceBytes);
     if (sp.max_blocks >= static_cast<int>(grid)) sp.partial = static_cast<float *>(g.split_ws);
   }
-  if (epi == kEpiBiasSilu)
-    hipLaunchKernelGGL((grouped_gemm_bf16_rs_kernel<kEpiBiasSilu, GM, false>), dim3(grid), dim3(256), 0, s, a, sp);
-  else
-    hipLaunchKernelGGL((grouped_gemm_bf16_rs_kernel<kEpiBias, GM, false>), dim3(grid), dim3(256), 0, s, a, sp);
+  const bool off32 = rs_off32(g);
+#define MOE_RS_LAUNCH(EPI, PIECE)                                                                \
+  {                                                                                              \
+    if (off32)                                                                                   \
+      hipLaunchKernelGGL((grouped_gemm_bf16_rs_kernel<EPI, GM, PIECE, true>), dim3(grid),        \
+                         dim3(256), 0, s, a, sp);                                                \
+    else                                                                                         \
+      hipLaunchKernelGGL((grouped_gemm_bf16_rs_kernel<EPI, GM, PIECE, false>), dim3(grid),       \
+                         dim3(256), 0, s, a, sp);                                                \
+  }
+  if (epi == kEpiBiasSilu) MOE_RS_LAUNCH(kEpiBiasSilu, false)
+  else MOE_RS_LAUNCH(kEpiBias, false)
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || !sp.partial) return e;
-  hipLaunchKernelGGL((grouped_gemm_bf16_rs_kernel<kEpiBias, GM, true>), dim3(grid), dim3(256), 0, s, a, sp);
+  MOE_RS_LAUNCH(kEpiBias, true)
+#undef MOE_RS_LAUNCH
   if ((e = hipGetLastError()) != hipSuccess) return e;
   // at most half of each XCD's workgroups hold remainder tiles; four
   // fixup workgroups per tile
