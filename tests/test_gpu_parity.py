@@ -362,6 +362,10 @@ FFN_CASES = [
     # the same partial rounds with too few K-steps to split along K: their
     # full-cost tiles are split along M into half-height tiles instead
     ("bf16_msplit", [700, 300, 520], 512, 1024, "bf16", True, 8192),
+    # a row bound of 1.1 M rows: A could span 9 GB (first Linear) and 4.5 GB
+    # (second), so the 256x256 kernel addresses its copies with 64-bit
+    # pointers instead of 32-bit offsets from uniform bases
+    ("bf16_wide_offsets", [700, 300, 520], 4096, 2048, "bf16", True, 1100000),
 ]
 
 
