@@ -1051,15 +1051,56 @@ __global__ __launch_bounds__(256) void rs_fixup_kernel(GemmArgs a, RsSplit sp, i
 // Few units (a decode batch touches few experts) would leave CUs idle, so
 // the kernel splits K into up to ks_cap parts when there are fewer than four
 // units per workgroup; every workgroup derives the same split from the
-// device-side counts.  Split parts write float32 partial sums per output row,
-// and stream_reduce_kernel adds them in part order and applies the epilogue.
+// device-side counts.  Split parts write float32 partial sums per output row.
+// Otherwise, when an XCD's last round of units would leave at least half its
+// workgroups idle, those units alone are split along K into pieces that fill
+// the round (stream_plan).  stream_finish_kernel adds the parts or pieces in
+// order and applies the epilogue.
 // ---------------------------------------------------------------------------
 struct StreamSplit {
   float *partial;      // [ks_cap][part_rows + n_shared * T_sh][Nout] or null
   int *ks_used;        // device scalar: the split the kernel chose
   int64_t part_rows;   // routed rows in the partial buffer (host bound)
   int ks_cap;          // 1: never split
+  float *rem;          // [grid][rows x features of a unit]: K pieces of last-round units, or null
 };
+
+// The last round of a stream launch: each XCD's units run in rounds of its
+// nslots workgroups; when the last round would leave at least half of them
+// idle, its units are split along K into P pieces (at least four chunks each)
+// that fill the idle workgroups, write float32 tiles to the rem buffer, and
+// are added in piece order by stream_finish_kernel.
+constexpr int kStreamRemBlocks = 256;                          // workgroups with a piece tile
+constexpr int64_t kStreamRemTile = 128 * 256;                  // floats per piece tile (largest unit)
+constexpr int64_t kStreamRemBytes = kStreamRemBlocks * kStreamRemTile * 4;
+
+struct StreamPlan {
+  int begin;   // first unit of the XCD
+  int full;    // units in full rounds
+  int rem;     // units of the last round
+  int P;       // pieces per last-round unit (1: not split)
+  int per;     // K chunks per piece
+};
+
+__device__ __forceinline__ StreamPlan stream_plan(int total, int xcd, int nslots, int nkc,
+                                                  bool can_split) {
+  StreamPlan p;
+  const int part = (total + kXcds - 1) / kXcds;
+  p.begin = xcd * part;
+  const int cnt = max(0, min(total, p.begin + part) - p.begin);
+  p.full = (cnt / nslots) * nslots;
+  p.rem = cnt - p.full;
+  p.P = 1;
+  p.per = nkc;
+  if (can_split && p.rem > 0 && 2 * p.rem <= nslots) {
+    const int P = min(min(nslots / p.rem, 8), nkc / 4);
+    if (P >= 2) {
+      p.per = (nkc + P - 1) / P;
+      p.P = (nkc + p.per - 1) / p.per;   // no empty pieces
+    }
+  }
+  return p;
+}
 
 namespace st {
 constexpr int NT = 256, NW = 4, KCH = 64;
@@ -1105,12 +1146,25 @@ __device__ __forceinline__ int stream_split(int base_units, int nkc, int ks_cap,
 template <int MB, int NTB, int EPI>
 __device__ __forceinline__ void stream_store(const f32x16_t (&acc)[MB][NTB], const GemmArgs &a,
                                              const TileView<uint16_t> &v, int g, int nw0, int kp,
-                                             int ks, const StreamSplit &sp, int r32, int h) {
+                                             int ks, const StreamSplit &sp, int r32, int h,
+                                             float *piece, int wf0) {
 #pragma unroll
   for (int j = 0; j < NTB; ++j) {
     const int64_t lr = v.row0 + 32 * j + r32;
     if (lr >= v.rows) continue;
-    if (ks > 1) {
+    if (piece) {
+      // a K piece of a last-round unit: float32 tile [unit row][unit feature]
+      constexpr int NB = 4 * 32 * MB;
+      float *dst = piece + static_cast<int64_t>(32 * j + r32) * NB + wf0;
+#pragma unroll
+      for (int i = 0; i < MB; ++i)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const f32x16_t &c = acc[i][j];
+          *reinterpret_cast<float4 *>(dst + 32 * i + 8 * q + 4 * h) =
+              make_float4(c[4 * q], c[4 * q + 1], c[4 * q + 2], c[4 * q + 3]);
+        }
+    } else if (ks > 1) {
       const int64_t prow = g < a.n_routed
                                ? v.out_base + lr
                                : sp.part_rows + static_cast<int64_t>(g - a.n_routed) * a.T_sh + lr;
@@ -1167,7 +1221,7 @@ template <int MB, int NTB, int S, int STRIDE, int EPI>
 __device__ __forceinline__ void stream_unit(const GemmArgs &a, const StreamSplit &sp, int g,
                                             int mg, int nb, int rb, int kp, int ks, int kc_per,
                                             uint16_t *s_ring, uint32_t ring0, int &stage,
-                                            int lane, int wave) {
+                                            int lane, int wave, float *piece) {
   using namespace st;
   constexpr int MR = 32 * NTB;                   // rows per unit
   constexpr int NB = 4 * 32 * MB;                // features per unit
@@ -1256,7 +1310,8 @@ __device__ __forceinline__ void stream_unit(const GemmArgs &a, const StreamSplit
     }
   }
   stage = (stage + nch) % S;
-  stream_store<MB, NTB, EPI>(acc, a, v, g, n0 + wave * 32 * MB, kp, ks, sp, r32, h);
+  stream_store<MB, NTB, EPI>(acc, a, v, g, n0 + wave * 32 * MB, kp, ks, sp, r32, h, piece,
+                             wave * 32 * MB);
 }
 
 // NTB2 > NTB gives the kernel a second unit height: groups of more than
@@ -1290,40 +1345,41 @@ __global__ __launch_bounds__(256) void grouped_gemm_bf16_stream_kernel(GemmArgs 
   const int xcd = blockIdx.x % kXcds;
   const int slot = blockIdx.x / kXcds;
   const int nslots = gridDim.x / kXcds;
-  const int part = (total + kXcds - 1) / kXcds;
-  const int begin = xcd * part;
-  const int end = min(total, begin + part);
   const uint32_t ring0 = uniform(static_cast<int>(lds_addr(s_ring)));
   int stage = 0;
-  for (int L = begin + slot; L < end; L += nslots) {
-    // unit order: part fastest, then row block, then feature block, so the
-    // workgroups running together share a weight block in L2
-    const int kp = L % ks;
-    const int u = L / ks;
+  auto run = [&](int u, int kp, int ks_u, int per, float *piece) {
     const int g = find_group(s_pref, n_groups, u / n_nb);
     const int mg = s_pref[g + 1] - s_pref[g];
     const int uu = u - s_pref[g] * n_nb;
     const int nb = uu / mg, rb = uu % mg;
     if (NTB2 <= NTB || group_rows(a, g) <= MR1)
-      stream_unit<MB, NTB, S, STRIDE, EPI>(a, sp, g, mg, nb, rb, kp, ks, kc_per, s_ring, ring0,
-                                           stage, lane, wave);
+      stream_unit<MB, NTB, S, STRIDE, EPI>(a, sp, g, mg, nb, rb, kp, ks_u, per, s_ring, ring0,
+                                           stage, lane, wave, piece);
     else
-      stream_unit<MB, (NTB2 > NTB ? NTB2 : NTB), S, STRIDE, EPI>(a, sp, g, mg, nb, rb, kp, ks,
-                                                                 kc_per, s_ring, ring0, stage,
-                                                                 lane, wave);
-  }
+      stream_unit<MB, (NTB2 > NTB ? NTB2 : NTB), S, STRIDE, EPI>(a, sp, g, mg, nb, rb, kp, ks_u,
+                                                                 per, s_ring, ring0, stage, lane,
+                                                                 wave, piece);
+  };
+  // unit order: part fastest, then row block, then feature block, so the
+  // workgroups running together share a weight block in L2
+  const StreamPlan pl = stream_plan(total, xcd, nslots, nkc, ks == 1 && sp.rem != nullptr &&
+                                                                 gridDim.x <= kStreamRemBlocks);
+  // the XCD's count of split units, for stream_finish_kernel (header ints
+  // 16 .. 23 of the split scratch; written on every launch)
+  if (slot == 0 && threadIdx.x == 0 && sp.rem) sp.ks_used[16 + xcd] = pl.P > 1 ? pl.rem : 0;
+  const int whole_end = pl.begin + pl.full + (pl.P > 1 ? 0 : pl.rem);
+  for (int L = pl.begin + slot; L < whole_end; L += nslots) run(L / ks, L % ks, ks, kc_per, nullptr);
+  if (pl.P > 1 && slot < pl.rem * pl.P)
+    run(pl.begin + pl.full + slot / pl.P, slot % pl.P, pl.P, pl.per,
+        sp.rem + static_cast<int64_t>(blockIdx.x) * kStreamRemTile);
 }
 
-// Sum of the k-split partials in part order, bias, epilogue, bf16 store.
-// One thread per four features of one output row; rows of routed groups past
+// Sum of the K-split partials of output row prow, features n .. n+3, in part
+// order; bias, epilogue, bf16 store.  Rows of routed groups past
 // offsets[n_routed] do not exist and are skipped.
 template <int EPI>
-__global__ __launch_bounds__(256) void stream_reduce_kernel(GemmArgs a, StreamSplit sp) {
-  const int ks = *sp.ks_used;
-  if (ks <= 1) return;
-  const int64_t prow = blockIdx.y;
-  const int n = (blockIdx.x * 256 + threadIdx.x) * 4;
-  if (n >= a.Nout) return;
+__device__ __forceinline__ void reduce_parts(const GemmArgs &a, const StreamSplit &sp, int ks,
+                                             int64_t prow, int n) {
   const int64_t nrows = sp.part_rows + static_cast<int64_t>(a.n_shared) * a.T_sh;
   const uint16_t *bias;
   uint16_t *dst;
@@ -1367,6 +1423,92 @@ __global__ __launch_bounds__(256) void stream_reduce_kernel(GemmArgs a, StreamSp
   packed.x = pack_bf16x2(o[0], o[1]);
   packed.y = pack_bf16x2(o[2], o[3]);
   *reinterpret_cast<uint2 *>(dst + n) = packed;
+}
+
+// After a stream launch of grid workgroups: with a uniform K split, the sum
+// of every row's parts; otherwise workgroups (xcd, j, 0 .. kFinishPerUnit-1)
+// of this launch add the pieces of the j-th last-round unit of that XCD, if
+// the launch split it (stream_plan on the same device counts decides exactly
+// as the stream kernel did).
+constexpr int kFinishPerUnit = 16;
+template <int MB, int NTB, int NTB2, int EPI>
+__global__ __launch_bounds__(256) void stream_finish_kernel(GemmArgs a, StreamSplit sp, int grid) {
+  using namespace st;
+  const int ks = *sp.ks_used;
+  if (ks > 1) {
+    const int64_t nrows = sp.part_rows + static_cast<int64_t>(a.n_shared) * a.T_sh;
+    const int nq = a.Nout / 4;
+    for (int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; i < nrows * nq;
+         i += static_cast<int64_t>(gridDim.x) * blockDim.x)
+      reduce_parts<EPI>(a, sp, ks, i / nq, static_cast<int>(i % nq) * 4);
+    return;
+  }
+  if (!sp.rem || grid > kStreamRemBlocks) return;
+  const int nslots = grid / kXcds;
+  const int xcd = blockIdx.x % kXcds;
+  const int j = (blockIdx.x / kXcds) % (nslots / 2 > 0 ? nslots / 2 : 1);
+  const int q = (blockIdx.x / kXcds) / (nslots / 2 > 0 ? nslots / 2 : 1);
+  if (j >= sp.ks_used[16 + xcd]) return;   // not a split unit of this launch
+  constexpr int MR1 = 32 * NTB, MR2 = 32 * (NTB2 > NTB ? NTB2 : NTB);
+  constexpr int NB = 4 * 32 * MB;
+  __shared__ int s_pref[kMaxGroups + 1];
+  __shared__ int s_tmp[NT / 64];
+  const int n_groups = a.n_routed + a.n_shared;
+  const int total_m = build_prefix<NT>(n_groups, [&](int g) {
+    const int64_t rows = group_rows(a, g);
+    const int mr = rows <= MR1 ? MR1 : MR2;
+    return static_cast<int>((rows + mr - 1) / mr);
+  }, s_pref, s_tmp);
+  const int n_nb = (a.Nout + NB - 1) / NB;
+  const StreamPlan pl = stream_plan(total_m * n_nb, xcd, nslots, a.K / KCH, true);
+  if (pl.P <= 1 || j >= pl.rem) return;
+  const int u = pl.begin + pl.full + j;
+  const int g = find_group(s_pref, n_groups, u / n_nb);
+  const int mg = s_pref[g + 1] - s_pref[g];
+  const int uu = u - s_pref[g] * n_nb;
+  const int nb = uu / mg, rb = uu % mg;
+  const int MR = group_rows(a, g) <= MR1 ? MR1 : MR2;
+  const TileView<uint16_t> v = tile_view<uint16_t>(a, g, rb, MR);
+  const int n0 = nb * NB;
+  const float *pieces = sp.rem + static_cast<int64_t>(j * pl.P * kXcds + xcd) * kStreamRemTile;
+  for (int e = q * blockDim.x + threadIdx.x; e < MR * (NB / 4); e += kFinishPerUnit * blockDim.x) {
+    const int r = e / (NB / 4), f = (e % (NB / 4)) * 4;
+    const int64_t lr = v.row0 + r;
+    const int n = n0 + f;
+    if (lr >= v.rows || n >= a.Nout) continue;
+    // piece kp of unit j sits at workgroup slot j*P + kp of this XCD; all of
+    // an element's pieces are loaded before they are added in piece order
+    float4 t[8];
+#pragma unroll
+    for (int kp = 0; kp < 8; ++kp)
+      if (kp < pl.P)
+        t[kp] = *reinterpret_cast<const float4 *>(
+            pieces + static_cast<int64_t>(kp) * kXcds * kStreamRemTile + static_cast<int64_t>(r) * NB + f);
+    float4 s = t[0];
+#pragma unroll
+    for (int kp = 1; kp < 8; ++kp)
+      if (kp < pl.P) {
+        s.x += t[kp].x;
+        s.y += t[kp].y;
+        s.z += t[kp].z;
+        s.w += t[kp].w;
+      }
+    float o[4] = {s.x, s.y, s.z, s.w};
+    if (v.bias) {
+      const uint2 bq = *reinterpret_cast<const uint2 *>(v.bias + n);
+      o[0] += __uint_as_float(bq.x << 16);
+      o[1] += __uint_as_float(bq.x & 0xFFFF0000u);
+      o[2] += __uint_as_float(bq.y << 16);
+      o[3] += __uint_as_float(bq.y & 0xFFFF0000u);
+    }
+    if (EPI == kEpiBiasSilu)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) o[q] = silu_fast(o[q]);
+    uint2 packed;
+    packed.x = pack_bf16x2(o[0], o[1]);
+    packed.y = pack_bf16x2(o[2], o[3]);
+    *reinterpret_cast<uint2 *>(v.C + (v.out_base + lr) * a.Nout + n) = packed;
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -1510,17 +1652,24 @@ int64_t split_rows(const GemmGroups &g) {
 template <int MB, int NTB, int S, int NTB2 = 0>
 hipError_t launch_bf16_stream(const GemmArgs &a, const GemmGroups &g, Epilogue epi, int per_cu,
                               hipStream_t s) {
+  // scratch: [0, 256) the split the kernel chose; then the last-round piece
+  // tiles; then, for small products, the uniform K-split partial sums
   StreamSplit sp{};
   sp.ks_cap = 1;
   const int64_t prows = split_rows(g);
-  if (g.split_ws && prows <= kSplitMaxRows && g.split_bytes > 256) {
-    const int64_t per = prows * g.Nout * static_cast<int64_t>(sizeof(float));
-    const int64_t cap = (static_cast<int64_t>(g.split_bytes) - 256) / per;
-    if (cap > 1) {
-      sp.ks_used = static_cast<int *>(g.split_ws);
-      sp.partial = reinterpret_cast<float *>(static_cast<char *>(g.split_ws) + 256);
-      sp.part_rows = g.max_routed_rows;
-      sp.ks_cap = static_cast<int>(cap < kSplitCap ? cap : kSplitCap);
+  const int64_t head = 256 + kStreamRemBytes;
+  if (g.split_ws && static_cast<int64_t>(g.split_bytes) >= head) {
+    char *ws = static_cast<char *>(g.split_ws);
+    sp.ks_used = reinterpret_cast<int *>(ws);
+    sp.rem = reinterpret_cast<float *>(ws + 256);
+    if (prows <= kSplitMaxRows) {
+      const int64_t per = prows * g.Nout * static_cast<int64_t>(sizeof(float));
+      const int64_t cap = (static_cast<int64_t>(g.split_bytes) - head) / per;
+      if (cap > 1) {
+        sp.partial = reinterpret_cast<float *>(ws + head);
+        sp.part_rows = g.max_routed_rows;
+        sp.ks_cap = static_cast<int>(cap < kSplitCap ? cap : kSplitCap);
+      }
     }
   }
   const unsigned grid =
@@ -1532,12 +1681,22 @@ hipError_t launch_bf16_stream(const GemmArgs &a, const GemmGroups &g, Epilogue e
     hipLaunchKernelGGL((grouped_gemm_bf16_stream_kernel<MB, NTB, NTB2, S, kEpiBias>), dim3(grid),
                        dim3(256), 0, s, a, sp);
   hipError_t e = hipGetLastError();
-  if (e != hipSuccess || sp.ks_cap <= 1) return e;
-  const dim3 rgrid(static_cast<unsigned>((g.Nout / 4 + 255) / 256), static_cast<unsigned>(prows));
+  if (e != hipSuccess || !sp.ks_used) return e;
+  // one workgroup per possible last-round unit (at most half of each XCD's
+  // workgroups), and enough for a uniform K-split sum
+  int64_t fgrid = static_cast<int64_t>(kXcds) * ((grid / kXcds) / 2 > 0 ? (grid / kXcds) / 2 : 1) *
+                  kFinishPerUnit;
+  if (sp.ks_cap > 1) {
+    const int64_t need = (prows * (g.Nout / 4) + 255) / 256;
+    const int64_t cap_blocks = need < 4096 ? need : 4096;
+    if (cap_blocks > fgrid) fgrid = cap_blocks;
+  }
   if (epi == kEpiBiasSilu)
-    hipLaunchKernelGGL((stream_reduce_kernel<kEpiBiasSilu>), rgrid, dim3(256), 0, s, a, sp);
+    hipLaunchKernelGGL((stream_finish_kernel<MB, NTB, NTB2, kEpiBiasSilu>), dim3(static_cast<unsigned>(fgrid)),
+                       dim3(256), 0, s, a, sp, static_cast<int>(grid));
   else
-    hipLaunchKernelGGL((stream_reduce_kernel<kEpiBias>), rgrid, dim3(256), 0, s, a, sp);
+    hipLaunchKernelGGL((stream_finish_kernel<MB, NTB, NTB2, kEpiBias>), dim3(static_cast<unsigned>(fgrid)),
+                       dim3(256), 0, s, a, sp, static_cast<int>(grid));
   return hipGetLastError();
 }
 
@@ -1593,12 +1752,13 @@ hipError_t launch_bf16_rs(const GemmArgs &a, const GemmGroups &g, Epilogue epi, 
 }  // namespace
 
 size_t grouped_gemm_split_bytes(const GemmGroups &g) {
-  // K split of the stream kernel (small products), or of the last round of
-  // the 256x256 kernel (one 256x256 float32 tile per workgroup)
+  // the stream kernel: its split word, the last-round piece tiles and, for
+  // small products, K-split partial sums; the 256x256 kernel: one float32
+  // 256x256 tile per workgroup of its split last round
   const int64_t prows = split_rows(g);
-  const size_t stream = prows <= kSplitMaxRows
-                            ? 256 + sizeof(float) * static_cast<size_t>(kSplitCap) * prows * g.Nout
-                            : 0;
+  size_t stream = 256 + static_cast<size_t>(kStreamRemBytes);
+  if (prows <= kSplitMaxRows)
+    stream += sizeof(float) * static_cast<size_t>(kSplitCap) * prows * g.Nout;
   const size_t rs = static_cast<size_t>(kRsMaxBlocks) * kRsPieceBytes;
   return stream > rs ? stream : rs;
 }

@@ -116,8 +116,9 @@ def test_workspace_sizes_grow_with_the_layer(B):
 def test_grouped_ffn_split_workspace_size(B):
     bf = B.config(128, 7168, 256, 8, 1, 2048, "bf16")
     n = B.grouped_ffn_workspace_size(bf, 256, 1024)
-    # one int, then up to 8 float32 partial sums of every row x max(d, f)
-    assert n == 256 + 4 * 8 * 1024 * 7168
+    # one int, the last-round piece tiles (256 workgroups x 128 x 256 float32),
+    # then up to 8 float32 partial sums of every row x max(d, f)
+    assert n == 256 + 256 * 128 * 256 * 4 + 4 * 8 * 1024 * 7168
     # large products only split the last round of 256x256 tiles: one float32
     # tile per workgroup of up to 256
     assert B.grouped_ffn_workspace_size(bf, 256, 1 << 20) == 256 * 256 * 256 * 4
