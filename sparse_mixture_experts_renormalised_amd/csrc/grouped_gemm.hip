@@ -23,14 +23,15 @@
 // Kernels, chosen by operand type and group size (rows per expert):
 //   * 256x256 tiles (groups above 128 rows): MFMA v_mfma_f32_32x32x16_bf16
 //     with fp32 accumulators, operands copied global -> two swizzled LDS
-//     buffers two K-steps ahead with the copies spread among the MFMAs, tail
-//     tiles of 1..128 rows at half height, and a K (or M) split of the last
-//     partial round of tiles;
+//     buffers two K-steps ahead with the copies spread among the MFMAs
+//     (addressed from wave-uniform SGPR bases when offsets fit in 32 bits),
+//     tail tiles of 1..128 rows at half height, and a K (or M) split of the
+//     last partial round of tiles;
 //   * a stream kernel (groups of up to 128 rows, bound by the weight stream):
 //     weights and activations copied straight into a ring of LDS stages
 //     several chunks ahead, non-temporal for weights read once, units of one
-//     or two heights, and a K split when a product has too few units to fill
-//     the chip (decode);
+//     or two heights, a K split when a product has too few units to fill
+//     the chip (decode), and otherwise a K split of the last round's units;
 //   * fp32 operands: a plain LDS-tiled VALU kernel (4x4 register tile).
 // The weight tile is the MFMA's first operand, so each lane ends up holding
 // four consecutive output features of one row and the epilogues store packed
