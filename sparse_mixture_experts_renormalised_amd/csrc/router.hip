@@ -175,17 +175,25 @@ __global__ __launch_bounds__(256) void router_logits_kernel(
 }
 
 // Short batches (and narrow routers) have few logits, each a long chain, so
-// the LDS tiles above cannot keep enough memory traffic in flight.  Here a
-// workgroup of 128 threads owns 16 tokens x 8 experts, one logit per thread,
-// and streams 64-wide k-chunks of x (bf16, as stored) and W (float32) into a
-// ring of S LDS stages with global-to-LDS copies issued S-1 chunks ahead.  A
-// copy instruction moves 1 KB: 8 rows of x or 4 rows of W.  x rows are 128
-// bytes of 8 pieces; piece c of row r sits at c ^ ((r >> 1) & 7), so the 16
-// tokens read by a 16-lane group hit distinct banks; the W row of such a
-// group is one broadcast address.
+// their time is the chain itself: one dependent float32 multiply-add costs
+// about 5 cycles on MI355X whatever else the wave issues in between, which is
+// 16 us for a 7168-long chain.  Here one logit is one lane's chain: a wave
+// owns 64 tokens (one per lane) and one expert, a workgroup E experts of the
+// same 64 tokens.  The expert's W row is the same for every lane, so it comes
+// through the scalar cache into SGPRs (s_load, read as a v_fmac operand) and
+// never touches LDS or vector registers; only x goes through LDS.  x (bf16,
+// as stored) streams in 64-wide k-chunks through a ring of S stages filled by
+// global-to-LDS copies S-1 chunks ahead (a copy instruction moves 8 rows of
+// 128 bytes; piece c of row r sits at c ^ ((r >> 1) & 7), so the 64 rows read
+// by one instruction spread over the banks).  Each stage also takes one copy
+// of the wave's W chunk into a landing slot that nothing reads: it brings the
+// row into L2 ahead of the scalar loads, which would otherwise wait on HBM.
+// A chunk is consumed in two halves of 32 k; the x fragment and the 32 W
+// values of the next half are requested before the current half's chain, so
+// the wait for them (LDS reads and scalar loads share one counter, and scalar
+// loads return out of order, so only a full wait is exact) falls one half
+// later.
 namespace ring {
-constexpr int NT = 128, BT = 16, BE = 8, KC = 64;
-
 __device__ __forceinline__ uint32_t lds_addr(const void *p) {
   return static_cast<uint32_t>(
       reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) const void *)p));
@@ -220,91 +228,142 @@ __device__ __forceinline__ void wait_chunks(int n) {
     wait_chunks<LPS, MAXN - 1>(n);
   }
 }
+
+// wait_and_barrier<n * LPS> for a run-time n in [0, MAXN]; n = 0 is the
+// unconditional last case, so every path waits (the compiler then knows the
+// LDS and scalar-load counter is clear after it).
+template <int LPS, int MAXN>
+__device__ __forceinline__ void wait_upto(int n) {
+  if constexpr (MAXN <= 0) {
+    wait_and_barrier<0>();
+  } else {
+    if (n >= MAXN) {
+      wait_and_barrier<MAXN * LPS>();
+      return;
+    }
+    wait_upto<LPS, MAXN - 1>(n);
+  }
+}
+
+// LDS and scalar loads issued so far have returned.
+__device__ __forceinline__ void wait_lgkm() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(0xC07F);
+  asm volatile("" ::: "memory");
+}
 }  // namespace ring
 
-template <int S>
-__global__ __launch_bounds__(128) void router_logits_ring_kernel(
+namespace swv {
+constexpr int BT = 64, KC = 64, XS = BT * KC * 2;   // tokens per tile, k per chunk, x bytes per stage
+}
+
+template <int E, int S>
+__global__ __launch_bounds__(64 * E) void router_logits_sw_kernel(
     const uint16_t *__restrict__ x, const float *__restrict__ w, const float *__restrict__ bias,
     float *__restrict__ logits, int64_t T, int d, int N) {
-  using namespace ring;
-  constexpr int XB = BT * KC * 2;                // bytes of x per stage (2 KB)
-  constexpr int WB = BE * KC * 4;                // bytes of W per stage (2 KB)
-  constexpr int STAGE = XB + WB;
-  constexpr int LPS = 2;                         // copies per wave per stage
-  static_assert((S - 2) * LPS <= 63, "vmcnt range");
+  using namespace swv;
+  static_assert(E == 1 || E == 2 || E == 4, "experts per workgroup");
+  constexpr int XC = 8 / E;                  // x copies per wave per stage
+  constexpr int STAGE = XS + E * 1024;       // x tile + one landing slot per wave
+  constexpr int LPS = XC + 1;                // copies per wave per stage
+  static_assert(S >= 4 && (S - 2) * LPS <= 63, "vmcnt range");
+  static_assert(S * STAGE <= 160 * 1024, "LDS");
   __shared__ __attribute__((aligned(16))) uint8_t s_ring[S * STAGE];
 
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = uniform(tid >> 6);
-  const int tt = tid & 15, te = tid >> 4;
+  const int lane = threadIdx.x & 63;
+  const int wave = uniform(static_cast<int>(threadIdx.x >> 6));
   const int64_t t0 = static_cast<int64_t>(blockIdx.x) * BT;
-  const int e0 = blockIdx.y * BE;
-  const uint32_t ring0 = uniform(static_cast<int>(lds_addr(s_ring)));
+  const int e_out = static_cast<int>(blockIdx.y) * E + wave;
+  const int e = uniform(min(e_out, N - 1));  // past N: a duplicate chain, not stored
+  const uint32_t ring0 = uniform(static_cast<int>(ring::lds_addr(s_ring)));
 
-  // wave w copies x rows 8w .. 8w+7 and W rows 4w .. 4w+3 of every chunk
-  const int xr = 8 * wave + (lane >> 3);
-  int64_t xt = t0 + xr;
-  if (xt >= T) xt = T - 1;
-  const uint16_t *x_src = x + xt * d + ((lane & 7) ^ ((xr >> 1) & 7)) * 8;
-  const int wr = 4 * wave + (lane >> 4);
-  const int we = min(e0 + wr, N - 1);
-  const float *w_src = w + static_cast<int64_t>(we) * d + (lane & 15) * 4;
+  // copy j of this wave moves x rows 8 (wave XC + j) .. +7 of every chunk
+  const uint16_t *x_src[XC];
+#pragma unroll
+  for (int j = 0; j < XC; ++j) {
+    const int r = 8 * (wave * XC + j) + (lane >> 3);
+    int64_t xt = t0 + r;
+    if (xt >= T) xt = T - 1;
+    x_src[j] = x + xt * d + ((lane & 7) ^ ((r >> 1) & 7)) * 8;
+  }
+  const float *w_row = w + static_cast<int64_t>(e) * d;
+  const float *w_touch = w_row + (lane & 15) * 4;   // the chunk's 256 bytes (each 4 times)
+  // the constant address space lets uniform loads of W become scalar loads
+  using cfloat = __attribute__((address_space(4))) const float;
+  cfloat *w_sc = (cfloat *)w_row;
   auto issue = [&](int c, int st) {
     const uint32_t base = ring0 + static_cast<uint32_t>(st) * STAGE;
-    dma16(x_src + c * KC, base + wave * 1024);
-    dma16(w_src + c * KC, base + XB + wave * 1024);
+#pragma unroll
+    for (int j = 0; j < XC; ++j) ring::dma16(x_src[j] + c * KC, base + (wave * XC + j) * 1024);
+    ring::dma16(w_touch + c * KC, base + XS + wave * 1024);
   };
 
   const int nch = d / KC;
+  const uint8_t *xrow = s_ring + lane * (KC * 2);
+  const int sw = (lane >> 1) & 7;
+  // operands of one half chunk: 32 bf16 of the lane's token, 32 W values
+  uint4 xa[4], xb[4];
+  float wa[32], wb[32];
+  auto fetch = [&](int c, int h, uint4 (&xq)[4], float (&wv)[32]) {
+    const uint8_t *st = xrow + (c % S) * STAGE;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      xq[i] = *reinterpret_cast<const uint4 *>(st + (((4 * h + i) ^ sw) << 4));
+    cfloat *wp = w_sc + c * KC + h * 32;
+#pragma unroll
+    for (int i = 0; i < 32; ++i) wv[i] = wp[i];
+  };
   float acc = 0.0f;
-  // a chunk's operands are read from LDS into registers before its chain of
-  // multiply-adds, so the LDS latency is paid once per chunk
-  uint4 xa[KC / 8];
-  float4 wa[KC / 4];
-  auto read = [&](int c, uint4 (&xq)[KC / 8], float4 (&wv)[KC / 4]) {
-    const uint8_t *st = s_ring + (c % S) * STAGE;
-    const uint16_t *xs = reinterpret_cast<const uint16_t *>(st) + tt * KC;
-    const float *ws = reinterpret_cast<const float *>(st + XB) + te * KC;
+  auto chain = [&](const uint4 (&xq)[4], const float (&wv)[32]) {
 #pragma unroll
-    for (int pc = 0; pc < KC / 8; ++pc) {
-      xq[pc] = *reinterpret_cast<const uint4 *>(xs + ((pc ^ ((tt >> 1) & 7)) << 3));
-      wv[2 * pc] = *reinterpret_cast<const float4 *>(ws + pc * 8);
-      wv[2 * pc + 1] = *reinterpret_cast<const float4 *>(ws + pc * 8 + 4);
+    for (int i = 0; i < 4; ++i) {
+      const uint4 q = xq[i];
+      acc = __builtin_fmaf(__uint_as_float(q.x << 16), wv[8 * i + 0], acc);
+      acc = __builtin_fmaf(__uint_as_float(q.x & 0xFFFF0000u), wv[8 * i + 1], acc);
+      acc = __builtin_fmaf(__uint_as_float(q.y << 16), wv[8 * i + 2], acc);
+      acc = __builtin_fmaf(__uint_as_float(q.y & 0xFFFF0000u), wv[8 * i + 3], acc);
+      acc = __builtin_fmaf(__uint_as_float(q.z << 16), wv[8 * i + 4], acc);
+      acc = __builtin_fmaf(__uint_as_float(q.z & 0xFFFF0000u), wv[8 * i + 5], acc);
+      acc = __builtin_fmaf(__uint_as_float(q.w << 16), wv[8 * i + 6], acc);
+      acc = __builtin_fmaf(__uint_as_float(q.w & 0xFFFF0000u), wv[8 * i + 7], acc);
     }
+    // keeps the chain ahead of the waits and copies that follow it
+    asm volatile("" : "+v"(acc));
   };
-  auto chain = [&](const uint4 (&xq)[KC / 8], const float4 (&wv)[KC / 4]) {
-#pragma unroll
-    for (int pc = 0; pc < KC / 8; ++pc) {
-      const uint4 q = xq[pc];
-      const float4 u = wv[2 * pc], v = wv[2 * pc + 1];
-      acc = __builtin_fmaf(__uint_as_float(q.x << 16), u.x, acc);
-      acc = __builtin_fmaf(__uint_as_float(q.x & 0xFFFF0000u), u.y, acc);
-      acc = __builtin_fmaf(__uint_as_float(q.y << 16), u.z, acc);
-      acc = __builtin_fmaf(__uint_as_float(q.y & 0xFFFF0000u), u.w, acc);
-      acc = __builtin_fmaf(__uint_as_float(q.z << 16), v.x, acc);
-      acc = __builtin_fmaf(__uint_as_float(q.z & 0xFFFF0000u), v.y, acc);
-      acc = __builtin_fmaf(__uint_as_float(q.w << 16), v.z, acc);
-      acc = __builtin_fmaf(__uint_as_float(q.w & 0xFFFF0000u), v.w, acc);
-    }
-  };
+
   const int pro = min(S - 1, nch);
-  for (int c = 0; c < pro; ++c) issue(c, c % S);
+  for (int c = 0; c < pro; ++c) issue(c, c);
+  ring::wait_upto<LPS, S - 2>(min(S - 2, nch - 1));   // chunk 0 has landed
+  fetch(0, 0, xa, wa);
   for (int c = 0; c < nch; ++c) {
-    // copies of chunks c+1 .. min(c+S-2, nch-1) may stay in flight
-    const int later = min(S - 2, nch - 1 - c);
-    if (later == S - 2) wait_and_barrier<(S - 2) * LPS>();
-    else wait_chunks<LPS, S - 3>(later);
-    if (c + S - 1 < nch) issue(c + S - 1, (c + S - 1) % S);
-    read(c, xa, wa);
+    // first half of chunk c while its second half is requested
+    ring::wait_lgkm();
+    __builtin_amdgcn_sched_barrier(0);
+    fetch(c, 1, xb, wb);
+    __builtin_amdgcn_sched_barrier(0);
     chain(xa, wa);
+    __builtin_amdgcn_sched_barrier(0);
+    // second half while the next chunk's first half is requested; chunk c+1
+    // must have landed first, and its arrival frees the stage of chunk c-1
+    // for chunk c+S-1.  After the last chunk the request repeats it, which
+    // keeps the register roles fixed (a conditional request would add copies
+    // and waits).
+    ring::wait_lgkm();
+    if (c + 1 < nch) {
+      ring::wait_upto<LPS, S - 3>(min(S - 3, nch - c - 2));
+      if (c + S - 1 < nch) issue(c + S - 1, (c + S - 1) % S);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    fetch(min(c + 1, nch - 1), 0, xa, wa);
+    __builtin_amdgcn_sched_barrier(0);
+    chain(xb, wb);
+    __builtin_amdgcn_sched_barrier(0);
   }
-  const int64_t t = t0 + tt;
-  const int e = e0 + te;
-  if (t < T && e < N) {
+  const int64_t t = t0 + lane;
+  if (t < T && e_out < N) {
     float v = acc;
-    if (bias) v = v + bias[e];
-    logits[t * N + e] = v;
+    if (bias) v = v + bias[e_out];
+    logits[t * N + e_out] = v;
   }
 }
 
@@ -565,7 +624,8 @@ hipError_t launch_router_logits(bool bf16, const void *x, const float *w, const 
   if (T <= 0) return hipSuccess;
   // Shapes measured on MI355X.  bf16 tokens with d a multiple of 64: few
   // 16 x 16 output tiles in all (a decode batch, a narrow router) go to the
-  // LDS-ring kernel, one logit per thread, the rest to the matrix cores.
+  // one-logit-per-lane kernel with W in scalar registers, the rest to the
+  // matrix cores.
   // float32 tokens and other d use the register-tiled kernel: 64x32 blocks
   // with 4x2 logits per thread for wide routers over many tokens, 32x32 with
   // 2x2 for mid-sized ones (both loading two chunks ahead), 64x8 with 2x1
@@ -587,11 +647,19 @@ hipError_t launch_router_logits(bool bf16, const void *x, const float *w, const 
     const int64_t tiles = ((T + 15) / 16) * ((N + 15) / 16);
     if (tiles <= 512) {
       // few 16 x 16 output tiles: a matrix-core chain per tile would be bound
-      // by the latency of its dependent multiplies, so one logit per thread
-      const dim3 grid(static_cast<unsigned>((T + ring::BT - 1) / ring::BT),
-                      static_cast<unsigned>((N + ring::BE - 1) / ring::BE));
-      hipLaunchKernelGGL((router_logits_ring_kernel<12>), grid, dim3(ring::NT), 0, s,
-                         static_cast<const uint16_t *>(x), w, bias, logits, T, d, N);
+      // by the latency of its dependent multiplies, so one logit per lane
+      const unsigned tb = static_cast<unsigned>((T + swv::BT - 1) / swv::BT);
+      const uint16_t *xb = static_cast<const uint16_t *>(x);
+      if (N == 1)
+        hipLaunchKernelGGL((router_logits_sw_kernel<1, 8>), dim3(tb, 1), dim3(64), 0, s, xb, w,
+                           bias, logits, T, d, N);
+      else if (N == 2)
+        hipLaunchKernelGGL((router_logits_sw_kernel<2, 8>), dim3(tb, 1), dim3(128), 0, s, xb, w,
+                           bias, logits, T, d, N);
+      else
+        hipLaunchKernelGGL((router_logits_sw_kernel<4, 8>),
+                           dim3(tb, static_cast<unsigned>((N + 3) / 4)), dim3(256), 0, s, xb, w,
+                           bias, logits, T, d, N);
       return hipGetLastError();
     }
 #define MOE_ROUTER_MFMA(AT, AE, TT, TE, S)                                                      \

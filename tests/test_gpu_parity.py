@@ -100,11 +100,21 @@ ROUTE_CASES = [W.get_workload(n) for n in W.WORKLOADS] + [
                       dtype="f32"),
     W.custom_workload("T1_K1", T=1, d_model=16, n_routed=3, top_k=1, n_shared=0, d_ff=16,
                       dtype="f32"),
-    # the LDS-ring logits kernel with ragged tails, then one case per launch
-    # shape of the matrix-core logits kernel, each with ragged token and
-    # expert tails: 32 x 32, 64 x 64 (ring of 4 stages wrapping over 5
-    # k-stages) and 64 tokens x 16 experts
+    # the one-logit-per-lane logits kernel (W in scalar registers) with ragged
+    # tails, with one, two and four experts per workgroup (N = 3 leaves one
+    # wave without an expert) and a k-ring that wraps (19 chunks, 8 stages);
+    # then one case per launch shape of the matrix-core logits kernel, each
+    # with ragged token and expert tails: 32 x 32, 64 x 64 (ring of 4 stages
+    # wrapping over 5 k-stages) and 64 tokens x 16 experts
     W.custom_workload("ring_ragged", T=203, d_model=128, n_routed=40, top_k=6, n_shared=0,
+                      d_ff=64, dtype="bf16", router_bias="gauss", router_bias_var=0.5),
+    W.custom_workload("sw_N1", T=70, d_model=128, n_routed=1, top_k=1, n_shared=0, d_ff=64,
+                      dtype="bf16"),
+    W.custom_workload("sw_N2", T=300, d_model=192, n_routed=2, top_k=2, n_shared=0, d_ff=64,
+                      dtype="bf16", router_bias="gauss", router_bias_var=0.5),
+    W.custom_workload("sw_N3", T=65, d_model=256, n_routed=3, top_k=2, n_shared=0, d_ff=64,
+                      dtype="bf16"),
+    W.custom_workload("sw_long_k", T=64, d_model=1216, n_routed=6, top_k=2, n_shared=0,
                       d_ff=64, dtype="bf16", router_bias="gauss", router_bias_var=0.5),
     W.custom_workload("mfma_32x32", T=1500, d_model=192, n_routed=100, top_k=8, n_shared=0,
                       d_ff=64, dtype="bf16"),
