@@ -1427,13 +1427,17 @@ __device__ __forceinline__ void reduce_parts(const GemmArgs &a, const StreamSpli
 }
 
 // After a stream launch of grid workgroups: with a uniform K split, the sum
-// of every row's parts; otherwise workgroups (xcd, j, 0 .. kFinishPerUnit-1)
-// of this launch add the pieces of the j-th last-round unit of that XCD, if
-// the launch split it (stream_plan on the same device counts decides exactly
-// as the stream kernel did).
-constexpr int kFinishPerUnit = 16;
+// of every row's parts; otherwise workgroups (xcd, j, 0 .. fpu-1) of this
+// launch add the pieces of the j-th last-round unit of that XCD, if the
+// launch split it (stream_plan on the same device counts decides exactly as
+// the stream kernel did).  fpu = workgroups per unit, one per 512 four-float
+// elements of the unit, so a launch that split nothing is a small grid that
+// exits at once.
+constexpr int kFinishMaxPerUnit = 16;
+constexpr int kFinishMaxUniform = 512;   // workgroups of the uniform K-split sum
 template <int MB, int NTB, int NTB2, int EPI>
-__global__ __launch_bounds__(256) void stream_finish_kernel(GemmArgs a, StreamSplit sp, int grid) {
+__global__ __launch_bounds__(256) void stream_finish_kernel(GemmArgs a, StreamSplit sp, int grid,
+                                                            int fpu) {
   using namespace st;
   const int ks = *sp.ks_used;
   if (ks > 1) {
@@ -1449,6 +1453,7 @@ __global__ __launch_bounds__(256) void stream_finish_kernel(GemmArgs a, StreamSp
   const int xcd = blockIdx.x % kXcds;
   const int j = (blockIdx.x / kXcds) % (nslots / 2 > 0 ? nslots / 2 : 1);
   const int q = (blockIdx.x / kXcds) / (nslots / 2 > 0 ? nslots / 2 : 1);
+  if (q >= fpu) return;                    // a workgroup of the uniform-sum grid only
   if (j >= sp.ks_used[16 + xcd]) return;   // not a split unit of this launch
   constexpr int MR1 = 32 * NTB, MR2 = 32 * (NTB2 > NTB ? NTB2 : NTB);
   constexpr int NB = 4 * 32 * MB;
@@ -1472,7 +1477,7 @@ __global__ __launch_bounds__(256) void stream_finish_kernel(GemmArgs a, StreamSp
   const TileView<uint16_t> v = tile_view<uint16_t>(a, g, rb, MR);
   const int n0 = nb * NB;
   const float *pieces = sp.rem + static_cast<int64_t>(j * pl.P * kXcds + xcd) * kStreamRemTile;
-  for (int e = q * blockDim.x + threadIdx.x; e < MR * (NB / 4); e += kFinishPerUnit * blockDim.x) {
+  for (int e = q * blockDim.x + threadIdx.x; e < MR * (NB / 4); e += fpu * blockDim.x) {
     const int r = e / (NB / 4), f = (e % (NB / 4)) * 4;
     const int64_t lr = v.row0 + r;
     const int n = n0 + f;
@@ -1683,21 +1688,24 @@ hipError_t launch_bf16_stream(const GemmArgs &a, const GemmGroups &g, Epilogue e
                        dim3(256), 0, s, a, sp);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || !sp.ks_used) return e;
-  // one workgroup per possible last-round unit (at most half of each XCD's
-  // workgroups), and enough for a uniform K-split sum
-  int64_t fgrid = static_cast<int64_t>(kXcds) * ((grid / kXcds) / 2 > 0 ? (grid / kXcds) / 2 : 1) *
-                  kFinishPerUnit;
+  // fpu workgroups per possible last-round unit (at most half of each XCD's
+  // workgroups), one per 512 four-float elements of the largest unit; at
+  // least enough for the uniform K-split sum's grid-stride loop
+  constexpr int kUnitElems = 32 * (NTB2 > NTB ? NTB2 : NTB) * (4 * 32 * MB) / 4;
+  constexpr int fpu = kUnitElems / 512 < 1 ? 1
+                      : (kUnitElems / 512 > kFinishMaxPerUnit ? kFinishMaxPerUnit : kUnitElems / 512);
+  int64_t fgrid = static_cast<int64_t>(kXcds) * ((grid / kXcds) / 2 > 0 ? (grid / kXcds) / 2 : 1) * fpu;
   if (sp.ks_cap > 1) {
     const int64_t need = (prows * (g.Nout / 4) + 255) / 256;
-    const int64_t cap_blocks = need < 4096 ? need : 4096;
+    const int64_t cap_blocks = need < kFinishMaxUniform ? need : kFinishMaxUniform;
     if (cap_blocks > fgrid) fgrid = cap_blocks;
   }
   if (epi == kEpiBiasSilu)
     hipLaunchKernelGGL((stream_finish_kernel<MB, NTB, NTB2, kEpiBiasSilu>), dim3(static_cast<unsigned>(fgrid)),
-                       dim3(256), 0, s, a, sp, static_cast<int>(grid));
+                       dim3(256), 0, s, a, sp, static_cast<int>(grid), fpu);
   else
     hipLaunchKernelGGL((stream_finish_kernel<MB, NTB, NTB2, kEpiBias>), dim3(static_cast<unsigned>(fgrid)),
-                       dim3(256), 0, s, a, sp, static_cast<int>(grid));
+                       dim3(256), 0, s, a, sp, static_cast<int>(grid), fpu);
   return hipGetLastError();
 }
 
