@@ -555,9 +555,17 @@ __global__ __launch_bounds__(64 * AT * AE) void router_logits_mfma_kernel(
   }
 }
 
-// Key order: a beats b iff a.v > b.v, or equal values and a.i < b.i.
-__device__ __forceinline__ bool key_better(float va, int ia, float vb, int ib) {
-  return va > vb || (va == vb && ia < ib);
+// Key order: a beats b iff a.v > b.v, or equal values and a.i < b.i.  As one
+// 64-bit integer whose unsigned order is that order: the float's bits mapped
+// to an order-preserving unsigned value (-0 taken as +0, so that equal values
+// tie as they compare), above the complement of the expert id, so that the
+// lower id wins a tie.  0 is below every key (an entry already taken or past
+// N); -inf maps above it.
+__device__ __forceinline__ uint64_t pack_key(float v, int e) {
+  uint32_t u = __float_as_uint(v);
+  if (u == 0x80000000u) u = 0u;
+  u = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+  return (static_cast<uint64_t>(u) << 32) | static_cast<uint32_t>(~e);
 }
 
 template <int J>   // J = ceil(N / 64) logits per lane
@@ -570,37 +578,37 @@ __global__ __launch_bounds__(256) void topk_gates_kernel(const float *__restrict
   const int64_t t = static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6);
   if (t >= T) return;
   const float *row = logits + t * N;
-  float v[J], key[J];
+  float v[J];
+  uint64_t key[J];
 #pragma unroll
   for (int j = 0; j < J; ++j) {
     const int e = lane + 64 * j;
-    v[j] = e < N ? row[e] : -__builtin_inff();
+    v[j] = e < N ? row[e] : 0.0f;
     // selection key: the logit, or (selection-only bias) fl32(logit + bias)
-    key[j] = (sel_bias && e < N) ? v[j] + sel_bias[e] : v[j];
+    key[j] = e < N ? pack_key(sel_bias ? v[j] + sel_bias[e] : v[j], e) : 0ull;
   }
-  uint32_t taken = 0;
   float kept_v = -__builtin_inff();   // lane k keeps slot k's (unbiased) logit
   int kept_i = 0;
   for (int k = 0; k < K; ++k) {
-    float bk = -__builtin_inff(), bv = 0.0f;
-    int bi = 0x7FFFFFFF;
+    // the lane's best remaining key and its logit, then the wave's best
+    uint64_t best = 0ull;
+    float bv = 0.0f;
 #pragma unroll
-    for (int j = 0; j < J; ++j) {
-      const int e = lane + 64 * j;
-      if (e < N && !((taken >> j) & 1u) && key_better(key[j], e, bk, bi)) {
-        bk = key[j];
+    for (int j = 0; j < J; ++j)
+      if (key[j] > best) {
+        best = key[j];
         bv = v[j];
-        bi = e;
       }
-    }
 #pragma unroll
     for (int off = 32; off >= 1; off >>= 1) {
-      const float ok = __shfl_xor(bk, off);
-      const float ov = __shfl_xor(bv, off);
-      const int oi = __shfl_xor(bi, off);
-      if (key_better(ok, oi, bk, bi)) { bk = ok; bv = ov; bi = oi; }
+      const uint64_t o = __shfl_xor(best, off);
+      best = o > best ? o : best;
     }
-    if ((bi & 63) == lane) taken |= 1u << (bi >> 6);
+    const int bi = static_cast<int>(~static_cast<uint32_t>(best));
+    bv = __shfl(bv, bi & 63);          // the owning lane's best is the winner
+#pragma unroll
+    for (int j = 0; j < J; ++j)
+      if (bi == lane + 64 * j) key[j] = 0ull;   // taken
     if (lane == k) { kept_v = bv; kept_i = bi; }
   }
   // softmax over the K kept logits, shifted by their largest
