@@ -12,7 +12,8 @@
 // reduction tree is involved and the bits do not depend on the launch shape.
 //
 // Top-K: one wave per token, N logits spread over the lanes' registers, K
-// rounds of a wave-wide arg-max on the key (logit desc, expert id asc).  Gates
+// rounds of a wave-wide arg-max on the key (logit desc, expert id asc), packed
+// into one ordered 64-bit integer.  Gates
 // are the softmax over the K kept logits, which equals s_j / sum_TopK s_k of
 // the DeepSeekMoE explainer's gate equation.
 #include "moe_common.h"
