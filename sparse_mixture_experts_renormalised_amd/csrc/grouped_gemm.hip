@@ -527,8 +527,14 @@ __device__ __forceinline__ RsPlan rs_plan(int cnt, int nslots, int nk, bool can_
 
 // The 256-row m-tiles in two lists: tiles of 129..256 rows, and the last
 // tiles of groups that end with 1..128 rows (computed at half height).  Each
-// XCD takes an equal contiguous share of both lists, full tiles first, so
-// that its last, partly filled round is made of the cheap tail tiles.
+// XCD takes an equal contiguous share of the full list and every kXcds-th
+// tail (in column order).  A tail reads the same weight block as the full
+// tiles of its column, so it should run while that block is still cached:
+// when the XCD's last, partly filled round has at least as many workgroups
+// as the XCD has tails and is not split along K, tail q goes to workgroup q
+// in round q*R/H (R rounds, H tails), which spreads the tails over the rounds
+// in column order and gives each workgroup at most one; otherwise the tails
+// run after the full tiles (a K-split last round is cheapest made of tails).
 __device__ __forceinline__ bool rs_half_tail(int64_t rows) {
   const int64_t r = rows % rs::BM;
   return r != 0 && r <= rh::BM;
@@ -536,11 +542,14 @@ __device__ __forceinline__ bool rs_half_tail(int64_t rows) {
 
 struct RsTiles {
   int total_mf, total_mh, n_nt;   // m-tiles per list, n-tiles
-  int begin_f, cnt_f, begin_h, cnt_h;
+  int begin_f, cnt_f, cnt_h;      // this XCD's full tiles, and its count of tails
+  int xcd, nslots, R;             // R = rounds of the XCD's cnt_f + cnt_h items
+  bool inter;                     // tails interleaved (else after the full tiles);
+                                  // cleared by the caller when the plan splits K
 };
 
 __device__ __forceinline__ RsTiles rs_tiles(const GemmArgs &a, int *s_pref_f, int *s_pref_h,
-                                            int *s_tmp, int xcd) {
+                                            int *s_tmp, int xcd, int nslots) {
   RsTiles t;
   const int n_groups = a.n_routed + a.n_shared;
   t.total_mf = build_prefix<rs::NT>(n_groups, [&](int g) {
@@ -552,30 +561,66 @@ __device__ __forceinline__ RsTiles rs_tiles(const GemmArgs &a, int *s_pref_f, in
   }, s_pref_h, s_tmp);
   t.n_nt = (a.Nout + rs::BN - 1) / rs::BN;
   const int tot_f = t.total_mf * t.n_nt, tot_h = t.total_mh * t.n_nt;
-  const int part_f = (tot_f + kXcds - 1) / kXcds, part_h = (tot_h + kXcds - 1) / kXcds;
+  const int part_f = (tot_f + kXcds - 1) / kXcds;
   t.begin_f = xcd * part_f;
   t.cnt_f = max(0, min(tot_f, t.begin_f + part_f) - t.begin_f);
-  t.begin_h = xcd * part_h;
-  t.cnt_h = max(0, min(tot_h, t.begin_h + part_h) - t.begin_h);
+  t.cnt_h = tot_h > xcd ? (tot_h - xcd + kXcds - 1) / kXcds : 0;
+  t.xcd = xcd;
+  t.nslots = nslots;
+  const int L = t.cnt_f + t.cnt_h;
+  t.R = L > 0 ? (L + nslots - 1) / nslots : 0;
+  const int last = L - (t.R - 1) * nslots;   // items of the last round
+  t.inter = t.cnt_h > 0 && t.cnt_h <= last;
   return t;
 }
 
-// Item i of this XCD's list: group, m-tile within the group, n-tile.
+// Whether item i of this XCD's list is a tail (and which: q-th of the XCD).
+__device__ __forceinline__ bool rs_is_tail(const RsTiles &t, int i, int *q) {
+  if (!t.inter) {
+    *q = i - t.cnt_f;
+    return i >= t.cnt_f;
+  }
+  const int w = i % t.nslots;
+  *q = w;
+  return w < t.cnt_h && i / t.nslots == (w * t.R) / t.cnt_h;
+}
+
+// Tails of this XCD before item i (its full tiles before i are i minus that).
+__device__ __forceinline__ int rs_tails_before(const RsTiles &t, int i) {
+  if (!t.inter) return max(0, i - t.cnt_f);
+  int n = 0;
+  for (int q = 0; q < t.cnt_h; ++q) n += ((q * t.R) / t.cnt_h) * t.nslots + q < i;
+  return n;
+}
+
+// Item i of this XCD's list: group, m-tile within the group, n-tile, and
+// whether it is a tail (computed at half height).
 template <int GM>
-__device__ __forceinline__ void rs_tile_at(const GemmArgs &a, const RsTiles &t,
+__device__ __forceinline__ bool rs_tile_at(const GemmArgs &a, const RsTiles &t,
                                            const int *s_pref_f, const int *s_pref_h, int i,
                                            int *g, int *lm, int *nt) {
   const int n_groups = a.n_routed + a.n_shared;
-  int mt;
-  if (i < t.cnt_f) {
-    decode_tile<GM>(t.begin_f + i, t.total_mf, t.n_nt, &mt, nt);
+  int mt, q;
+  if (!rs_is_tail(t, i, &q)) {
+    decode_tile<GM>(t.begin_f + i - rs_tails_before(t, i), t.total_mf, t.n_nt, &mt, nt);
     *g = find_group(s_pref_f, n_groups, mt);
     *lm = mt - s_pref_f[*g];
-  } else {
-    decode_tile<GM>(t.begin_h + (i - t.cnt_f), t.total_mh, t.n_nt, &mt, nt);
-    *g = find_group(s_pref_h, n_groups, mt);
-    *lm = static_cast<int>((group_rows(a, *g) + rs::BM - 1) / rs::BM) - 1;
+    return false;
   }
+  decode_tile<GM>(t.xcd + kXcds * q, t.total_mh, t.n_nt, &mt, nt);
+  *g = find_group(s_pref_h, n_groups, mt);
+  *lm = static_cast<int>((group_rows(a, *g) + rs::BM - 1) / rs::BM) - 1;
+  return true;
+}
+
+// The k-th tail (want_tail) or full tile of this XCD's items from..end-1.
+__device__ __forceinline__ int rs_kth_item(const RsTiles &t, int from, int end, int k,
+                                           bool want_tail) {
+  for (int i = from; i < end; ++i) {
+    int q;
+    if (rs_is_tail(t, i, &q) == want_tail && k-- == 0) return i;
+  }
+  return end - 1;   // not reached: the caller counted the items
 }
 
 // Source addresses of this thread's 16-byte chunks of a 256x256 tile, from
@@ -868,19 +913,20 @@ void grouped_gemm_bf16_rs_kernel(GemmArgs a, RsSplit sp) {
   const int slot = blockIdx.x / kXcds;
   const int nslots = gridDim.x / kXcds;
   const int nk = a.K / BK;
-  const RsTiles t = rs_tiles(a, s_pref_f, s_pref_h, s_tmp, xcd);
+  RsTiles t = rs_tiles(a, s_pref_f, s_pref_h, s_tmp, xcd, nslots);
   const RsPlan pl = rs_plan(t.cnt_f + t.cnt_h, nslots, nk,
                             sp.partial != nullptr && static_cast<int>(gridDim.x) <= sp.max_blocks);
+  t.inter = t.inter && pl.P <= 1;
   f32x16_t acc[TN][TM];
   if constexpr (PIECE) {
     if (pl.P <= 1 || slot >= pl.rem * pl.P) return;
     int g, lm, nt;
-    rs_tile_at<GM>(a, t, s_pref_f, s_pref_h, pl.full + slot / pl.P, &g, &lm, &nt);
+    const bool tail = rs_tile_at<GM>(a, t, s_pref_f, s_pref_h, pl.full + slot / pl.P, &g, &lm, &nt);
     const TileView<uint16_t> v = tile_view<uint16_t>(a, g, lm, BM);
     const int k0 = (slot % pl.P) * pl.kper;
     const int kn = min(nk, k0 + pl.kper) - k0;
     float4 *dst = reinterpret_cast<float4 *>(sp.partial + static_cast<int64_t>(blockIdx.x) * (BM * BN));
-    if (pl.full + slot / pl.P >= t.cnt_f) {   // a half-height tail: its own register layout
+    if (tail) {   // a half-height tail: its own register layout
       f32x16_t acch[rh::TN][rh::TM];
       rh_tile(a, v, nt * BN, k0, kn, s_tile, tid, lane, wm, wn, acch);
 #pragma unroll
@@ -909,32 +955,29 @@ void grouped_gemm_bf16_rs_kernel(GemmArgs a, RsSplit sp) {
     // is split along M instead when it fits: each full-cost tile of that
     // round becomes two half-height tiles on two workgroups.
     const int cnt = t.cnt_f + t.cnt_h;
-    const int rem_f = max(0, t.cnt_f - pl.full);
+    const int rem_f = (cnt - pl.full) - (t.cnt_h - rs_tails_before(t, pl.full));
     const bool msplit = pl.P <= 1 && pl.rem > 0 && 2 * rem_f + (pl.rem - rem_f) <= nslots;
     const int end = pl.P > 1 || msplit ? pl.full : cnt;
-    const int end_f = min(end, t.cnt_f);
     int g, lm, nt;
-    int i = slot;
-    for (; i < end_f; i += nslots) {       // full-cost tiles
-      rs_tile_at<GM>(a, t, s_pref_f, s_pref_h, i, &g, &lm, &nt);
-      const TileView<uint16_t> v = tile_view<uint16_t>(a, g, lm, BM);
-      rs_tile<OFF32>(a, v, nt * BN, 0, nk, s_tile, tid, lane, wm, wn, acc);
-      rs_epilogue<EPI>(acc, a, v, nt * BN, s_tile, lane, wm, wn, tid);
-    }
-    for (; i < end; i += nslots) {         // half-height tail tiles
-      rs_tile_at<GM>(a, t, s_pref_f, s_pref_h, i, &g, &lm, &nt);
-      const TileView<uint16_t> v = tile_view<uint16_t>(a, g, lm, BM);
-      f32x16_t acch[rh::TN][rh::TM];
-      rh_tile(a, v, nt * BN, 0, nk, s_tile, tid, lane, wm, wn, acch);
-      rh_epilogue<EPI>(acch, a, v, nt * BN, s_tile, lane, wm, wn, tid);
+    for (int i = slot; i < end; i += nslots) {
+      if (rs_tile_at<GM>(a, t, s_pref_f, s_pref_h, i, &g, &lm, &nt)) {   // half-height tail
+        const TileView<uint16_t> v = tile_view<uint16_t>(a, g, lm, BM);
+        f32x16_t acch[rh::TN][rh::TM];
+        rh_tile(a, v, nt * BN, 0, nk, s_tile, tid, lane, wm, wn, acch);
+        rh_epilogue<EPI>(acch, a, v, nt * BN, s_tile, lane, wm, wn, tid);
+      } else {
+        const TileView<uint16_t> v = tile_view<uint16_t>(a, g, lm, BM);
+        rs_tile<OFF32>(a, v, nt * BN, 0, nk, s_tile, tid, lane, wm, wn, acc);
+        rs_epilogue<EPI>(acc, a, v, nt * BN, s_tile, lane, wm, wn, tid);
+      }
     }
     if (msplit && slot < 2 * rem_f + (pl.rem - rem_f)) {
       int item, upper = 0;
       if (slot < 2 * rem_f) {
-        item = pl.full + slot / 2;
+        item = rs_kth_item(t, pl.full, cnt, slot / 2, false);
         upper = slot & 1;
       } else {
-        item = pl.full + rem_f + (slot - 2 * rem_f);
+        item = rs_kth_item(t, pl.full, cnt, slot - 2 * rem_f, true);
       }
       rs_tile_at<GM>(a, t, s_pref_f, s_pref_h, item, &g, &lm, &nt);
       // rows 128*(2*lm + upper) .. +127 of the group: the upper or lower half
@@ -965,18 +1008,18 @@ __global__ __launch_bounds__(256) void rs_fixup_kernel(GemmArgs a, RsSplit sp, i
   const int xcd = blockIdx.x % kXcds;
   const int t = (blockIdx.x / kXcds) >> 2;
   const int quarter = (blockIdx.x / kXcds) & 3;
-  const RsTiles tl = rs_tiles(a, s_pref_f, s_pref_h, s_tmp, xcd);
+  RsTiles tl = rs_tiles(a, s_pref_f, s_pref_h, s_tmp, xcd, gemm_grid / kXcds);
   const RsPlan pl = rs_plan(tl.cnt_f + tl.cnt_h, gemm_grid / kXcds, a.K / BK,
                             sp.partial != nullptr && gemm_grid <= sp.max_blocks);
+  tl.inter = tl.inter && pl.P <= 1;   // as in the GEMM launch
   if (pl.P <= 1 || t >= pl.rem) return;
   int g, lm, nt;
-  rs_tile_at<GM>(a, tl, s_pref_f, s_pref_h, pl.full + t, &g, &lm, &nt);
+  const bool half = rs_tile_at<GM>(a, tl, s_pref_f, s_pref_h, pl.full + t, &g, &lm, &nt);
   const TileView<uint16_t> v = tile_view<uint16_t>(a, g, lm, BM);
   const int n0 = nt * BN;
   const int64_t blk0 = static_cast<int64_t>(t * pl.P) * kXcds + xcd;   // piece 0's workgroup
   // a half-height tail holds 32 register chunks per thread (rh layout), a
   // full tile 64; this workgroup takes a quarter of them
-  const bool half = pl.full + t >= tl.cnt_f;
   const int per = half ? 8 : 16;
   // all chunks of one piece are loaded together, pieces are added in order
   float4 acc[16];
