@@ -332,23 +332,24 @@ __device__ __forceinline__ void lds_barrier() {
 }
 }  // namespace rs
 
-// Half-height tiles: the last m-tile of a group often holds 128 rows or
-// fewer (an expert of 1,052 rows leaves 28 in its fifth 256-row tile).  Such
-// a tile is computed as 128 x 256 by all four waves (2 x 2 waves of 64 x 128)
-// instead of leaving half the waves to multiply padding rows: same operand
-// path and swizzle, half the A rows and MFMAs.
-namespace rh {
-constexpr int BM = 128, BN = 256, BK = 64, NT = 256, WTM = 64, WTN = 128;
-constexpr int TM = WTM / 32, TN = WTN / 32, NS = BK / 16;
-constexpr int A_CH = BM * 8 / NT, B_CH = BN * 8 / NT;
-using rs::swz;
+// Half- and quarter-height tiles: the last m-tile of a group often holds 128
+// rows or fewer (an expert of 1,052 rows leaves 28 in its fifth 256-row
+// tile).  Such a tile is computed as H x 256 (H = 128 or 64) by all four
+// waves (2 x 2 waves of H/2 x 128) instead of leaving waves to multiply
+// padding rows: same operand path and swizzle, H/256 of the A rows and MFMAs.
+template <int H>
+struct Rh {
+static constexpr int BM = H, BN = 256, BK = 64, NT = 256, WTM = H / 2, WTN = 128;
+static constexpr int TM = WTM / 32, TN = WTN / 32, NS = BK / 16;
+static constexpr int A_CH = BM * 8 / NT, B_CH = BN * 8 / NT;
+static __device__ __forceinline__ int swz(int r, int c) { return rs::swz(r, c); }
 
 struct Frags {
   bf16x8_t a[NS][TM];
   bf16x8_t b[NS][TN];
 };
 
-__device__ __forceinline__ void gload(u32x4_t (&ra)[A_CH], u32x4_t (&rb)[B_CH],
+static __device__ __forceinline__ void gload(u32x4_t (&ra)[A_CH], u32x4_t (&rb)[B_CH],
                                       const uint16_t *const (&a_src)[A_CH],
                                       const uint16_t *const (&b_src)[B_CH], int kb) {
 #pragma unroll
@@ -357,7 +358,7 @@ __device__ __forceinline__ void gload(u32x4_t (&ra)[A_CH], u32x4_t (&rb)[B_CH],
   for (int i = 0; i < B_CH; ++i) rb[i] = *reinterpret_cast<const u32x4_t *>(b_src[i] + kb * BK);
 }
 
-__device__ __forceinline__ void lstore(uint16_t *tile, const u32x4_t (&ra)[A_CH],
+static __device__ __forceinline__ void lstore(uint16_t *tile, const u32x4_t (&ra)[A_CH],
                                        const u32x4_t (&rb)[B_CH], int tid) {
   const int kc = tid & 7;
 #pragma unroll
@@ -372,7 +373,7 @@ __device__ __forceinline__ void lstore(uint16_t *tile, const u32x4_t (&ra)[A_CH]
   }
 }
 
-__device__ __forceinline__ void read_frags(const uint16_t *tile, Frags &f, int wm, int wn,
+static __device__ __forceinline__ void read_frags(const uint16_t *tile, Frags &f, int wm, int wn,
                                            int lane) {
 #pragma unroll
   for (int ks = 0; ks < NS; ++ks) {
@@ -391,7 +392,7 @@ __device__ __forceinline__ void read_frags(const uint16_t *tile, Frags &f, int w
   }
 }
 
-__device__ __forceinline__ void mfma_all(const Frags &f, f32x16_t (&acc)[TN][TM]) {
+static __device__ __forceinline__ void mfma_all(const Frags &f, f32x16_t (&acc)[TN][TM]) {
 #pragma unroll
   for (int ks = 0; ks < NS; ++ks)
 #pragma unroll
@@ -402,22 +403,43 @@ __device__ __forceinline__ void mfma_all(const Frags &f, f32x16_t (&acc)[TN][TM]
                                                               0, 0, 0);
 }
 
-// One step: 32 MFMAs; each of the 12 global loads / LDS writes shares a slot
-// with two MFMAs, then three fragment reads precede each of the last eight.
-__device__ __forceinline__ void schedule_step() {
+// One step: each global load / LDS write shares a slot with one or two MFMAs
+// (two when there are enough: H = 128 has 32 MFMAs for 12 loads), then the
+// fragment reads go before the remaining MFMAs, a few per MFMA.
+static __device__ __forceinline__ void schedule_step() {
+  constexpr int LOADS = A_CH + B_CH, MF = NS * TN * TM, READS = NS * (TM + TN);
+  constexpr int PER = MF >= 2 * LOADS ? 2 : 1;
+  constexpr int REST = MF - PER * LOADS;
+  constexpr int RPM = REST > 0 ? (READS + REST - 1) / REST : READS;
 #pragma unroll
-  for (int i = 0; i < A_CH + B_CH; ++i) {
+  for (int i = 0; i < LOADS; ++i) {
     __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);   // DS write
     __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA
     __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);   // VMEM read
-    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA
+    if constexpr (PER == 2) __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA
   }
 #pragma unroll
-  for (int i = 0; i < NS * (TM + TN) / 3; ++i) {
-    __builtin_amdgcn_sched_group_barrier(0x100, 3, 0);   // DS read
-    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA
+  for (int i = 0; i < REST; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x100, RPM, 0);   // DS read
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);     // MFMA
   }
 }
+
+// Accumulators of one H x 256 tile over K-steps k0 .. k0+nk-1, and its
+// epilogue (bias, SiLU, bf16 store through the LDS staging rows).
+static __device__ __forceinline__ void tile(const GemmArgs &a, const TileView<uint16_t> &v, int n0,
+                                            int k0, int nk, uint16_t *s_tile, int tid, int lane,
+                                            int wm, int wn, f32x16_t (&acc)[TN][TM]);
+template <int EPI>
+static __device__ __forceinline__ void epilogue(const f32x16_t (&acc)[TN][TM], const GemmArgs &a,
+                                                const TileView<uint16_t> &v, int n0,
+                                                uint16_t *s_tile, int lane, int wm, int wn,
+                                                int tid);
+};
+// the 128-row tiles, the height of the split and M-split paths
+namespace rh {
+using T = Rh<128>;
+constexpr int BM = T::BM, TM = T::TM, TN = T::TN, WTM = T::WTM;
 }  // namespace rh
 
 // Epilogue of a 256x256 tile through LDS in two passes of 128 rows (the tile
@@ -784,12 +806,10 @@ __device__ __forceinline__ void rs_tile(const GemmArgs &a, const TileView<uint16
   rs::lds_barrier();
 }
 
-// Accumulators of one 128 x 256 tile (the half-height tail of a group) over
-// K-steps k0 .. k0+nk-1.
-__device__ __forceinline__ void rh_tile(const GemmArgs &a, const TileView<uint16_t> &v, int n0,
-                                        int k0, int nk, uint16_t *s_tile, int tid, int lane,
-                                        int wm, int wn, f32x16_t (&acc)[rh::TN][rh::TM]) {
-  using namespace rh;
+template <int H>
+__device__ __forceinline__ void Rh<H>::tile(const GemmArgs &a, const TileView<uint16_t> &v, int n0,
+                                            int k0, int nk, uint16_t *s_tile, int tid, int lane,
+                                            int wm, int wn, f32x16_t (&acc)[TN][TM]) {
   const int kc = tid & 7;
   const uint16_t *a_src[A_CH];
   const uint16_t *b_src[B_CH];
@@ -839,13 +859,12 @@ __device__ __forceinline__ void rh_tile(const GemmArgs &a, const TileView<uint16
   __syncthreads();
 }
 
-// Epilogue of a 128 x 256 tile: one pass through the LDS staging rows.
+template <int H>
 template <int EPI>
-__device__ __forceinline__ void rh_epilogue(const f32x16_t (&acc)[rh::TN][rh::TM],
-                                            const GemmArgs &a, const TileView<uint16_t> &v,
-                                            int n0, uint16_t *s_tile, int lane, int wm, int wn,
-                                            int tid) {
-  using namespace rh;
+__device__ __forceinline__ void Rh<H>::epilogue(const f32x16_t (&acc)[TN][TM], const GemmArgs &a,
+                                                const TileView<uint16_t> &v, int n0,
+                                                uint16_t *s_tile, int lane, int wm, int wn,
+                                                int tid) {
   int el = lane, ewm = wm, ewn = wn, etid = tid;
   asm volatile("" : "+v"(el), "+v"(etid), "+s"(ewm), "+s"(ewn));
   constexpr int CH = BN / 8;
@@ -929,7 +948,7 @@ void grouped_gemm_bf16_rs_kernel(GemmArgs a, RsSplit sp) {
     float4 *dst = reinterpret_cast<float4 *>(sp.partial + static_cast<int64_t>(blockIdx.x) * (BM * BN));
     if (tail) {   // a half-height tail: its own register layout
       f32x16_t acch[rh::TN][rh::TM];
-      rh_tile(a, v, nt * BN, k0, kn, s_tile, tid, lane, wm, wn, acch);
+      rh::T::tile(a, v, nt * BN, k0, kn, s_tile, tid, lane, wm, wn, acch);
 #pragma unroll
       for (int i = 0; i < rh::TN; ++i)
 #pragma unroll
@@ -961,11 +980,24 @@ void grouped_gemm_bf16_rs_kernel(GemmArgs a, RsSplit sp) {
     const int end = pl.P > 1 || msplit ? pl.full : cnt;
     int g, lm, nt;
     for (int i = slot; i < end; i += nslots) {
-      if (rs_tile_at<GM>(a, t, s_pref_f, s_pref_h, i, &g, &lm, &nt)) {   // half-height tail
+      if (rs_tile_at<GM>(a, t, s_pref_f, s_pref_h, i, &g, &lm, &nt)) {   // a tail
         const TileView<uint16_t> v = tile_view<uint16_t>(a, g, lm, BM);
-        f32x16_t acch[rh::TN][rh::TM];
-        rh_tile(a, v, nt * BN, 0, nk, s_tile, tid, lane, wm, wn, acch);
-        rh_epilogue<EPI>(acch, a, v, nt * BN, s_tile, lane, wm, wn, tid);
+        // at quarter height in the first Linear (measured: in the second one
+        // the extra path costs the K loop registers and time)
+        bool quarter = false;
+        if constexpr (EPI == kEpiBiasSilu) {
+          quarter = v.rows - v.row0 <= Rh<64>::BM;
+          if (quarter) {
+            f32x16_t accq[Rh<64>::TN][Rh<64>::TM];
+            Rh<64>::tile(a, v, nt * BN, 0, nk, s_tile, tid, lane, wm, wn, accq);
+            Rh<64>::epilogue<EPI>(accq, a, v, nt * BN, s_tile, lane, wm, wn, tid);
+          }
+        }
+        if (!quarter) {
+          f32x16_t acch[rh::TN][rh::TM];
+          rh::T::tile(a, v, nt * BN, 0, nk, s_tile, tid, lane, wm, wn, acch);
+          rh::T::epilogue<EPI>(acch, a, v, nt * BN, s_tile, lane, wm, wn, tid);
+        }
       } else {
         const TileView<uint16_t> v = tile_view<uint16_t>(a, g, lm, BM);
         rs_tile<OFF32>(a, v, nt * BN, 0, nk, s_tile, tid, lane, wm, wn, acc);
@@ -985,8 +1017,8 @@ void grouped_gemm_bf16_rs_kernel(GemmArgs a, RsSplit sp) {
       // of a full-cost tile, or a tail tile (upper = 0)
       const TileView<uint16_t> v = tile_view<uint16_t>(a, g, 2 * lm + upper, rh::BM);
       f32x16_t acch[rh::TN][rh::TM];
-      rh_tile(a, v, nt * BN, 0, nk, s_tile, tid, lane, wm, wn, acch);
-      rh_epilogue<EPI>(acch, a, v, nt * BN, s_tile, lane, wm, wn, tid);
+      rh::T::tile(a, v, nt * BN, 0, nk, s_tile, tid, lane, wm, wn, acch);
+      rh::T::epilogue<EPI>(acch, a, v, nt * BN, s_tile, lane, wm, wn, tid);
     }
   }
 }
