@@ -25,9 +25,10 @@
 //     with fp32 accumulators, operands copied global -> two swizzled LDS
 //     buffers two K-steps ahead with the copies spread among the MFMAs
 //     (addressed from wave-uniform SGPR bases when offsets fit in 32 bits),
-//     tail tiles of 1..128 rows at half height (run beside the full tiles of
-//     their columns while their weight blocks are cached), and a K (or M)
-//     split of the last partial round of tiles;
+//     tail tiles of 1..128 rows at half height, or quarter height up to 64
+//     rows in the first Linear (run beside the full tiles of their columns
+//     while their weight blocks are cached), and a K (or M) split of the last
+//     partial round of tiles;
 //   * a stream kernel (groups of up to 128 rows, bound by the weight stream):
 //     weights and activations copied straight into a ring of LDS stages
 //     several chunks ahead, non-temporal for weights read once, units of one
