@@ -38,9 +38,14 @@
  *     outside [0, N) handed to moe_permute) are not validated; behaviour is
  *     then undefined.  No C++ exception crosses this interface.
  *   - T == 0 is a successful no-op.
- *   - Supported sizes: 1 <= top_k <= n_routed <= 1024; n_shared <= 64;
- *     d_model, d_ff multiples of 64 for MOE_BF16 and of 16 for MOE_F32;
- *     T * top_k < 2^31.  Others return MOE_ERR_UNSUPPORTED.
+ *   - Supported sizes: 1 <= top_k <= n_routed (top_k > n_routed or
+ *     top_k < 1 is MOE_ERR_INVALID_ARG); n_routed <= 1024 and top_k <= 64
+ *     (the top-K kernel keeps slot k of a token in lane k of one 64-wide
+ *     wave, and the combine stages a token's slot rows in 64 entries);
+ *     n_shared <= 64; d_model and d_ff multiples of 64 for MOE_BF16 (one
+ *     64-element reduction step of the matrix-core kernels, 128 bytes) and of
+ *     16 for MOE_F32; T * top_k < 2^31.  Sizes outside these limits return
+ *     MOE_ERR_UNSUPPORTED.
  *
  * Numerical contract
  *   - Logits: float32, per (t, e) one fused multiply-add chain over k
@@ -123,7 +128,14 @@ typedef struct {
  *   x           [T][d] act
  *   w_router    [N][d] float32;  router_bias [N] float32 or NULL (part of the
  *               logit for both selection and gates)
- *   logits      [T][N] float32 output (required; also the gates' input)
+ *   logits      [T][N] float32 output, required: the top-K pass reads the
+ *               logits back from here.  The logits of one token are computed
+ *               by many workgroups (one logit per lane, each a d-long fixed
+ *               order chain), so no single workgroup holds a token's N
+ *               logits on chip; a pass that did would serialise N/64 of those
+ *               chains per wave, far slower than this T*N*4-byte round trip
+ *               (4 MB, under a microsecond of HBM time, at 4096 tokens and
+ *               256 experts).
  *   topk_idx    [T][K] int32 output, expert ids in slot order
  *   topk_gate   [T][K] float32 output, sums to 1 per token
  */
@@ -158,7 +170,12 @@ size_t moe_permute_workspace_size(const moe_config *cfg);
  *   n_groups    number of experts in w1/w2 (>= 1)
  *   x_rows      [max_rows][d] act input
  *   offsets     [n_groups+1] int32 DEVICE array, non-decreasing, offsets[0]=0
- *   max_rows    host-side upper bound on offsets[n_groups] (sizes the launch)
+ *   max_rows    host-side upper bound on offsets[n_groups].  The offsets
+ *               stay on the device (no call copies them back), so the host
+ *               sizes the persistent launch and the split scratch from this
+ *               bound; the kernels read the true row counts on the device.
+ *               Rows at or beyond offsets[n_groups] are neither read nor
+ *               written; offsets[n_groups] > max_rows is undefined.
  *   w1 [G][f][d], b1 [G][f] or NULL, w2 [G][d][f], b2 [G][d] or NULL (act)
  *   h           [max_rows][f] act output (hidden activations)
  *   y_rows      [max_rows][d] act output
@@ -188,17 +205,48 @@ int moe_combine(const moe_config *cfg, const void *y_rows, const int32_t *slot_r
                 const float *topk_gate, const void *shared_out, void *y, void *stream);
 
 /*
- * moe_layer_forward — the whole layer: route, permute (the gather is fused
+ * moe_layer_forward — the whole layer of [DSMoE] 共有エキスパート機構 (output
+ * equation: the shared experts' sum plus the gate-weighted routed experts),
+ * with the routing of [TopK] ルーティングの仕組み and [DSMoE] gate equation and
+ * the capacity limit of [TopK] 解決策2: route, permute (the gather is fused
  * into the first expert GEMM), routed and shared expert FFNs, combine.
  *   x [T][d] act input, y [T][d] act output.
- *   topk_idx, topk_gate ([T][K]) and counts ([N]) are optional copies of the
- *   routing outputs (NULL to skip).
- *   ws          device workspace of moe_layer_workspace_size(cfg) bytes.
+ *   topk_idx, topk_gate ([T][K]) and counts ([N]) are optional outputs of the
+ *   routing (NULL to skip).  When one is given, the layer writes that array
+ *   there instead of into its workspace region.
+ *   ws          device workspace of moe_workspace_size(cfg) bytes.  After the
+ *               call has run on the stream, the regions named by
+ *               moe_workspace_layout hold the layer's routing: logits,
+ *               offsets, n_dropped, row_token and slot_row always, and
+ *               topk_idx, topk_gate and counts when their optional output is
+ *               NULL.  The rest of ws is scratch.
  */
 int moe_layer_forward(const moe_config *cfg, const moe_weights *w, const void *x, void *y,
                       int32_t *topk_idx, float *topk_gate, int32_t *counts,
                       void *ws, size_t ws_bytes, void *stream);
-size_t moe_layer_workspace_size(const moe_config *cfg);
+
+/* Bytes of device workspace moe_layer_forward needs for cfg (0 when cfg is
+ * invalid or unsupported). */
+size_t moe_workspace_size(const moe_config *cfg);
+
+/* Byte offsets, from the start of moe_layer_forward's workspace, of the
+ * routing arrays the layer leaves there (shapes as in moe_permute; every
+ * offset is a multiple of 256). */
+typedef struct {
+    size_t logits;      /* [T][N] float32                                     */
+    size_t topk_idx;    /* [T][K] int32                                       */
+    size_t topk_gate;   /* [T][K] float32                                     */
+    size_t counts;      /* [N] int32: kept rows per expert                    */
+    size_t offsets;     /* [N+1] int32                                        */
+    size_t n_dropped;   /* [1] int32                                          */
+    size_t row_token;   /* [T*K] int32 (rows 0 .. offsets[N]-1 hold tokens)   */
+    size_t slot_row;    /* [T][K] int32 (-1 = dropped)                        */
+    size_t total;       /* moe_workspace_size(cfg)                            */
+} moe_ws_layout;
+
+/* Fills *out for cfg; MOE_OK, or the status moe_layer_forward would return
+ * for cfg's shape. */
+int moe_workspace_layout(const moe_config *cfg, moe_ws_layout *out);
 
 /* Stages of moe_layer_forward, in launch order. */
 enum {

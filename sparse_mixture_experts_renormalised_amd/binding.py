@@ -27,7 +27,8 @@ STATUS = {0: "ok", -1: "invalid argument", -2: "unsupported size", -3: "workspac
 EXPORTS = ("moe_route", "moe_permute", "moe_permute_workspace_size", "moe_grouped_ffn",
            "moe_grouped_ffn_workspace_size", "moe_combine", "moe_balance_stats",
            "moe_balance_stats_workspace_size", "moe_layer_forward", "moe_layer_forward_events",
-           "moe_layer_workspace_size", "moe_capacity", "moe_status_string", "moe_version")
+           "moe_workspace_size", "moe_workspace_layout", "moe_capacity", "moe_status_string",
+           "moe_version")
 STAGES = ("router", "topk", "dispatch", "up", "down", "combine")
 
 
@@ -43,6 +44,13 @@ class Config(ctypes.Structure):
                 ("top_k", ctypes.c_int32), ("n_shared", ctypes.c_int32), ("d_ff", ctypes.c_int32),
                 ("dtype", ctypes.c_int32), ("capacity_factor", ctypes.c_float),
                 ("capacity", ctypes.c_int32), ("bias_mode", ctypes.c_int32)]
+
+
+class WsLayout(ctypes.Structure):
+    """Mirror of moe_ws_layout (byte offsets into the layer workspace)."""
+    _fields_ = [(n, ctypes.c_size_t) for n in
+                ("logits", "topk_idx", "topk_gate", "counts", "offsets", "n_dropped", "row_token",
+                 "slot_row", "total")]
 
 
 class Weights(ctypes.Structure):
@@ -76,7 +84,8 @@ def lib():
             "moe_layer_forward": (I, [C, ctypes.POINTER(Weights), P, P, P, P, P, P, Z, P]),
             "moe_layer_forward_events": (I, [C, ctypes.POINTER(Weights), P, P, P, P, P, P, Z,
                                              ctypes.POINTER(ctypes.c_void_p), P]),
-            "moe_layer_workspace_size": (Z, [C]),
+            "moe_workspace_size": (Z, [C]),
+            "moe_workspace_layout": (I, [C, ctypes.POINTER(WsLayout)]),
             "moe_capacity": (I64, [C]),
             "moe_status_string": (ctypes.c_char_p, [I]),
             "moe_version": (I, []),
@@ -173,8 +182,14 @@ def combine(cfg: Config, y_rows, slot_row, topk_gate, shared_out, y, stream=None
                                             _stream(stream)))
 
 
-def layer_workspace_size(cfg: Config) -> int:
-    return int(lib().moe_layer_workspace_size(ctypes.byref(cfg)))
+def workspace_size(cfg: Config) -> int:
+    return int(lib().moe_workspace_size(ctypes.byref(cfg)))
+
+
+def workspace_layout(cfg: Config) -> WsLayout:
+    out = WsLayout()
+    _check("moe_workspace_layout", lib().moe_workspace_layout(ctypes.byref(cfg), ctypes.byref(out)))
+    return out
 
 
 def weights(w_router, router_bias, w1, b1, w2, b2, ws1=None, bs1=None, ws2=None,

@@ -1595,7 +1595,7 @@ __global__ __launch_bounds__(256) void stream_finish_kernel(GemmArgs a, StreamSp
 }
 
 // ---------------------------------------------------------------------------
-// fp32 VALU kernel (also accepts bf16 operands): 64x64 tiles, 256 threads
+// fp32 VALU kernel: 64x64 tiles, 256 threads
 // ---------------------------------------------------------------------------
 template <typename TA, int EPI>
 __global__ __launch_bounds__(256) void grouped_gemm_valu_kernel(GemmArgs a) {
@@ -1878,18 +1878,14 @@ hipError_t launch_grouped_gemm(bool bf16, const GemmGroups &g, Epilogue epi, hip
     if (e != hipSuccess) return e;
     return launch_bf16_stream<2, 2, 3, 4>(as, g, epi, 1, s);
   }
+  // bf16 widths are multiples of 64 (checked at the interface), so only
+  // float32 operands reach the VALU kernel
+  if (bf16) return hipErrorInvalidValue;
   const unsigned grid = persistent_grid(tiles_upper_bound(g, 64, 64), 4);
-  if (bf16) {
-    if (epi == kEpiBiasSilu)
-      hipLaunchKernelGGL((grouped_gemm_valu_kernel<uint16_t, kEpiBiasSilu>), dim3(grid), dim3(256), 0, s, a);
-    else
-      hipLaunchKernelGGL((grouped_gemm_valu_kernel<uint16_t, kEpiBias>), dim3(grid), dim3(256), 0, s, a);
-  } else {
-    if (epi == kEpiBiasSilu)
-      hipLaunchKernelGGL((grouped_gemm_valu_kernel<float, kEpiBiasSilu>), dim3(grid), dim3(256), 0, s, a);
-    else
-      hipLaunchKernelGGL((grouped_gemm_valu_kernel<float, kEpiBias>), dim3(grid), dim3(256), 0, s, a);
-  }
+  if (epi == kEpiBiasSilu)
+    hipLaunchKernelGGL((grouped_gemm_valu_kernel<float, kEpiBiasSilu>), dim3(grid), dim3(256), 0, s, a);
+  else
+    hipLaunchKernelGGL((grouped_gemm_valu_kernel<float, kEpiBias>), dim3(grid), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 

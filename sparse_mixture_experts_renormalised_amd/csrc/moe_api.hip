@@ -4,6 +4,8 @@
 #include <math.h>
 #include <string.h>
 
+#include <initializer_list>
+
 #include "moe_common.h"
 #include "moe_mi355x.h"
 
@@ -15,6 +17,15 @@ constexpr size_t kAlign = 256;
 inline size_t align_up(size_t b) { return (b + kAlign - 1) & ~(kAlign - 1); }
 
 bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// Every device pointer the header declares must be 16-byte aligned (the
+// kernels read operands as 16-byte vectors, biases as 8-byte pairs); NULL
+// passes here and is checked where it is not allowed.
+bool all_aligned16(std::initializer_list<const void *> ps) {
+  for (const void *p : ps)
+    if (p && !aligned16(p)) return false;
+  return true;
+}
 
 size_t act_bytes(const moe_config *c) { return c->dtype == MOE_BF16 ? 2 : 4; }
 
@@ -156,7 +167,8 @@ int moe_route(const moe_config *cfg, const void *x, const float *w_router,
   if (st != MOE_OK) return st;
   if (cfg->T == 0) return MOE_OK;
   if (!x || !w_router || !logits || !topk_idx || !topk_gate) return MOE_ERR_INVALID_ARG;
-  if (!aligned16(x) || !aligned16(w_router)) return MOE_ERR_INVALID_ARG;
+  if (!all_aligned16({x, w_router, router_bias, logits, topk_idx, topk_gate}))
+    return MOE_ERR_INVALID_ARG;
   hipStream_t s = static_cast<hipStream_t>(stream);
   const bool bf16 = cfg->dtype == MOE_BF16;
   const bool sel_only = cfg->bias_mode == MOE_BIAS_SELECTION_ONLY;
@@ -179,6 +191,7 @@ int moe_balance_stats(const moe_config *cfg, const float *logits, const int32_t 
   if (st != MOE_OK) return st;
   if (cfg->T == 0) return MOE_OK;
   if (!logits || !topk_idx || !f || !P || !loss) return MOE_ERR_INVALID_ARG;
+  if (!all_aligned16({logits, topk_idx, f, P, loss, ws})) return MOE_ERR_INVALID_ARG;
   if (!ws || ws_bytes < moe::balance_workspace_bytes(cfg->T, cfg->n_routed))
     return MOE_ERR_WORKSPACE;
   return hip_status(moe::launch_balance_stats(logits, topk_idx, cfg->T, cfg->n_routed,
@@ -199,7 +212,10 @@ int moe_permute(const moe_config *cfg, const int32_t *topk_idx, const void *x, i
   if (cfg->T == 0) return MOE_OK;
   if (!topk_idx || !counts || !offsets || !row_token || !slot_row || !n_dropped)
     return MOE_ERR_INVALID_ARG;
-  if (x_perm && (!x || !aligned16(x) || !aligned16(x_perm))) return MOE_ERR_INVALID_ARG;
+  if (x_perm && !x) return MOE_ERR_INVALID_ARG;
+  if (!all_aligned16({topk_idx, counts, offsets, row_token, slot_row, n_dropped, ws,
+                      x_perm ? x : nullptr, x_perm}))
+    return MOE_ERR_INVALID_ARG;
   const size_t need = moe::dispatch_workspace_bytes(cfg->T, cfg->top_k, cfg->n_routed);
   if (!ws || ws_bytes < need) return MOE_ERR_WORKSPACE;
   hipStream_t s = static_cast<hipStream_t>(stream);
@@ -233,8 +249,7 @@ int moe_grouped_ffn(const moe_config *cfg, int32_t n_groups, const void *x_rows,
   if (max_rows == 0) return MOE_OK;
   if (max_rows >= (int64_t(1) << 31)) return MOE_ERR_UNSUPPORTED;
   if (!x_rows || !offsets || !w1 || !w2 || !h || !y_rows) return MOE_ERR_INVALID_ARG;
-  if (!aligned16(x_rows) || !aligned16(w1) || !aligned16(w2) || !aligned16(h) ||
-      !aligned16(y_rows))
+  if (!all_aligned16({x_rows, offsets, w1, b1, w2, b2, h, y_rows, ws}))
     return MOE_ERR_INVALID_ARG;
   const size_t need = moe_grouped_ffn_workspace_size(cfg, n_groups, max_rows);
   if (ws && ws_bytes < need) return MOE_ERR_WORKSPACE;
@@ -273,17 +288,36 @@ int moe_combine(const moe_config *cfg, const void *y_rows, const int32_t *slot_r
   if (cfg->T == 0) return MOE_OK;
   if (!y_rows || !slot_row || !topk_gate || !y) return MOE_ERR_INVALID_ARG;
   if (cfg->n_shared > 0 && !shared_out) return MOE_ERR_INVALID_ARG;
-  if (!aligned16(y_rows) || !aligned16(y) || (shared_out && !aligned16(shared_out)))
-    return MOE_ERR_INVALID_ARG;
+  if (!all_aligned16({y_rows, slot_row, topk_gate, shared_out, y})) return MOE_ERR_INVALID_ARG;
   return hip_status(moe::launch_combine(cfg->dtype == MOE_BF16, y_rows, slot_row, topk_gate,
                                         cfg->n_shared > 0 ? shared_out : nullptr, cfg->n_shared,
                                         cfg->T, cfg->top_k, cfg->d_model, y,
                                         static_cast<hipStream_t>(stream)));
 }
 
-size_t moe_layer_workspace_size(const moe_config *cfg) {
+size_t moe_workspace_size(const moe_config *cfg) {
   if (check_config(cfg, true, true) != MOE_OK) return 0;
   return layer_ws(cfg, nullptr).bytes;
+}
+
+int moe_workspace_layout(const moe_config *cfg, moe_ws_layout *out) {
+  const int st = check_config(cfg, true, true);
+  if (st != MOE_OK) return st;
+  if (!out) return MOE_ERR_INVALID_ARG;
+  // carve from a base of 256 (not NULL, which the carver reads as "sizes only")
+  char *const base = reinterpret_cast<char *>(static_cast<uintptr_t>(kAlign));
+  const LayerWs L = layer_ws(cfg, base);
+  auto off = [&](const void *p) { return static_cast<size_t>(static_cast<const char *>(p) - base); };
+  out->logits = off(L.logits);
+  out->topk_idx = off(L.idx);
+  out->topk_gate = off(L.gates);
+  out->counts = off(L.counts);
+  out->offsets = off(L.offsets);
+  out->n_dropped = off(L.n_dropped);
+  out->row_token = off(L.row_token);
+  out->slot_row = off(L.slot_row);
+  out->total = L.bytes;
+  return MOE_OK;
 }
 
 int moe_layer_forward(const moe_config *cfg, const moe_weights *w, const void *x, void *y,
@@ -303,8 +337,8 @@ int moe_layer_forward_events(const moe_config *cfg, const moe_weights *w, const 
   if (cfg->T == 0) return MOE_OK;
   if (!x || !y || !w->w_router || !w->w1 || !w->w2) return MOE_ERR_INVALID_ARG;
   if (cfg->n_shared > 0 && (!w->ws1 || !w->ws2)) return MOE_ERR_INVALID_ARG;
-  if (!aligned16(x) || !aligned16(y) || !aligned16(w->w_router) || !aligned16(w->w1) ||
-      !aligned16(w->w2))
+  if (!all_aligned16({x, y, w->w_router, w->router_bias, w->w1, w->b1, w->w2, w->b2, w->ws1,
+                      w->bs1, w->ws2, w->bs2, topk_idx, topk_gate, counts, ws}))
     return MOE_ERR_INVALID_ARG;
   const LayerWs L = layer_ws(cfg, ws);
   if (!ws || ws_bytes < L.bytes) return MOE_ERR_WORKSPACE;

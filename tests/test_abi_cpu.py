@@ -85,14 +85,57 @@ def test_invalid_arguments_are_rejected_before_launch(B):
     # misaligned device pointer
     assert L.moe_layer_forward(ctypes.byref(good), ctypes.byref(w), P(4100), P(4096), None, None,
                                None, None, 1 << 30, P(4096)) == -1
+    # misaligned shared-expert weights and biases (every device pointer is
+    # 16-byte aligned; the epilogues read biases as 8-byte pairs)
+    sh = B.config(64, 128, 8, 2, 1, 256, "bf16")
+    for field in ("ws1", "ws2", "b1", "b2", "bs1", "bs2", "router_bias"):
+        w2 = B.Weights(w_router=4096, w1=4096, w2=4096, ws1=4096, ws2=4096)
+        setattr(w2, field, 4104)
+        assert L.moe_layer_forward(ctypes.byref(sh), ctypes.byref(w2), P(4096), P(4096), None,
+                                   None, None, P(4096), 1 << 30, None) == -1, field
+    # optional routing outputs too
+    w3 = B.Weights(w_router=4096, w1=4096, w2=4096, ws1=4096, ws2=4096)
+    assert L.moe_layer_forward(ctypes.byref(sh), ctypes.byref(w3), P(4096), P(4096), P(4100),
+                               None, None, P(4096), 1 << 30, None) == -1
     # grouped FFN argument checks
     assert L.moe_grouped_ffn(ctypes.byref(good), 0, None, None, 10, None, None, None, None, None,
                              None, None, 0, None) == -1
     assert L.moe_grouped_ffn(ctypes.byref(good), 3, None, None, 10, None, None, None, None, None,
                              None, None, 0, None) == -1
+    # misaligned bias of the grouped FFN
+    for b1, b2 in ((P(4100), None), (None, P(4104))):
+        assert L.moe_grouped_ffn(ctypes.byref(good), 3, P(4096), P(4096), 10, P(4096), b1,
+                                 P(4096), b2, P(4096), P(4096), None, 0, None) == -1
     # combine needs shared outputs when shared experts exist
     sh = B.config(64, 128, 8, 2, 2, 256, "bf16")
     assert L.moe_combine(ctypes.byref(sh), P(16), P(16), P(16), None, P(16), None) == -1
+
+
+def test_top_k_limit(B):
+    # top_k <= 64: slot k of a token lives in lane k of one wave
+    L = B.lib()
+    w = B.Weights()
+    assert L.moe_layer_forward(ctypes.byref(B.config(64, 128, 100, 65, 0, 256, "bf16")),
+                               ctypes.byref(w), None, None, None, None, None, None, 0, None) == -2
+    assert L.moe_route(ctypes.byref(B.config(64, 128, 100, 65, 0, 256, "bf16")), None, None, None,
+                       None, None, None, None) == -2
+    assert B.workspace_size(B.config(64, 128, 100, 65, 0, 256, "bf16")) == 0
+    assert B.workspace_size(B.config(64, 128, 100, 64, 0, 256, "bf16")) > 0
+
+
+def test_workspace_layout(B):
+    cfg = B.config(333, 128, 16, 4, 1, 256, "bf16")
+    lay = B.workspace_layout(cfg)
+    assert lay.total == B.workspace_size(cfg)
+    T, N, K = 333, 16, 4
+    regions = sorted([(lay.logits, T * N * 4), (lay.topk_idx, T * K * 4), (lay.topk_gate, T * K * 4),
+                      (lay.counts, N * 4), (lay.offsets, (N + 1) * 4), (lay.n_dropped, 4),
+                      (lay.row_token, T * K * 4), (lay.slot_row, T * K * 4)])
+    # 256-aligned, disjoint, inside the workspace
+    for (o, n), (o2, _) in zip(regions, regions[1:] + [(lay.total, 0)]):
+        assert o % 256 == 0 and o + n <= o2
+    with pytest.raises(B.MoeError):
+        B.workspace_layout(B.config(64, 128, 4, 5, 0, 256, "bf16"))
 
 
 def test_empty_batch_is_a_no_op(B):
@@ -105,12 +148,12 @@ def test_empty_batch_is_a_no_op(B):
 
 
 def test_workspace_sizes_grow_with_the_layer(B):
-    small = B.layer_workspace_size(B.config(64, 128, 8, 2, 0, 256, "f32"))
-    big = B.layer_workspace_size(B.config(4096, 7168, 256, 8, 1, 2048, "bf16"))
+    small = B.workspace_size(B.config(64, 128, 8, 2, 0, 256, "f32"))
+    big = B.workspace_size(B.config(4096, 7168, 256, 8, 1, 2048, "bf16"))
     assert 0 < small < big
     # hidden + expert outputs of every assignment dominate: T*K*(d+f) act elements
     assert big >= 4096 * 8 * (7168 + 2048) * 2
-    assert B.layer_workspace_size(B.config(64, 128, 8, 9, 0, 256, "f32")) == 0
+    assert B.workspace_size(B.config(64, 128, 8, 9, 0, 256, "f32")) == 0
 
 
 def test_grouped_ffn_split_workspace_size(B):

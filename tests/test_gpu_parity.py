@@ -40,6 +40,45 @@ def rel_l2(got, ref):
     return float(np.linalg.norm(got - ref) / (den if den > 0 else 1.0))
 
 
+# Per-token bound: the largest row-wise relative L2 error over the tokens.
+# One global norm would let a wrong block of a few rows or columns pass
+# (a bad 28 x 32 corner of one 256 x 256 tile moves the global figure of a
+# 4096 x 4096 output by well under 1e-2); every row must meet this bound.
+ROW_TOL = {"f32": 1e-4, "bf16": 3e-2}
+
+
+def row_rel_l2_max(got, ref):
+    got = np.asarray(got, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    num = np.linalg.norm(got - ref, axis=1)
+    den = np.linalg.norm(ref, axis=1)
+    den = np.where(den > 0, den, 1.0)
+    return float((num / den).max())
+
+
+def check_layer(dl, ref, wl, toks=None, label=""):
+    """Everything the layer leaves behind against the oracle: the routing
+    outputs bit exact (ids, counts, and, read back from the workspace, the
+    logits, offsets, row_token, slot_row and n_dropped), gates within 1e-6,
+    and y within the global and the per-row tolerance."""
+    assert np.array_equal(dl.topk_idx.cpu().numpy(), ref["topk_idx"])
+    assert np.array_equal(dl.counts.cpu().numpy(), ref["counts"])
+    assert np.abs(dl.topk_gate.cpu().numpy() - ref["gates"]).max() <= 1e-6
+    r = dl.routing_from_workspace()
+    assert np.array_equal(r["logits"].view(np.uint32), ref["logits"].view(np.uint32))
+    assert np.array_equal(r["offsets"], ref["offsets"])
+    assert np.array_equal(r["row_token"], ref["row_token"])
+    assert np.array_equal(r["slot_row"], ref["slot_row"])
+    assert r["n_dropped"] == ref["n_dropped"]
+    y = host(dl.y) if toks is None else host(dl.y[torch.from_numpy(toks).long().cuda()])
+    err = rel_l2(y, ref["y"])
+    row = row_rel_l2_max(y, ref["y"])
+    print(f"[layer] {label or wl.name}: rel_l2={err:.3e} max_row_rel_l2={row:.3e} "
+          f"kept={int(ref['offsets'][-1])} dropped={ref['n_dropped']}", flush=True)
+    assert err <= TOL[wl.dtype]
+    assert row <= ROW_TOL[wl.dtype]
+
+
 def host(t):
     return t.float().cpu().numpy() if t.dtype in (torch.bfloat16, torch.float32) else t.cpu().numpy()
 
@@ -477,10 +516,7 @@ def test_layer_forward_matches_oracle(wl):
     ref = oracle.layer_forward(host(dl.x), wl.w_router().numpy(), bias_np(wl), routed, shared,
                                top_k=wl.top_k, n_shared=wl.n_shared,
                                capacity_factor=wl.capacity_factor)
-    assert np.array_equal(dl.topk_idx.cpu().numpy(), ref["topk_idx"])
-    assert np.array_equal(dl.counts.cpu().numpy(), ref["counts"])
-    assert np.abs(dl.topk_gate.cpu().numpy() - ref["gates"]).max() <= 1e-6
-    assert rel_l2(host(dl.y), ref["y"]) <= TOL[wl.dtype]
+    check_layer(dl, ref, wl)
 
 
 def test_layer_forward_is_deterministic():
@@ -522,12 +558,8 @@ def test_layer_identical_experts():
 
 # ---------------------------------------------------------------------------
 # full-size workloads, in the launch configuration the benchmark times:
-# routing compared on every token, outputs on sampled tokens
+# every token's output and the whole routing compared with the oracle
 # ---------------------------------------------------------------------------
-
-SAMPLES = {"tiny_fp32": None, "mixtral_shape": 12, "deepseekmoe_fine": 24, "dsv3_prefill": 8,
-           "dsv3_decode": 16}
-
 
 @pytest.mark.parametrize("name", list(W.WORKLOADS))
 def test_full_size_workload(name):
@@ -535,28 +567,16 @@ def test_full_size_workload(name):
     print(f"[full-size] {name}: T={wl.T} d={wl.d_model} N={wl.n_routed} K={wl.top_k} "
           f"Ks={wl.n_shared} f={wl.d_ff}", flush=True)
     dl = run_layer(wl)
-    n = SAMPLES[name]
-    rng = np.random.default_rng(123)
-    toks = None if n is None else np.sort(rng.choice(wl.T, size=n, replace=False))
-    cache = {}
 
-    def routed(e):
-        if ("r", e) not in cache:
-            cache[("r", e)] = dl.expert_host(e)
-        return cache[("r", e)]
-
-    def shared(i):
-        return dl.expert_host(i, shared=True)
+    # one expert at a time, widened to float64 on the device and copied over,
+    # with no cache: the oracle asks for each expert once
+    def expert64(e, shared=False):
+        src = (dl.ws1, dl.bs1, dl.ws2, dl.bs2) if shared else (dl.w1, dl.b1, dl.w2, dl.b2)
+        return tuple(None if t is None else t[e].double().cpu().numpy() for t in src)
 
     ref = oracle.layer_forward(host(dl.x), host(dl.w_router),
                                None if dl.router_bias is None else host(dl.router_bias),
-                               routed, shared, top_k=wl.top_k, n_shared=wl.n_shared,
-                               capacity_factor=wl.capacity_factor, tokens=toks)
-    assert np.array_equal(dl.topk_idx.cpu().numpy(), ref["topk_idx"])
-    assert np.array_equal(dl.counts.cpu().numpy(), ref["counts"])
-    assert np.abs(dl.topk_gate.cpu().numpy() - ref["gates"]).max() <= 1e-6
-    y = host(dl.y) if toks is None else host(dl.y[torch.from_numpy(toks).long().cuda()])
-    err = rel_l2(y, ref["y"])
-    print(f"[full-size] {name}: rel_l2={err:.3e} kept={int(ref['offsets'][-1])} "
-          f"dropped={ref['n_dropped']}", flush=True)
-    assert err <= TOL[wl.dtype]
+                               lambda e: expert64(e), lambda i: expert64(i, True),
+                               top_k=wl.top_k, n_shared=wl.n_shared,
+                               capacity_factor=wl.capacity_factor)
+    check_layer(dl, ref, wl, label=f"full-size {name}")

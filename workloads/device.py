@@ -39,7 +39,7 @@ class DeviceLayer:
         self.topk_idx = torch.zeros((T, K), dtype=torch.int32, device=dev)
         self.topk_gate = torch.zeros((T, K), dtype=torch.float32, device=dev)
         self.counts = torch.zeros((N,), dtype=torch.int32, device=dev)
-        self.ws = torch.empty((max(1, B.layer_workspace_size(self.cfg)),), dtype=torch.uint8,
+        self.ws = torch.empty((max(1, B.workspace_size(self.cfg)),), dtype=torch.uint8,
                               device=dev)
 
     def forward(self, stream=None):
@@ -51,6 +51,27 @@ class DeviceLayer:
         B.layer_forward_events(self.cfg, self.weights, self.x, self.y, events, self.topk_idx,
                                self.topk_gate, self.counts, self.ws, stream)
         return self.y
+
+    def routing_from_workspace(self):
+        """The layer's own routing arrays, read back from its workspace (the
+        regions moe_workspace_layout names), as host numpy arrays."""
+        wl = self.wl
+        T, K, N = wl.T, wl.top_k, wl.n_routed
+        lay = B.workspace_layout(self.cfg)
+
+        def region(off, n, dtype):
+            nbytes = n * torch.tensor([], dtype=dtype).element_size()
+            return self.ws[off:off + nbytes].view(dtype).cpu().numpy()
+
+        offsets = region(lay.offsets, N + 1, torch.int32)
+        R = int(offsets[-1])
+        return {
+            "logits": region(lay.logits, T * N, torch.float32).reshape(T, N),
+            "offsets": offsets,
+            "n_dropped": int(region(lay.n_dropped, 1, torch.int32)[0]),
+            "row_token": region(lay.row_token, T * K, torch.int32)[:R],
+            "slot_row": region(lay.slot_row, T * K, torch.int32).reshape(T, K),
+        }
 
     def expert_host(self, e: int, shared: bool = False):
         """One expert's tensors copied to the host as float32 numpy (None for absent bias)."""
