@@ -225,6 +225,34 @@ int moe_layer_forward(const moe_config *cfg, const moe_weights *w, const void *x
                       int32_t *topk_idx, float *topk_gate, int32_t *counts,
                       void *ws, size_t ws_bytes, void *stream);
 
+/*
+ * moe_layer_forward_noalloc — moe_layer_forward for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc): the same stages and kernels, with the
+ * workspace taken from a library-owned device array instead of `ws`.
+ *   - The array holds MOE_NOALLOC_SCRATCH_BYTES (64 MiB) per GPU, from the
+ *     first use of the library on that GPU until the process ends.  The
+ *     call allocates nothing (no hipMalloc, hipFree or allocating library
+ *     routine); its first call on a device looks up the array's address there.
+ *   - A layer whose workspace, without the expert GEMMs' optional K-split
+ *     scratch, exceeds that size returns MOE_ERR_WORKSPACE before anything is
+ *     enqueued.  The K-split scratch gets what is left (a DeepSeek-V3-shaped
+ *     decode layer of 128 tokens needs about 22 MB plus 32 MB of it); with
+ *     less, fewer products are split.  Batches of a few hundred tokens at
+ *     DeepSeek-V3 widths fit; 4096-token prefill layers do not.
+ *   - Every call on one GPU uses that GPU's one array.  Calls that overlap on
+ *     one GPU (on different streams, or from several host threads without
+ *     ordering) race and give undefined results; calls on one stream are
+ *     ordered and safe.  Each call writes every part of the array it later
+ *     reads, so nothing left by an earlier call is used.
+ *   Arguments as moe_layer_forward; the routing arrays are not readable
+ *   through moe_workspace_layout here (pass topk_idx, topk_gate, counts).
+ */
+#define MOE_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+int moe_layer_forward_noalloc(const moe_config *cfg, const moe_weights *w, const void *x,
+                              void *y, int32_t *topk_idx, float *topk_gate, int32_t *counts,
+                              void *stream);
+
 /* Bytes of device workspace moe_layer_forward needs for cfg (0 when cfg is
  * invalid or unsupported). */
 size_t moe_workspace_size(const moe_config *cfg);

@@ -27,8 +27,8 @@ STATUS = {0: "ok", -1: "invalid argument", -2: "unsupported size", -3: "workspac
 EXPORTS = ("moe_route", "moe_permute", "moe_permute_workspace_size", "moe_grouped_ffn",
            "moe_grouped_ffn_workspace_size", "moe_combine", "moe_balance_stats",
            "moe_balance_stats_workspace_size", "moe_layer_forward", "moe_layer_forward_events",
-           "moe_workspace_size", "moe_workspace_layout", "moe_capacity", "moe_status_string",
-           "moe_version")
+           "moe_layer_forward_noalloc", "moe_workspace_size", "moe_workspace_layout",
+           "moe_capacity", "moe_status_string", "moe_version")
 STAGES = ("router", "topk", "dispatch", "up", "down", "combine")
 
 
@@ -84,6 +84,7 @@ def lib():
             "moe_layer_forward": (I, [C, ctypes.POINTER(Weights), P, P, P, P, P, P, Z, P]),
             "moe_layer_forward_events": (I, [C, ctypes.POINTER(Weights), P, P, P, P, P, P, Z,
                                              ctypes.POINTER(ctypes.c_void_p), P]),
+            "moe_layer_forward_noalloc": (I, [C, ctypes.POINTER(Weights), P, P, P, P, P, P]),
             "moe_workspace_size": (Z, [C]),
             "moe_workspace_layout": (I, [C, ctypes.POINTER(WsLayout)]),
             "moe_capacity": (I64, [C]),
@@ -204,6 +205,15 @@ def layer_forward(cfg: Config, w: Weights, x, y, topk_idx=None, topk_gate=None, 
                                                         _ptr(x), _ptr(y), _ptr(topk_idx),
                                                         _ptr(topk_gate), _ptr(counts), _ptr(ws),
                                                         nbytes, _stream(stream)))
+
+
+def layer_forward_noalloc(cfg: Config, w: Weights, x, y, topk_idx=None, topk_gate=None,
+                          counts=None, stream=None):
+    """layer_forward with the library's own static device scratch (no workspace)."""
+    _check("moe_layer_forward_noalloc",
+           lib().moe_layer_forward_noalloc(ctypes.byref(cfg), ctypes.byref(w), _ptr(x), _ptr(y),
+                                           _ptr(topk_idx), _ptr(topk_gate), _ptr(counts),
+                                           _stream(stream)))
 
 
 def layer_forward_events(cfg: Config, w: Weights, x, y, events, topk_idx=None, topk_gate=None,

@@ -5,6 +5,7 @@
 #include <string.h>
 
 #include <initializer_list>
+#include <mutex>
 
 #include "moe_common.h"
 #include "moe_mi355x.h"
@@ -80,6 +81,7 @@ struct LayerWs {
   void *y_rows;  // routed outputs [T*K][d]
   void *s_out;   // shared outputs [Ks][T][d]
   void *split;   // k-split scratch of the expert GEMMs (may be empty)
+  size_t split_bytes;
   size_t bytes;
 };
 
@@ -108,7 +110,11 @@ size_t layer_split_bytes(const moe_config *c) {
   return moe::grouped_gemm_split_bytes(g);
 }
 
-LayerWs layer_ws(const moe_config *c, void *base) {
+// The layer's workspace carved from base (NULL: sizes only).  The K-split
+// scratch of the expert GEMMs is the last piece, at most split_cap bytes:
+// with less than they could use, the GEMMs split fewer products (same
+// results within the tolerance, possibly slower).
+LayerWs layer_ws(const moe_config *c, void *base, size_t split_cap = SIZE_MAX) {
   LayerWs w;
   char *p = static_cast<char *>(base);
   size_t off = 0;
@@ -132,10 +138,58 @@ LayerWs layer_ws(const moe_config *c, void *base) {
   w.h_sh = take(ab * Ks * T * c->d_ff);
   w.y_rows = take(ab * T * K * c->d_model);
   w.s_out = take(ab * Ks * T * c->d_model);
-  const size_t sb = layer_split_bytes(c);
+  size_t sb = layer_split_bytes(c);
+  if (sb > split_cap) sb = split_cap & ~(kAlign - 1);
   w.split = sb ? take(sb) : nullptr;
+  w.split_bytes = sb;
   w.bytes = off;
   return w;
+}
+
+// Pointer checks of the layer entry points (after check_config).
+int check_layer_args(const moe_weights *w, const moe_config *cfg, const void *x, const void *y,
+                     const int32_t *topk_idx, const float *topk_gate, const int32_t *counts) {
+  if (!x || !y || !w->w_router || !w->w1 || !w->w2) return MOE_ERR_INVALID_ARG;
+  if (cfg->n_shared > 0 && (!w->ws1 || !w->ws2)) return MOE_ERR_INVALID_ARG;
+  if (!all_aligned16({x, y, w->w_router, w->router_bias, w->w1, w->b1, w->w2, w->b2, w->ws1,
+                      w->bs1, w->ws2, w->bs2, topk_idx, topk_gate, counts}))
+    return MOE_ERR_INVALID_ARG;
+  return MOE_OK;
+}
+
+int run_layer(const moe_config *cfg, const moe_weights *w, const void *x, void *y,
+              int32_t *topk_idx, float *topk_gate, int32_t *counts, const LayerWs &L,
+              void *const *stage_events, hipStream_t s);
+
+}  // namespace
+
+// Workspace of moe_layer_forward_noalloc: a file-scope device array, so
+// that entry point needs no allocation.  Every GPU the library runs on gets
+// its own copy when the code object is loaded there, held until the process
+// ends.  In host code `scratch` is only a handle: its device address is
+// looked up once per device (noalloc_scratch) and used everywhere instead.
+static __device__ __align__(256) unsigned char scratch[MOE_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[kMaxDevices];
+
+// Device address of this device's `scratch`, found with the device current
+// on the first call there and kept per device.
+int noalloc_scratch(void **out) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return MOE_ERR_HIP;
+  if (dev < 0 || dev >= kMaxDevices) return MOE_ERR_UNSUPPORTED;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void *p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return MOE_ERR_HIP;
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return MOE_OK;
 }
 
 }  // namespace
@@ -335,15 +389,41 @@ int moe_layer_forward_events(const moe_config *cfg, const moe_weights *w, const 
   if (st != MOE_OK) return st;
   if (!w) return MOE_ERR_INVALID_ARG;
   if (cfg->T == 0) return MOE_OK;
-  if (!x || !y || !w->w_router || !w->w1 || !w->w2) return MOE_ERR_INVALID_ARG;
-  if (cfg->n_shared > 0 && (!w->ws1 || !w->ws2)) return MOE_ERR_INVALID_ARG;
-  if (!all_aligned16({x, y, w->w_router, w->router_bias, w->w1, w->b1, w->w2, w->b2, w->ws1,
-                      w->bs1, w->ws2, w->bs2, topk_idx, topk_gate, counts, ws}))
-    return MOE_ERR_INVALID_ARG;
+  if ((st = check_layer_args(w, cfg, x, y, topk_idx, topk_gate, counts)) != MOE_OK) return st;
+  if (!aligned16(ws)) return MOE_ERR_INVALID_ARG;
   const LayerWs L = layer_ws(cfg, ws);
   if (!ws || ws_bytes < L.bytes) return MOE_ERR_WORKSPACE;
+  return run_layer(cfg, w, x, y, topk_idx, topk_gate, counts, L, stage_events,
+                   static_cast<hipStream_t>(stream));
+}
 
-  hipStream_t s = static_cast<hipStream_t>(stream);
+int moe_layer_forward_noalloc(const moe_config *cfg, const moe_weights *w, const void *x,
+                              void *y, int32_t *topk_idx, float *topk_gate, int32_t *counts,
+                              void *stream) {
+  int st = check_config(cfg, true, true);
+  if (st != MOE_OK) return st;
+  if (!w) return MOE_ERR_INVALID_ARG;
+  if (cfg->T == 0) return MOE_OK;
+  if ((st = check_layer_args(w, cfg, x, y, topk_idx, topk_gate, counts)) != MOE_OK) return st;
+  // everything but the K-split scratch must fit; that scratch gets the rest
+  const size_t need = layer_ws(cfg, nullptr, 0).bytes;
+  if (need > MOE_NOALLOC_SCRATCH_BYTES) return MOE_ERR_WORKSPACE;
+  void *base = nullptr;
+  if ((st = noalloc_scratch(&base)) != MOE_OK) return st;
+  const LayerWs L = layer_ws(cfg, base, MOE_NOALLOC_SCRATCH_BYTES - need);
+  if (L.bytes > MOE_NOALLOC_SCRATCH_BYTES) return MOE_ERR_WORKSPACE;   // not reached
+  return run_layer(cfg, w, x, y, topk_idx, topk_gate, counts, L, nullptr,
+                   static_cast<hipStream_t>(stream));
+}
+
+}  // extern "C"
+
+namespace {
+
+int run_layer(const moe_config *cfg, const moe_weights *w, const void *x, void *y,
+              int32_t *topk_idx, float *topk_gate, int32_t *counts, const LayerWs &L,
+              void *const *stage_events, hipStream_t s) {
+  int st = MOE_OK;
   const bool bf16 = cfg->dtype == MOE_BF16;
   const int64_t T = cfg->T;
   const int K = cfg->top_k, N = cfg->n_routed, Ks = cfg->n_shared;
@@ -391,7 +471,7 @@ int moe_layer_forward_events(const moe_config *cfg, const moe_weights *w, const 
   g.max_routed_rows = routed_rows_bound(cfg);
   g.max_group_rows = group_rows_bound(cfg);
   g.split_ws = L.split;
-  g.split_bytes = L.split ? layer_split_bytes(cfg) : 0;
+  g.split_bytes = L.split ? L.split_bytes : 0;
   if ((st = mark(MOE_STAGE_UP)) != MOE_OK) return st;
   st = hip_status(moe::launch_grouped_gemm(bf16, g, moe::kEpiBiasSilu, s));
   if (st != MOE_OK) return st;
@@ -420,4 +500,4 @@ int moe_layer_forward_events(const moe_config *cfg, const moe_weights *w, const 
   return mark(MOE_STAGE_COUNT);
 }
 
-}  // extern "C"
+}  // namespace

@@ -1,0 +1,105 @@
+"""moe_layer_forward_noalloc (the entry point that takes its workspace from
+the library's static device array) against moe_layer_forward on the same
+inputs, through the C interface: routing bit exact, outputs within the
+tolerance, on two calls in a row (the second with fewer tokens), and a layer
+too large for the array rejected before anything is enqueued."""
+import ctypes
+
+import numpy as np
+import pytest
+import torch
+
+import workloads as W
+import workloads.device  # noqa: F401  (device-resident instances)
+
+pytestmark = pytest.mark.gpu
+
+TOL = {"f32": 1e-5, "bf16": 1e-2}
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from sparse_mixture_experts_renormalised_amd import binding
+    binding.lib()
+    yield
+
+
+def rel_l2(a, b):
+    a = a.double().cpu().numpy()
+    b = b.double().cpu().numpy()
+    return float(np.linalg.norm(a - b) / max(np.linalg.norm(b), 1e-300))
+
+
+def run_both(B, dl, wl, T):
+    """The layer on the first T tokens, once per entry point."""
+    cfg = B.config(T, wl.d_model, wl.n_routed, wl.top_k, wl.n_shared, wl.d_ff, wl.dtype,
+                   wl.capacity_factor, selection_only_bias=wl.selection_only_bias)
+    x = dl.x[:T]
+    out = {}
+    for name in ("ws", "noalloc"):
+        y = torch.full((T, wl.d_model), float("nan"), dtype=dl.act, device="cuda")
+        idx = torch.full((T, wl.top_k), -7, dtype=torch.int32, device="cuda")
+        gate = torch.full((T, wl.top_k), float("nan"), dtype=torch.float32, device="cuda")
+        cnt = torch.full((wl.n_routed,), -7, dtype=torch.int32, device="cuda")
+        if name == "ws":
+            ws = torch.empty(B.workspace_size(cfg), dtype=torch.uint8, device="cuda")
+            B.layer_forward(cfg, dl.weights, x, y, idx, gate, cnt, ws)
+        else:
+            B.layer_forward_noalloc(cfg, dl.weights, x, y, idx, gate, cnt)
+        torch.cuda.synchronize()
+        out[name] = (y, idx, gate, cnt)
+    return out
+
+
+def compare(out, dtype, label):
+    (y0, i0, g0, c0), (y1, i1, g1, c1) = out["ws"], out["noalloc"]
+    assert torch.equal(i0, i1), label
+    assert torch.equal(c0, c1), label
+    assert torch.equal(g0, g1), label
+    assert torch.isfinite(y1.float()).all(), label
+    err = rel_l2(y1, y0)
+    print(f"[noalloc] {label}: rel_l2 vs workspace call {err:.3e}, "
+          f"bitwise equal {torch.equal(y0, y1)}", flush=True)
+    assert err <= TOL[dtype], label
+
+
+def test_noalloc_matches_layer_forward_on_two_calls():
+    from sparse_mixture_experts_renormalised_amd import binding as B
+    wl = W.get_workload("dsv3_decode")          # T = 128, DeepSeek-V3 widths, capacity 5
+    print(f"[noalloc] {wl.name}: T={wl.T} d={wl.d_model} N={wl.n_routed} K={wl.top_k}",
+          flush=True)
+    dl = W.device.DeviceLayer(wl)
+    compare(run_both(B, dl, wl, wl.T), wl.dtype, f"{wl.name} T={wl.T}")
+    # second call, fewer tokens (capacity 3): the array keeps the first
+    # call's contents, which must not leak into this one
+    compare(run_both(B, dl, wl, 40), wl.dtype, f"{wl.name} T=40")
+    del dl
+    torch.cuda.empty_cache()
+
+
+def test_noalloc_small_layers_back_to_back():
+    from sparse_mixture_experts_renormalised_amd import binding as B
+    for wl, T2 in ((W.get_workload("tiny_fp32"), 33),
+                   (W.custom_workload("noalloc_bf16", T=300, d_model=256, n_routed=16, top_k=4,
+                                      n_shared=1, d_ff=320, dtype="bf16", router_bias="gauss",
+                                      router_bias_var=0.5, capacity_factor=1.25), 77)):
+        print(f"[noalloc] {wl.name}: T={wl.T} then {T2}", flush=True)
+        dl = W.device.DeviceLayer(wl)
+        compare(run_both(B, dl, wl, wl.T), wl.dtype, f"{wl.name} T={wl.T}")
+        compare(run_both(B, dl, wl, T2), wl.dtype, f"{wl.name} T={T2}")
+
+
+def test_noalloc_rejects_a_layer_beyond_its_array():
+    from sparse_mixture_experts_renormalised_amd import binding as B
+    # the DeepSeek-V3-shaped prefill layer needs far more than the array: its
+    # hidden activations alone are 134 MB; rejected on the host, nothing runs
+    wl = W.get_workload("dsv3_prefill")
+    cfg = B.config(wl.T, wl.d_model, wl.n_routed, wl.top_k, wl.n_shared, wl.d_ff, wl.dtype)
+    assert B.workspace_size(cfg) > (64 << 20)
+    w = B.Weights(w_router=4096, w1=4096, w2=4096, ws1=4096, ws2=4096)
+    st = B.lib().moe_layer_forward_noalloc(ctypes.byref(cfg), ctypes.byref(w),
+                                           ctypes.c_void_p(4096), ctypes.c_void_p(4096),
+                                           None, None, None, None)
+    assert st == -3
