@@ -49,6 +49,18 @@ the design notes):
    the T*K routed assignments that go to expert j (so the f_j sum to 1 and a
    perfectly even routing gives L = alpha), P_j the mean over tokens of the
    full softmax over all N logits.
+10. FP8 dispatch ([DeepEP] section "DeepEP とは？", item 5, native FP8 data
+    dispatch that cuts transfer volume; section "DeepEP の性能", settings with
+    FP8 dispatch and BF16 combine).  The pages fix neither the FP8 format nor
+    the scaling, so: the dispatched token rows are OCP FP8 E4M3 (E4M3FN: sign,
+    4 exponent bits with bias 7, 3 mantissa bits; exponent field 0 holds the
+    subnormals m * 2^-9; largest finite value 448; no infinities), with one
+    power-of-two scale per token row, 2^E with E the smallest integer such
+    that max_k |x[t,k]| <= 448 * 2^E (E = 0 for an all-zero row).  Codes are
+    x / 2^E rounded to the nearest E4M3 value, ties to the even mantissa.
+    The routed experts consume the dispatched rows x~ = 2^E * value(code);
+    the router and the shared experts (which the pages keep on every device,
+    never dispatched) use x itself; the combine is unchanged (BF16).
 """
 from __future__ import annotations
 
@@ -66,6 +78,8 @@ __all__ = [
     "dispatch", "gather_rows", "silu", "expert_ffn", "grouped_ffn",
     "combine", "route", "layer_forward", "dense_masked_forward",
     "balance_statistics", "fmaf_array",
+    "e4m3_values", "round_e4m3", "fp8_scale_exponent", "quantize_fp8_rows",
+    "dequantize_fp8_rows",
 ]
 
 _LIB = None
@@ -226,6 +240,86 @@ def gather_rows(x: np.ndarray, row_token: np.ndarray) -> np.ndarray:
 
 
 # ---------------------------------------------------------------------------
+# FP8 dispatch: [DeepEP] "DeepEP とは？" item 5; reading 10
+# ---------------------------------------------------------------------------
+
+E4M3_MAX = 448.0
+
+
+def e4m3_values() -> np.ndarray:
+    """Value of every E4M3 code 0..255 (float64); NaN for the two NaN codes.
+
+    Code = sign (bit 7), exponent field e (bits 6..3, bias 7), mantissa m
+    (bits 2..0): e > 0 gives (1 + m/8) * 2^(e-7), e = 0 gives (m/8) * 2^-6;
+    e = 15 with m = 7 is NaN.
+    """
+    vals = np.empty(256, dtype=np.float64)
+    for c in range(256):
+        sign = -1.0 if c & 0x80 else 1.0
+        e = (c >> 3) & 0xF
+        m = c & 0x7
+        if e == 15 and m == 7:
+            vals[c] = np.nan
+        elif e == 0:
+            vals[c] = sign * (m / 8.0) * 2.0 ** -6
+        else:
+            vals[c] = sign * (1.0 + m / 8.0) * 2.0 ** (e - 7)
+    return vals
+
+
+def round_e4m3(v) -> np.ndarray:
+    """Codes (uint8) of the E4M3 values nearest to v (|v| <= 448), ties to the
+    code with the even mantissa; the sign bit follows v's sign (-0 -> 0x80).
+
+    Among the non-negative codes 0x00..0x7E the magnitudes ascend with the
+    code, so the two candidates are found by a search on |v|; the mantissa's
+    last bit is the code's last bit.
+    """
+    v = np.asarray(v, dtype=np.float64)
+    a = np.abs(v)
+    if np.any(a > E4M3_MAX) or np.any(np.isnan(a)):
+        raise ValueError("round_e4m3 takes finite values within +-448")
+    mags = e4m3_values()[:0x7F]                  # codes 0x00 .. 0x7E, ascending
+    hi = np.clip(np.searchsorted(mags, a, side="left"), 0, 0x7E)
+    lo = np.clip(hi - 1, 0, 0x7E)
+    d_lo = a - mags[lo]
+    d_hi = mags[hi] - a
+    pick_hi = (d_hi < d_lo) | ((d_hi == d_lo) & (hi % 2 == 0))
+    code = np.where(pick_hi, hi, lo).astype(np.uint8)
+    code[a == mags[hi]] = hi[a == mags[hi]]      # exact values
+    return code | np.where(np.signbit(v), 0x80, 0).astype(np.uint8)
+
+
+def fp8_scale_exponent(row) -> int:
+    """Smallest integer E with max|row| <= 448 * 2^E (0 for an all-zero row).
+
+    With max|row| = m * 2^e, m in [0.5, 1), and 448 = 0.875 * 2^9:
+    448 * 2^(e-9) >= max|row| exactly when m <= 0.875.
+    """
+    amax = float(np.max(np.abs(np.asarray(row, dtype=np.float64)))) if np.size(row) else 0.0
+    if amax == 0.0:
+        return 0
+    m, e = math.frexp(amax)
+    return e - 9 if m <= 0.875 else e - 8
+
+
+def quantize_fp8_rows(x):
+    """Per-token FP8 dispatch (reading 10): exponents E [T] (int32) and codes
+    q [T, d] (uint8) with q[t] = round_e4m3(x[t] / 2^E[t])."""
+    x = np.asarray(x, dtype=np.float64)
+    E = np.array([fp8_scale_exponent(r) for r in x], dtype=np.int32)
+    q = np.stack([round_e4m3(r / 2.0 ** int(e)) for r, e in zip(x, E)]) if len(x) else \
+        np.zeros(x.shape, dtype=np.uint8)
+    return E, q
+
+
+def dequantize_fp8_rows(E, q) -> np.ndarray:
+    """Dispatched rows x~[t, k] = 2^E[t] * value(q[t, k]) (float64, exact)."""
+    vals = e4m3_values()
+    return vals[np.asarray(q, dtype=np.int64)] * np.exp2(np.asarray(E, dtype=np.float64))[:, None]
+
+
+# ---------------------------------------------------------------------------
 # Experts: [DSMoE] reference layer (Linear - SiLU - Linear); reading 6
 # ---------------------------------------------------------------------------
 
@@ -300,13 +394,16 @@ def layer_forward(x, w_r, bias, routed_expert: Callable[[int], tuple],
                   n_shared: int, capacity_factor: float = 0.0,
                   capacity: Optional[int] = None,
                   tokens: Optional[Sequence[int]] = None,
-                  selection_only_bias: bool = False) -> Dict[str, np.ndarray]:
+                  selection_only_bias: bool = False,
+                  dispatch_fp8: bool = False) -> Dict[str, np.ndarray]:
     """Routing for all tokens and y for ``tokens`` (default: all), float64.
 
     The routing (logits, selection, gates, dispatch) always covers every token,
     because a token's rank in an expert depends on the earlier tokens.  Only
     the experts that the requested tokens keep are evaluated, each on just
     those tokens, so a handful of tokens of a large layer stays cheap.
+    With ``dispatch_fp8`` (reading 10) the routed experts take the dispatched
+    FP8 rows x~; the router and the shared experts take x.
     """
     x = np.asarray(x, dtype=np.float32)
     T = x.shape[0]
@@ -316,6 +413,12 @@ def layer_forward(x, w_r, bias, routed_expert: Callable[[int], tuple],
     disp = dispatch(idx, N, C)
     toks = np.arange(T) if tokens is None else np.asarray(tokens, dtype=np.int64)
     xs = x[toks].astype(np.float64)
+    xr = xs
+    fp8 = {}
+    if dispatch_fp8:
+        E, q = quantize_fp8_rows(x[toks])
+        xr = dequantize_fp8_rows(E, q)
+        fp8 = {"fp8_exp": E, "fp8_codes": q}
     y = np.zeros((len(toks), x.shape[1]), dtype=np.float64)
     for i in range(n_shared):
         w1, b1, w2, b2 = shared_expert(i)
@@ -328,22 +431,25 @@ def layer_forward(x, w_r, bias, routed_expert: Callable[[int], tuple],
         for k in range(top_k):
             m = (sel[:, k] == e) & (slot[:, k] >= 0)
             if m.any():
-                y[m] += g[m, k:k + 1] * expert_ffn(xs[m], w1, b1, w2, b2)
+                y[m] += g[m, k:k + 1] * expert_ffn(xr[m], w1, b1, w2, b2)
     out = dict(disp)
     out.update({"logits": logits, "topk_idx": idx, "gates": gates, "capacity": C,
                 "tokens": toks, "y": y})
+    out.update(fp8)
     return out
 
 
 def dense_masked_forward(x, w_r, bias, routed_expert, shared_expert, *, top_k: int,
                          n_shared: int, capacity_factor: float = 0.0,
                          capacity: Optional[int] = None,
-                         selection_only_bias: bool = False) -> np.ndarray:
+                         selection_only_bias: bool = False,
+                         dispatch_fp8: bool = False) -> np.ndarray:
     """Brute force in the shape of the pages' reference layer.
 
     Every routed expert is evaluated on every token; for each slot k and each
     expert e the output gains gate * mask(idx[:,k] == e, kept) * E_e(x).  It
     shares the routing with :func:`layer_forward` but none of its dispatch.
+    With ``dispatch_fp8`` the routed experts see the dispatched rows x~.
     """
     x = np.asarray(x, dtype=np.float32)
     T, d = x.shape
@@ -359,11 +465,12 @@ def dense_masked_forward(x, w_r, bias, routed_expert, shared_expert, *, top_k: i
                 earlier = int(np.sum(idx[:t] == e))
                 kept[t, k] = earlier < C
     xs = x.astype(np.float64)
+    xr = dequantize_fp8_rows(*quantize_fp8_rows(x)) if dispatch_fp8 else xs
     out = np.zeros((T, d), dtype=np.float64)
     for i in range(n_shared):
         out += expert_ffn(xs, *shared_expert(i))
     for e in range(N):
-        ye = expert_ffn(xs, *routed_expert(e))
+        ye = expert_ffn(xr, *routed_expert(e))
         for k in range(top_k):
             mask = ((idx[:, k] == e) & kept[:, k]).astype(np.float64)[:, None]
             out += gates[:, k:k + 1] * mask * ye

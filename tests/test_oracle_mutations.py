@@ -125,3 +125,50 @@ def test_assignment_share_over_tokens_instead_of_assignments_is_caught(monkeypat
         return f, P, float(alpha * N * np.sum(f * P))
     patch(monkeypatch, "balance_statistics", bad)
     expect_failure(pins.test_balance_statistics_invariants_and_even_routing)
+
+
+# ---------------------------------------------------------------------------
+# FP8 dispatch (reading 10)
+# ---------------------------------------------------------------------------
+import test_oracle_fp8 as fp8pins  # noqa: E402
+
+
+def test_e4m3_ties_away_from_zero_are_caught(monkeypatch):
+    orig = mo.round_e4m3
+
+    def bad(v):
+        v = np.asarray(v, dtype=np.float64)
+        c = orig(v)
+        vals = mo.e4m3_values()
+        up = np.minimum((c & 0x7F).astype(np.int64) + 1, 0x7E)
+        mid = (np.abs(vals[(c & 0x7F).astype(np.int64)]) + vals[up]) / 2
+        tie_down = np.abs(v) == mid                        # a tie rounded to the even code below
+        return np.where(tie_down, (up | (c & 0x80)).astype(np.uint8), c)
+    patch(monkeypatch, "round_e4m3", bad)
+    expect_failure(fp8pins.test_hand_rounded_codes)
+    expect_failure(fp8pins.test_rounding_matches_torch_cast)
+
+
+def test_e4m3_truncation_is_caught(monkeypatch):
+    def bad(v):
+        v = np.asarray(v, dtype=np.float64)
+        mags = mo.e4m3_values()[:0x7F]
+        code = np.clip(np.searchsorted(mags, np.abs(v), side="right") - 1, 0, 0x7E).astype(np.uint8)
+        return code | np.where(np.signbit(v), 0x80, 0).astype(np.uint8)
+    patch(monkeypatch, "round_e4m3", bad)
+    expect_failure(fp8pins.test_hand_rounded_codes)
+
+
+def test_scale_exponent_off_by_one_is_caught(monkeypatch):
+    orig = mo.fp8_scale_exponent
+    patch(monkeypatch, "fp8_scale_exponent", lambda row: orig(row) + 1)
+    expect_failure(fp8pins.test_scale_exponent_is_the_smallest_that_fits)
+    expect_failure(fp8pins.test_quantisation_error_bound)
+
+
+def test_dequantisation_without_the_scale_is_caught(monkeypatch):
+    def bad(E, q):
+        return mo.e4m3_values()[np.asarray(q, dtype=np.int64)]
+    patch(monkeypatch, "dequantize_fp8_rows", bad)
+    expect_failure(fp8pins.test_quantisation_error_bound)
+    expect_failure(fp8pins.test_fp8_dispatch_of_representable_rows_changes_nothing)
