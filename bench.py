@@ -44,6 +44,8 @@ def parse():
     p.add_argument("--warmup", type=int, default=5)
     p.add_argument("--workload", default=DEFAULT_WORKLOAD)
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--dispatch", choices=("bf16", "fp8"), default="bf16",
+                   help="precision of the routed experts' token rows (the FP8 dispatch mode)")
     p.add_argument("--only", action="store_true",
                    help="time only --workload (no per-config lines for the other workloads)")
     p.add_argument("--calibrate-copy", action="store_true",
@@ -88,14 +90,19 @@ def stage_work(wl, kept_rows: int, touched: int):
     T, d, f, N, K, Ks = wl.T, wl.d_model, wl.d_ff, wl.n_routed, wl.top_k, wl.n_shared
     a = wl.act_bytes
     R = kept_rows
+    fp8 = getattr(wl, "dispatch_fp8", False)
     w1_bytes = (touched + Ks) * f * d * a + ((touched + Ks) * f * a if wl.expert_bias else 0)
     w2_bytes = (touched + Ks) * d * f * a + ((touched + Ks) * d * a if wl.expert_bias else 0)
     return {
         "router": {"flops": 2 * T * d * N, "bytes": T * d * a + N * d * 4 + T * N * 4},
         "topk": {"flops": 0, "bytes": T * N * 4 + T * K * 8},
         "dispatch": {"flops": 0, "bytes": T * K * 4 * 3 + R * 4},
+        # with FP8 dispatch the routed rows arrive as one byte per element plus
+        # a 4-byte exponent, after a pass that reads x and writes the codes
         "up": {"flops": 2 * (R + Ks * T) * d * f,
-               "bytes": w1_bytes + (R + Ks * T) * (d + f) * a + R * 4},
+               "bytes": (w1_bytes + (R + Ks * T) * (d + f) * a + R * 4) if not fp8 else
+                        (w1_bytes + R * d + R * 4 + Ks * T * d * a + (R + Ks * T) * f * a
+                         + R * 4 + T * d * a + T * d + T * 4)},
         "down": {"flops": 2 * (R + Ks * T) * d * f,
                  "bytes": w2_bytes + (R + Ks * T) * (d + f) * a},
         "combine": {"flops": 0, "bytes": (R + Ks * T + T) * d * a + T * K * 8},
@@ -219,6 +226,7 @@ def measure(wl, steps: int, warmup: int, keep_layer: bool = False):
         "config": {"workload": wl.name, "T": wl.T, "d_model": wl.d_model,
                    "n_routed": wl.n_routed, "top_k": wl.top_k, "n_shared": wl.n_shared,
                    "d_ff": wl.d_ff, "capacity_factor": wl.capacity_factor,
+                   "dispatch": "fp8" if wl.dispatch_fp8 else "bf16",
                    "kept_rows": kept, "experts_touched": touched},
         "roofline": roofline(wl, work, stage_ms),
         # algorithmic bytes of the whole layer over its wall time per step
@@ -256,6 +264,8 @@ def main():
 
     torch.cuda.set_device(0)
     wl = W.get_workload(args.workload)
+    if args.dispatch == "fp8":
+        wl = wl.with_(dispatch_fp8=True)
     head, dl = measure(wl, args.steps, args.warmup, keep_layer=not args.no_cpu_baseline)
     cpu = None
     if dl is not None:
@@ -272,7 +282,9 @@ def main():
             # the tiny float32 layer is a parity case (launch-bound), not a bench line
             if name == wl.name or name == "tiny_fp32":
                 continue
-            r, _ = measure(W.get_workload(name), args.steps, args.warmup)
+            w = W.get_workload(name)
+            r, _ = measure(w.with_(dispatch_fp8=True) if args.dispatch == "fp8" else w,
+                           args.steps, args.warmup)
             per_config[name] = r
 
     out = {

@@ -98,7 +98,23 @@ typedef struct {
     float capacity_factor;    /* <= 0: no factor-derived limit                     */
     int32_t capacity;         /* >= 0: explicit per-expert limit; -1: use factor   */
     int32_t bias_mode;        /* MOE_BIAS_IN_LOGIT or MOE_BIAS_SELECTION_ONLY      */
+    int32_t dispatch;         /* MOE_DISPATCH_BF16 or MOE_DISPATCH_FP8             */
 } moe_config;
+
+/* Precision of the token rows the routed experts receive (the dispatch).
+ *   MOE_DISPATCH_BF16: the rows as given (act dtype).
+ *   MOE_DISPATCH_FP8: the FP8 dispatch of [DeepEP] ("DeepEP とは？" item 5;
+ *     "DeepEP の性能": FP8 dispatch, BF16 combine).  Each token row is sent as
+ *     OCP FP8 E4M3 codes (bias 7, 3 mantissa bits, largest value 448) with one
+ *     power-of-two scale 2^E per row, E the smallest integer with
+ *     max|x[t]| <= 448 * 2^E (0 for an all-zero row); codes are x / 2^E
+ *     rounded to nearest, ties to even.  The routed experts' first Linear
+ *     reads the codes through the dispatch permutation and widens them to
+ *     bf16 (exactly 2^E * code value) on chip; the router and the shared
+ *     experts use x; the combine is unchanged (bf16).  MOE_BF16 layers only
+ *     (MOE_ERR_UNSUPPORTED otherwise); honoured by moe_layer_forward and
+ *     moe_layer_forward_noalloc, ignored by the other entry points. */
+enum { MOE_DISPATCH_BF16 = 0, MOE_DISPATCH_FP8 = 1 };
 
 /* How router_bias enters the routing.
  *   MOE_BIAS_IN_LOGIT: the bias is part of the logit, for selection and gates.
@@ -269,6 +285,8 @@ typedef struct {
     size_t n_dropped;   /* [1] int32                                          */
     size_t row_token;   /* [T*K] int32 (rows 0 .. offsets[N]-1 hold tokens)   */
     size_t slot_row;    /* [T][K] int32 (-1 = dropped)                        */
+    size_t x_fp8;       /* MOE_DISPATCH_FP8: [T][d] uint8 E4M3 codes, else 0  */
+    size_t x_fp8_exp;   /* MOE_DISPATCH_FP8: [T] int32 scale exponents, else 0 */
     size_t total;       /* moe_workspace_size(cfg)                            */
 } moe_ws_layout;
 

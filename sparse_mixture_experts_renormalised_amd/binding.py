@@ -43,14 +43,15 @@ class Config(ctypes.Structure):
     _fields_ = [("T", ctypes.c_int64), ("d_model", ctypes.c_int32), ("n_routed", ctypes.c_int32),
                 ("top_k", ctypes.c_int32), ("n_shared", ctypes.c_int32), ("d_ff", ctypes.c_int32),
                 ("dtype", ctypes.c_int32), ("capacity_factor", ctypes.c_float),
-                ("capacity", ctypes.c_int32), ("bias_mode", ctypes.c_int32)]
+                ("capacity", ctypes.c_int32), ("bias_mode", ctypes.c_int32),
+                ("dispatch", ctypes.c_int32)]
 
 
 class WsLayout(ctypes.Structure):
     """Mirror of moe_ws_layout (byte offsets into the layer workspace)."""
     _fields_ = [(n, ctypes.c_size_t) for n in
                 ("logits", "topk_idx", "topk_gate", "counts", "offsets", "n_dropped", "row_token",
-                 "slot_row", "total")]
+                 "slot_row", "x_fp8", "x_fp8_exp", "total")]
 
 
 class Weights(ctypes.Structure):
@@ -118,14 +119,16 @@ def _check(fn: str, st: int):
 
 
 MOE_BIAS_IN_LOGIT, MOE_BIAS_SELECTION_ONLY = 0, 1
+MOE_DISPATCH_BF16, MOE_DISPATCH_FP8 = 0, 1
 
 
 def config(T, d_model, n_routed, top_k, n_shared, d_ff, dtype, capacity_factor=0.0,
-           capacity=-1, selection_only_bias=False) -> Config:
+           capacity=-1, selection_only_bias=False, dispatch_fp8=False) -> Config:
     dt = {"f32": MOE_F32, "bf16": MOE_BF16, MOE_F32: MOE_F32, MOE_BF16: MOE_BF16}[dtype]
     return Config(int(T), int(d_model), int(n_routed), int(top_k), int(n_shared), int(d_ff),
                   dt, float(capacity_factor), int(capacity),
-                  MOE_BIAS_SELECTION_ONLY if selection_only_bias else MOE_BIAS_IN_LOGIT)
+                  MOE_BIAS_SELECTION_ONLY if selection_only_bias else MOE_BIAS_IN_LOGIT,
+                  MOE_DISPATCH_FP8 if dispatch_fp8 else MOE_DISPATCH_BF16)
 
 
 def capacity(cfg: Config) -> int:

@@ -71,6 +71,11 @@ struct GemmArgs {
   // kernels can split one grouped product by group size.
   int64_t cls_lo;
   int64_t cls_hi;
+  // FP8-dispatched A rows of the routed groups (stream kernel's FP8 form):
+  // E4M3 codes [rows of A][K] gathered through a_index, and the power-of-two
+  // exponent of each A row; the rows are widened to bf16 x 2^E in LDS.
+  const uint8_t *A8;
+  const int32_t *a8_exp;
 };
 
 __device__ __forceinline__ int64_t group_rows(const GemmArgs &a, int g) {
@@ -199,6 +204,23 @@ __device__ __forceinline__ const T *a_row_ptr(const GemmArgs &a, const TileView<
   return static_cast<const T *>(a.A_sh) + static_cast<int64_t>(gs) * a.a_sh_stride + r * a.K;
 }
 
+// FP8 code row of local row r of a routed group (clamped into the group),
+// and that row's power-of-two exponent.
+__device__ __forceinline__ const uint8_t *a8_row_ptr(const GemmArgs &a,
+                                                     const TileView<uint16_t> &v, int64_t r) {
+  if (r >= v.rows) r = v.rows - 1;
+  const int64_t gr = v.out_base + r;
+  const int64_t src = a.a_index ? static_cast<int64_t>(a.a_index[gr]) : gr;
+  return a.A8 + src * a.K;
+}
+__device__ __forceinline__ int a8_row_exp(const GemmArgs &a, const TileView<uint16_t> &v,
+                                          int64_t r) {
+  if (r >= v.rows) r = v.rows - 1;
+  const int64_t gr = v.out_base + r;
+  const int64_t src = a.a_index ? static_cast<int64_t>(a.a_index[gr]) : gr;
+  return a.a8_exp[src];
+}
+
 // Decode a linear tile index into (m-tile, n-tile), banded by GM m-tiles.
 template <int GM>
 __device__ __forceinline__ void decode_tile(int L, int total_m, int n_nt, int *mt, int *nt) {
@@ -232,6 +254,12 @@ __device__ __forceinline__ void dma16(const uint16_t *src, uint32_t m0) {
 // raises the sustained read rate from about 6.1 to 7.2 TB/s on MI355X.
 __device__ __forceinline__ void dma16_nt(const uint16_t *src, uint32_t m0) {
   asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, off nt" : : "v"(src), "{m0}"(m0) : "memory");
+}
+
+// A four-byte-per-lane LDS DMA (64 lanes x 4 B into the 256 B at m0), for
+// rows of FP8 codes.
+__device__ __forceinline__ void dma4(const uint8_t *src, uint32_t m0) {
+  asm volatile("s_nop 0\n\tglobal_load_lds_dword %0, off" : : "v"(src), "{m0}"(m0) : "memory");
 }
 
 // The same copy addressed as a wave-uniform 64-bit base in SGPRs plus a 32-bit
@@ -1295,7 +1323,7 @@ __device__ __forceinline__ void stream_store(const f32x16_t (&acc)[MB][NTB], con
 // features nb*128*MB .., K part kp of kc_per chunks.  Ring stages are STRIDE
 // bf16 elements apart; `stage` is the ring position of the next chunk,
 // carried from unit to unit of one workgroup.
-template <int MB, int NTB, int S, int STRIDE, int EPI>
+template <int MB, int NTB, int S, int STRIDE, int EPI, bool FP8, int MR2>
 __device__ __forceinline__ void stream_unit(const GemmArgs &a, const StreamSplit &sp, int g,
                                             int mg, int nb, int rb, int kp, int ks, int kc_per,
                                             uint16_t *s_ring, uint32_t ring0, int &stage,
@@ -1304,9 +1332,15 @@ __device__ __forceinline__ void stream_unit(const GemmArgs &a, const StreamSplit
   constexpr int MR = 32 * NTB;                   // rows per unit
   constexpr int NB = 4 * 32 * MB;                // features per unit
   constexpr int W_INS = NB / 8 / NW;             // weight copies per wave per chunk
-  constexpr int X_INS = MR / 8 / NW;             // activation copies per wave per chunk
+  // activation copies per wave per chunk: 16-byte copies of bf16 rows, or
+  // 4-byte copies of FP8 rows (64 bytes a row) into the slot's staging area
+  constexpr int X_INS = FP8 ? MR / 16 : MR / 8 / NW;
   constexpr int LPS = W_INS + X_INS;
-  static_assert((NB + MR) * KCH <= STRIDE, "stage fits its ring slot");
+  // slot layout: weights [NB][KCH], activations [MR2][KCH] (bf16, swizzled),
+  // then, for FP8 rows, their codes [MR2][64] bytes
+  constexpr int STAGE8 = (NB + MR2) * KCH * 2;   // byte offset of the FP8 staging area
+  static_assert((NB + MR) * KCH + (FP8 ? MR2 * KCH / 2 : 0) <= STRIDE, "stage fits its ring slot");
+  static_assert(MR <= MR2, "unit height");
   static_assert((S - 2) * LPS <= 63, "vmcnt range");
   const int r32 = lane & 31, h = lane >> 5;
   const int nkc = a.K / KCH;
@@ -1319,17 +1353,33 @@ __device__ __forceinline__ void stream_unit(const GemmArgs &a, const StreamSplit
 
   // sources of this wave's copies (chunk 0 of the part)
   const uint16_t *w_src[W_INS];
-  const uint16_t *x_src[X_INS];
+  const uint16_t *x_src[FP8 ? 1 : X_INS];
+  const uint8_t *x8_src[FP8 ? X_INS : 1];
 #pragma unroll
   for (int i = 0; i < W_INS; ++i) {
     const int r = (i * NW + wave) * 8 + crow;
     const int n = min(n0 + r, a.Nout - 1);
     w_src[i] = v.W + static_cast<int64_t>(n) * a.K + kc0 * KCH + swz(r, cpos) * 8;
   }
+  // FP8 rows: copy i of wave w moves staging bytes (i NW + w) * 256 .. +255,
+  // rows 4 (i NW + w) + lane/16, bytes 4 (lane % 16) .. +3 of the row's chunk
+  float x8_scale[FP8 ? MR / 32 : 1];
+  if constexpr (FP8) {
 #pragma unroll
-  for (int i = 0; i < X_INS; ++i) {
-    const int r = (i * NW + wave) * 8 + crow;
-    x_src[i] = a_row_ptr(a, v, v.row0 + r) + kc0 * KCH + swz(r, cpos) * 8;
+    for (int i = 0; i < X_INS; ++i) {
+      const int r = (i * NW + wave) * 4 + (lane >> 4);
+      x8_src[i] = a8_row_ptr(a, v, v.row0 + r) + kc0 * KCH + (lane & 15) * 4;
+    }
+    // the rows this thread widens: (tid / 8) + 32 j
+#pragma unroll
+    for (int j = 0; j < MR / 32; ++j)
+      x8_scale[j] = __builtin_ldexpf(1.0f, a8_row_exp(a, v, v.row0 + (wave * 64 + lane) / 8 + 32 * j));
+  } else {
+#pragma unroll
+    for (int i = 0; i < X_INS; ++i) {
+      const int r = (i * NW + wave) * 8 + crow;
+      x_src[i] = a_row_ptr(a, v, v.row0 + r) + kc0 * KCH + swz(r, cpos) * 8;
+    }
   }
   // weights of a group with one row block are read once: stream them
   const bool w_once = mg == 1;
@@ -1342,9 +1392,15 @@ __device__ __forceinline__ void stream_unit(const GemmArgs &a, const StreamSplit
 #pragma unroll
       for (int i = 0; i < W_INS; ++i) dma16(w_src[i] + c * KCH, base + (i * NW + wave) * 1024);
     }
+    if constexpr (FP8) {
 #pragma unroll
-    for (int i = 0; i < X_INS; ++i)
-      dma16(x_src[i] + c * KCH, base + NB * KCH * 2 + (i * NW + wave) * 1024);
+      for (int i = 0; i < X_INS; ++i)
+        dma::dma4(x8_src[i] + c * KCH, base + STAGE8 + (i * NW + wave) * 256);
+    } else {
+#pragma unroll
+      for (int i = 0; i < X_INS; ++i)
+        dma16(x_src[i] + c * KCH, base + NB * KCH * 2 + (i * NW + wave) * 1024);
+    }
   };
 
   f32x16_t acc[MB][NTB];
@@ -1366,6 +1422,33 @@ __device__ __forceinline__ void stream_unit(const GemmArgs &a, const StreamSplit
     if (c + S - 1 < nch) issue(c + S - 1, (stage + c + S - 1) % S);
     const uint16_t *sw = s_ring + cur * STRIDE;
     const uint16_t *sx = sw + NB * KCH;
+    if constexpr (FP8) {
+      // widen the chunk's FP8 rows into the slot's bf16 activation rows:
+      // thread t takes 8 codes of row t/8 + 32 j (logical piece t % 8) and
+      // writes them, times the row's scale, where the swizzle puts that piece
+      const uint8_t *s8 = reinterpret_cast<const uint8_t *>(sw) + STAGE8;
+      uint16_t *sxw = const_cast<uint16_t *>(sx);
+      const int tid = wave * 64 + lane;
+#pragma unroll
+      for (int j = 0; j < MR / 32; ++j) {
+        const int r = tid / 8 + 32 * j, lc = tid & 7;
+        const uint2 cw = *reinterpret_cast<const uint2 *>(s8 + r * 64 + lc * 8);
+        uint4 o;
+        uint32_t *op = reinterpret_cast<uint32_t *>(&o);
+        const uint32_t w2[2] = {cw.x, cw.y};
+#pragma unroll
+        for (int h2 = 0; h2 < 2; ++h2) {
+          const f32x2_t lo = __builtin_amdgcn_cvt_pk_f32_fp8(static_cast<int>(w2[h2]), false);
+          const f32x2_t hi = __builtin_amdgcn_cvt_pk_f32_fp8(static_cast<int>(w2[h2]), true);
+          op[2 * h2] = pack_bf16x2(lo.x * x8_scale[j], lo.y * x8_scale[j]);
+          op[2 * h2 + 1] = pack_bf16x2(hi.x * x8_scale[j], hi.y * x8_scale[j]);
+        }
+        *reinterpret_cast<uint4 *>(sxw + r * KCH + swz(r, lc) * 8) = o;
+      }
+      // every wave's widened rows are in LDS (LDS only: the copies of later
+      // chunks stay in flight)
+      asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    }
 #pragma unroll
     for (int kst = 0; kst < 4; ++kst) {
       const int p = 2 * kst + h;
@@ -1396,12 +1479,13 @@ __device__ __forceinline__ void stream_unit(const GemmArgs &a, const StreamSplit
 // 32*NTB rows take units of 32*NTB2 rows, so a group of up to 32*NTB2 rows
 // reads each weight block once.  Both shapes share the ring (slots sized
 // for the larger stage) and its position.
-template <int MB, int NTB, int NTB2, int S, int EPI>
+template <int MB, int NTB, int NTB2, int S, int EPI, bool FP8 = false>
 __global__ __launch_bounds__(256) void grouped_gemm_bf16_stream_kernel(GemmArgs a, StreamSplit sp) {
   using namespace st;
   constexpr int MR1 = 32 * NTB, MR2 = 32 * (NTB2 > NTB ? NTB2 : NTB);
   constexpr int NB = 4 * 32 * MB;
-  constexpr int STRIDE = (NB + MR2) * KCH;
+  // slot: weights and bf16 activation rows, plus the FP8 staging rows
+  constexpr int STRIDE = (NB + MR2) * KCH + (FP8 ? MR2 * KCH / 2 : 0);
   __shared__ __attribute__((aligned(16))) uint16_t s_ring[S * STRIDE];
   __shared__ int s_pref[kMaxGroups + 1];
   __shared__ int s_tmp[NT / 64];
@@ -1431,12 +1515,11 @@ __global__ __launch_bounds__(256) void grouped_gemm_bf16_stream_kernel(GemmArgs 
     const int uu = u - s_pref[g] * n_nb;
     const int nb = uu / mg, rb = uu % mg;
     if (NTB2 <= NTB || group_rows(a, g) <= MR1)
-      stream_unit<MB, NTB, S, STRIDE, EPI>(a, sp, g, mg, nb, rb, kp, ks_u, per, s_ring, ring0,
-                                           stage, lane, wave, piece);
+      stream_unit<MB, NTB, S, STRIDE, EPI, FP8, MR2>(a, sp, g, mg, nb, rb, kp, ks_u, per, s_ring,
+                                                     ring0, stage, lane, wave, piece);
     else
-      stream_unit<MB, (NTB2 > NTB ? NTB2 : NTB), S, STRIDE, EPI>(a, sp, g, mg, nb, rb, kp, ks_u,
-                                                                 per, s_ring, ring0, stage, lane,
-                                                                 wave, piece);
+      stream_unit<MB, (NTB2 > NTB ? NTB2 : NTB), S, STRIDE, EPI, FP8, MR2>(
+          a, sp, g, mg, nb, rb, kp, ks_u, per, s_ring, ring0, stage, lane, wave, piece);
   };
   // unit order: part fastest, then row block, then feature block, so the
   // workgroups running together share a weight block in L2
@@ -1706,6 +1789,8 @@ GemmArgs make_args(const GemmGroups &g) {
   a.K = g.K;
   a.cls_lo = 0;
   a.cls_hi = INT64_MAX;
+  a.A8 = g.A8;
+  a.a8_exp = g.a8_exp;
   return a;
 }
 
@@ -1732,7 +1817,7 @@ int64_t split_rows(const GemmGroups &g) {
   return g.max_routed_rows + static_cast<int64_t>(g.n_shared) * g.T_sh;
 }
 
-template <int MB, int NTB, int S, int NTB2 = 0>
+template <int MB, int NTB, int S, int NTB2 = 0, bool FP8 = false>
 hipError_t launch_bf16_stream(const GemmArgs &a, const GemmGroups &g, Epilogue epi, int per_cu,
                               hipStream_t s) {
   // scratch: [0, 256) the split the kernel chose; then the last-round piece
@@ -1758,11 +1843,11 @@ hipError_t launch_bf16_stream(const GemmArgs &a, const GemmGroups &g, Epilogue e
   const unsigned grid =
       persistent_grid(tiles_upper_bound(g, 32 * NTB, 128 * MB) * sp.ks_cap, per_cu);
   if (epi == kEpiBiasSilu)
-    hipLaunchKernelGGL((grouped_gemm_bf16_stream_kernel<MB, NTB, NTB2, S, kEpiBiasSilu>),
+    hipLaunchKernelGGL((grouped_gemm_bf16_stream_kernel<MB, NTB, NTB2, S, kEpiBiasSilu, FP8>),
                        dim3(grid), dim3(256), 0, s, a, sp);
   else
-    hipLaunchKernelGGL((grouped_gemm_bf16_stream_kernel<MB, NTB, NTB2, S, kEpiBias>), dim3(grid),
-                       dim3(256), 0, s, a, sp);
+    hipLaunchKernelGGL((grouped_gemm_bf16_stream_kernel<MB, NTB, NTB2, S, kEpiBias, FP8>),
+                       dim3(grid), dim3(256), 0, s, a, sp);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || !sp.ks_used) return e;
   // fpu workgroups per possible last-round unit (at most half of each XCD's
@@ -1852,6 +1937,16 @@ size_t grouped_gemm_split_bytes(const GemmGroups &g) {
 hipError_t launch_grouped_gemm(bool bf16, const GemmGroups &g, Epilogue epi, hipStream_t s) {
   GemmArgs a = make_args(g);
   if (g.n_routed + g.n_shared <= 0 || g.Nout <= 0) return hipSuccess;
+  if (g.A8) {
+    // FP8-dispatched rows of routed groups (no shared groups in this launch):
+    // the stream kernel at every group size, its activation rows widened in
+    // LDS; decode-sized groups take the deep 32-row ring, others 64- and
+    // 128-row units of 128 features (the staging rows leave no room for 256)
+    if (!bf16 || g.n_shared != 0 || g.K % 64 != 0 || g.Nout % 4 != 0 || !g.a8_exp)
+      return hipErrorInvalidValue;
+    if (g.max_group_rows <= 32) return launch_bf16_stream<1, 1, 6, 0, true>(a, g, epi, 1, s);
+    return launch_bf16_stream<1, 2, 3, 4, true>(a, g, epi, 1, s);
+  }
   if (bf16 && g.K % 64 == 0 && g.Nout % 4 == 0) {
     // Groups of up to kStreamRows rows are bound by their weight stream and
     // go to the stream kernel (units of 64 rows up to 64 rows, else 128, so

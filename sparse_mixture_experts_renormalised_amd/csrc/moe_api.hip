@@ -46,6 +46,9 @@ int check_config(const moe_config *c, bool need_route, bool need_ffn) {
     if (c->bias_mode != MOE_BIAS_IN_LOGIT && c->bias_mode != MOE_BIAS_SELECTION_ONLY)
       return MOE_ERR_INVALID_ARG;
   }
+  if (c->dispatch != MOE_DISPATCH_BF16 && c->dispatch != MOE_DISPATCH_FP8)
+    return MOE_ERR_INVALID_ARG;
+  if (c->dispatch == MOE_DISPATCH_FP8 && c->dtype != MOE_BF16) return MOE_ERR_UNSUPPORTED;
   if (need_ffn) {
     if (c->d_ff <= 0) return MOE_ERR_INVALID_ARG;
     if (c->d_ff % mult != 0) return MOE_ERR_UNSUPPORTED;
@@ -82,6 +85,8 @@ struct LayerWs {
   void *s_out;   // shared outputs [Ks][T][d]
   void *split;   // k-split scratch of the expert GEMMs (may be empty)
   size_t split_bytes;
+  uint8_t *xq;     // FP8 dispatch: E4M3 codes [T][d] (else null)
+  int32_t *xexp;   // FP8 dispatch: scale exponents [T] (else null)
   size_t bytes;
 };
 
@@ -138,6 +143,9 @@ LayerWs layer_ws(const moe_config *c, void *base, size_t split_cap = SIZE_MAX) {
   w.h_sh = take(ab * Ks * T * c->d_ff);
   w.y_rows = take(ab * T * K * c->d_model);
   w.s_out = take(ab * Ks * T * c->d_model);
+  const bool fp8 = c->dispatch == MOE_DISPATCH_FP8;
+  w.xq = fp8 ? static_cast<uint8_t *>(take(static_cast<size_t>(T) * c->d_model)) : nullptr;
+  w.xexp = fp8 ? static_cast<int32_t *>(take(sizeof(int32_t) * T)) : nullptr;
   size_t sb = layer_split_bytes(c);
   if (sb > split_cap) sb = split_cap & ~(kAlign - 1);
   w.split = sb ? take(sb) : nullptr;
@@ -370,6 +378,8 @@ int moe_workspace_layout(const moe_config *cfg, moe_ws_layout *out) {
   out->n_dropped = off(L.n_dropped);
   out->row_token = off(L.row_token);
   out->slot_row = off(L.slot_row);
+  out->x_fp8 = L.xq ? off(L.xq) : 0;
+  out->x_fp8_exp = L.xexp ? off(L.xexp) : 0;
   out->total = L.bytes;
   return MOE_OK;
 }
@@ -473,8 +483,31 @@ int run_layer(const moe_config *cfg, const moe_weights *w, const void *x, void *
   g.split_ws = L.split;
   g.split_bytes = L.split ? L.split_bytes : 0;
   if ((st = mark(MOE_STAGE_UP)) != MOE_OK) return st;
-  st = hip_status(moe::launch_grouped_gemm(bf16, g, moe::kEpiBiasSilu, s));
-  if (st != MOE_OK) return st;
+  if (cfg->dispatch == MOE_DISPATCH_FP8) {
+    // FP8 dispatch: the routed rows go out as E4M3 codes with a per-row
+    // scale and are widened in the first Linear; the shared experts, which
+    // are not dispatched, take x in its own launch
+    st = hip_status(moe::launch_quantize_fp8(x, T, cfg->d_model, L.xq, L.xexp, s));
+    if (st != MOE_OK) return st;
+    GemmGroups gr = g;
+    gr.n_shared = 0;
+    gr.A8 = L.xq;
+    gr.a8_exp = L.xexp;
+    st = hip_status(moe::launch_grouped_gemm(bf16, gr, moe::kEpiBiasSilu, s));
+    if (st != MOE_OK) return st;
+    if (Ks > 0) {
+      GemmGroups gs = g;
+      gs.n_routed = 0;
+      gs.a_index = nullptr;
+      gs.max_routed_rows = 0;
+      gs.max_group_rows = 0;
+      st = hip_status(moe::launch_grouped_gemm(bf16, gs, moe::kEpiBiasSilu, s));
+      if (st != MOE_OK) return st;
+    }
+  } else {
+    st = hip_status(moe::launch_grouped_gemm(bf16, g, moe::kEpiBiasSilu, s));
+    if (st != MOE_OK) return st;
+  }
 
   // Second Linear.
   g.A = L.h;

@@ -182,7 +182,8 @@ class Workload:
     "zipf" (deterministic, bias[e] = -s*ln(e+1)).
     ``capacity_factor <= 0`` means no per-expert limit.
     ``selection_only_bias`` marks a router bias that enters the selection key
-    only (the gates then use the unbiased logits).
+    only (the gates then use the unbiased logits).  ``dispatch_fp8`` sends
+    the routed experts' token rows as FP8 (E4M3 with a per-row scale).
     """
     name: str
     T: int
@@ -198,6 +199,7 @@ class Workload:
     router_bias_var: float = 0.0
     zipf_s: float = 0.0
     selection_only_bias: bool = False
+    dispatch_fp8: bool = False
     seed: int = 0
     description: str = field(default="", compare=False)
 

@@ -23,7 +23,8 @@ class DeviceLayer:
         self.act = torch.bfloat16 if wl.dtype == "bf16" else torch.float32
         self.cfg = B.config(wl.T, wl.d_model, wl.n_routed, wl.top_k, wl.n_shared, wl.d_ff,
                             wl.dtype, wl.capacity_factor,
-                            selection_only_bias=wl.selection_only_bias)
+                            selection_only_bias=wl.selection_only_bias,
+                            dispatch_fp8=wl.dispatch_fp8)
         self.x = wl.x(dev)
         self.w_router = wl.w_router(dev)
         self.router_bias = wl.router_bias_values(dev)
@@ -65,7 +66,11 @@ class DeviceLayer:
 
         offsets = region(lay.offsets, N + 1, torch.int32)
         R = int(offsets[-1])
-        return {
+        out = {}
+        if lay.x_fp8:
+            out["fp8_codes"] = region(lay.x_fp8, T * wl.d_model, torch.uint8).reshape(T, wl.d_model)
+            out["fp8_exp"] = region(lay.x_fp8_exp, T, torch.int32)
+        return out | {
             "logits": region(lay.logits, T * N, torch.float32).reshape(T, N),
             "offsets": offsets,
             "n_dropped": int(region(lay.n_dropped, 1, torch.int32)[0]),
