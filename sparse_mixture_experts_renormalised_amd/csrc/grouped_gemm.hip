@@ -366,6 +366,23 @@ __device__ __forceinline__ void lds_barrier() {
 // tile).  Such a tile is computed as H x 256 (H = 128 or 64) by all four
 // waves (2 x 2 waves of H/2 x 128) instead of leaving waves to multiply
 // padding rows: same operand path and swizzle, H/256 of the A rows and MFMAs.
+// Eight E4M3 codes (bytes of cw, element order) widened to bf16 times the
+// row's scale sc, a power of two: each code's value is exact in float32
+// (v_cvt_pk_f32_fp8 reads two codes), the product by 2^E is exact, and the
+// result, at most 4 significant bits, is exact in bf16.
+__device__ __forceinline__ u32x4_t widen_fp8x8(uint2 cw, float sc) {
+  u32x4_t o;
+  const uint32_t w2[2] = {cw.x, cw.y};
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const f32x2_t lo = __builtin_amdgcn_cvt_pk_f32_fp8(static_cast<int>(w2[h]), false);
+    const f32x2_t hi = __builtin_amdgcn_cvt_pk_f32_fp8(static_cast<int>(w2[h]), true);
+    o[2 * h] = pack_bf16x2(lo.x * sc, lo.y * sc);
+    o[2 * h + 1] = pack_bf16x2(hi.x * sc, hi.y * sc);
+  }
+  return o;
+}
+
 template <int H>
 struct Rh {
 static constexpr int BM = H, BN = 256, BK = 64, NT = 256, WTM = H / 2, WTN = 128;
@@ -385,6 +402,32 @@ static __device__ __forceinline__ void gload(u32x4_t (&ra)[A_CH], u32x4_t (&rb)[
   for (int i = 0; i < A_CH; ++i) ra[i] = *reinterpret_cast<const u32x4_t *>(a_src[i] + kb * BK);
 #pragma unroll
   for (int i = 0; i < B_CH; ++i) rb[i] = *reinterpret_cast<const u32x4_t *>(b_src[i] + kb * BK);
+}
+
+// FP8 A rows: 8 codes (8 bytes) per 8-element piece, widened when stored.
+static __device__ __forceinline__ void gload8(uint2 (&ra)[A_CH], u32x4_t (&rb)[B_CH],
+                                       const uint8_t *const (&a_src)[A_CH],
+                                       const uint16_t *const (&b_src)[B_CH], int kb) {
+#pragma unroll
+  for (int i = 0; i < A_CH; ++i) ra[i] = *reinterpret_cast<const uint2 *>(a_src[i] + kb * BK);
+#pragma unroll
+  for (int i = 0; i < B_CH; ++i) rb[i] = *reinterpret_cast<const u32x4_t *>(b_src[i] + kb * BK);
+}
+
+static __device__ __forceinline__ void lstore8(uint16_t *tile, const uint2 (&ra)[A_CH],
+                                        const float (&sc)[A_CH], const u32x4_t (&rb)[B_CH],
+                                        int tid) {
+  const int kc = tid & 7;
+#pragma unroll
+  for (int i = 0; i < A_CH; ++i) {
+    const int row = (tid >> 3) + i * (NT / 8);
+    *reinterpret_cast<u32x4_t *>(tile + row * BK + (swz(row, kc) << 3)) = widen_fp8x8(ra[i], sc[i]);
+  }
+#pragma unroll
+  for (int i = 0; i < B_CH; ++i) {
+    const int row = (tid >> 3) + i * (NT / 8);
+    *reinterpret_cast<u32x4_t *>(tile + BM * BK + row * BK + (swz(row, kc) << 3)) = rb[i];
+  }
 }
 
 static __device__ __forceinline__ void lstore(uint16_t *tile, const u32x4_t (&ra)[A_CH],
@@ -459,6 +502,11 @@ static __device__ __forceinline__ void schedule_step() {
 static __device__ __forceinline__ void tile(const GemmArgs &a, const TileView<uint16_t> &v, int n0,
                                             int k0, int nk, uint16_t *s_tile, int tid, int lane,
                                             int wm, int wn, f32x16_t (&acc)[TN][TM]);
+// The same with the A rows read as FP8 codes (a.A8, a.a8_exp) and widened.
+static __device__ __forceinline__ void tile_fp8(const GemmArgs &a, const TileView<uint16_t> &v,
+                                                int n0, int nk, uint16_t *s_tile, int tid,
+                                                int lane, int wm, int wn,
+                                                f32x16_t (&acc)[TN][TM]);
 template <int EPI>
 static __device__ __forceinline__ void epilogue(const f32x16_t (&acc)[TN][TM], const GemmArgs &a,
                                                 const TileView<uint16_t> &v, int n0,
@@ -880,6 +928,65 @@ __device__ __forceinline__ void Rh<H>::tile(const GemmArgs &a, const TileView<ui
   if (kb + 1 < nk) {
     rs::lds_barrier();
     lstore(s_tile, ra, rb, tid);
+    mfma_all(f, acc);
+    rs::lds_barrier();
+    read_frags(s_tile, f, wm, wn, lane);
+  }
+  mfma_all(f, acc);
+  __syncthreads();
+}
+
+template <int H>
+__device__ __forceinline__ void Rh<H>::tile_fp8(const GemmArgs &a, const TileView<uint16_t> &v,
+                                                int n0, int nk, uint16_t *s_tile, int tid,
+                                                int lane, int wm, int wn,
+                                                f32x16_t (&acc)[TN][TM]) {
+  const int kc = tid & 7;
+  const uint8_t *a_src[A_CH];
+  float a_sc[A_CH];
+  const uint16_t *b_src[B_CH];
+#pragma unroll
+  for (int i = 0; i < A_CH; ++i) {
+    const int64_t r = v.row0 + (tid >> 3) + i * (NT / 8);
+    a_src[i] = a8_row_ptr(a, v, r) + kc * 8;
+    a_sc[i] = __builtin_ldexpf(1.0f, a8_row_exp(a, v, r));
+  }
+#pragma unroll
+  for (int i = 0; i < B_CH; ++i) {
+    int n = n0 + (tid >> 3) + i * (NT / 8);
+    if (n >= a.Nout) n = a.Nout - 1;
+    b_src[i] = v.W + static_cast<int64_t>(n) * a.K + kc * 8;
+  }
+#pragma unroll
+  for (int i = 0; i < TN; ++i)
+#pragma unroll
+    for (int j = 0; j < TM; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+
+  uint2 ra[A_CH];
+  u32x4_t rb[B_CH];
+  Frags f;
+  gload8(ra, rb, a_src, b_src, 0);
+  lstore8(s_tile, ra, a_sc, rb, tid);
+  if (nk > 1) gload8(ra, rb, a_src, b_src, 1);
+  __syncthreads();
+  read_frags(s_tile, f, wm, wn, lane);
+  __builtin_amdgcn_sched_barrier(0);
+  int kb = 0;
+  for (; kb + 2 < nk; ++kb) {
+    rs::lds_barrier();
+    lstore8(s_tile, ra, a_sc, rb, tid);
+    gload8(ra, rb, a_src, b_src, kb + 2);
+    mfma_all(f, acc);
+    rs::lds_barrier();
+    read_frags(s_tile, f, wm, wn, lane);
+    schedule_step();
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  if (kb + 1 < nk) {
+    rs::lds_barrier();
+    lstore8(s_tile, ra, a_sc, rb, tid);
     mfma_all(f, acc);
     rs::lds_barrier();
     read_frags(s_tile, f, wm, wn, lane);
@@ -1433,17 +1540,7 @@ __device__ __forceinline__ void stream_unit(const GemmArgs &a, const StreamSplit
       for (int j = 0; j < MR / 32; ++j) {
         const int r = tid / 8 + 32 * j, lc = tid & 7;
         const uint2 cw = *reinterpret_cast<const uint2 *>(s8 + r * 64 + lc * 8);
-        uint4 o;
-        uint32_t *op = reinterpret_cast<uint32_t *>(&o);
-        const uint32_t w2[2] = {cw.x, cw.y};
-#pragma unroll
-        for (int h2 = 0; h2 < 2; ++h2) {
-          const f32x2_t lo = __builtin_amdgcn_cvt_pk_f32_fp8(static_cast<int>(w2[h2]), false);
-          const f32x2_t hi = __builtin_amdgcn_cvt_pk_f32_fp8(static_cast<int>(w2[h2]), true);
-          op[2 * h2] = pack_bf16x2(lo.x * x8_scale[j], lo.y * x8_scale[j]);
-          op[2 * h2 + 1] = pack_bf16x2(hi.x * x8_scale[j], hi.y * x8_scale[j]);
-        }
-        *reinterpret_cast<uint4 *>(sxw + r * KCH + swz(r, lc) * 8) = o;
+        *reinterpret_cast<u32x4_t *>(sxw + r * KCH + swz(r, lc) * 8) = widen_fp8x8(cw, x8_scale[j]);
       }
       // every wave's widened rows are in LDS (LDS only: the copies of later
       // chunks stay in flight)
@@ -1674,6 +1771,46 @@ __global__ __launch_bounds__(256) void stream_finish_kernel(GemmArgs a, StreamSp
     packed.x = pack_bf16x2(o[0], o[1]);
     packed.y = pack_bf16x2(o[2], o[3]);
     *reinterpret_cast<uint2 *>(v.C + (v.out_base + lr) * a.Nout + n) = packed;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// FP8-dispatched rows of groups above 128 rows: 128 x 256 tiles, registers
+// staging both operands (8-byte FP8 pieces for A, widened as they are stored
+// to LDS).  Persistent workgroups, the tile list split into eight contiguous
+// parts (one per XCD) and banded by eight m-tiles (1,024 rows), so the
+// workgroups of one XCD share a weight block across an expert's rows.
+// ---------------------------------------------------------------------------
+template <int EPI>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void grouped_gemm_bf16_rh_fp8_kernel(GemmArgs a) {
+  using R = Rh<128>;
+  constexpr int NT = 256;
+  // the tile (384 x 64 bf16) and, in the epilogue, 128 x 256 staged outputs
+  __shared__ __attribute__((aligned(16))) uint16_t s_tile[R::BM * R::BN];
+  static_assert((R::BM + R::BN) * R::BK <= R::BM * R::BN, "tile fits the epilogue staging");
+  __shared__ int s_pref[kMaxGroups + 1];
+  __shared__ int s_tmp[NT / 64];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = uniform(tid >> 6);
+  const int wm = wave & 1, wn = wave >> 1;
+  const int n_groups = a.n_routed + a.n_shared;
+  const int total_m = build_tile_prefix<NT, R::BM>(a, s_pref, s_tmp);
+  const int n_nt = (a.Nout + R::BN - 1) / R::BN;
+  const int total = total_m * n_nt;
+  const int xcd = blockIdx.x % kXcds, slot = blockIdx.x / kXcds, nslots = gridDim.x / kXcds;
+  const int part = (total + kXcds - 1) / kXcds;
+  const int begin = xcd * part, end = min(total, begin + part);
+  const int nk = a.K / R::BK;
+  for (int L = begin + slot; L < end; L += nslots) {
+    int mt, nt;
+    decode_tile<8>(L, total_m, n_nt, &mt, &nt);
+    const int g = find_group(s_pref, n_groups, mt);
+    const TileView<uint16_t> v = tile_view<uint16_t>(a, g, mt - s_pref[g], R::BM);
+    f32x16_t acc[R::TN][R::TM];
+    R::tile_fp8(a, v, nt * R::BN, nk, s_tile, tid, lane, wm, wn, acc);
+    R::epilogue<EPI>(acc, a, v, nt * R::BN, s_tile, lane, wm, wn, tid);
   }
 }
 
@@ -1944,8 +2081,23 @@ hipError_t launch_grouped_gemm(bool bf16, const GemmGroups &g, Epilogue epi, hip
     // 128-row units of 128 features (the staging rows leave no room for 256)
     if (!bf16 || g.n_shared != 0 || g.K % 64 != 0 || g.Nout % 4 != 0 || !g.a8_exp)
       return hipErrorInvalidValue;
+    constexpr int64_t kStreamRows = 128;
     if (g.max_group_rows <= 32) return launch_bf16_stream<1, 1, 6, 0, true>(a, g, epi, 1, s);
-    return launch_bf16_stream<1, 2, 3, 4, true>(a, g, epi, 1, s);
+    if (g.max_group_rows <= kStreamRows) return launch_bf16_stream<1, 2, 3, 4, true>(a, g, epi, 1, s);
+    // groups above 128 rows on 128 x 256 tiles; the rest on the stream kernel
+    // when the mean leaves room for them
+    const int64_t mean_rows = g.max_routed_rows / (g.n_routed > 0 ? g.n_routed : 1);
+    GemmArgs ab = a, as = a;
+    ab.cls_lo = kStreamRows + 1;
+    as.cls_hi = kStreamRows;
+    const unsigned grid = persistent_grid(tiles_upper_bound(g, 128, 256), 1);
+    if (epi == kEpiBiasSilu)
+      hipLaunchKernelGGL((grouped_gemm_bf16_rh_fp8_kernel<kEpiBiasSilu>), dim3(grid), dim3(256), 0, s, ab);
+    else
+      hipLaunchKernelGGL((grouped_gemm_bf16_rh_fp8_kernel<kEpiBias>), dim3(grid), dim3(256), 0, s, ab);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess || mean_rows >= 384) return e;
+    return launch_bf16_stream<1, 2, 3, 4, true>(as, g, epi, 1, s);
   }
   if (bf16 && g.K % 64 == 0 && g.Nout % 4 == 0) {
     // Groups of up to kStreamRows rows are bound by their weight stream and
