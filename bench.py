@@ -50,6 +50,11 @@ def parse():
                    help="time only --workload (no per-config lines for the other workloads)")
     p.add_argument("--calibrate-copy", action="store_true",
                    help="only copy 1 GiB device-to-device three times (counter calibration)")
+    p.add_argument("--traffic-from", nargs=4, metavar=("FETCH_CSV", "WRITE_CSV", "COPY_FETCH_CSV",
+                                                       "COPY_WRITE_CSV"),
+                   help="no GPU: turn rocprofv3 FETCH_SIZE / WRITE_SIZE counter files of a "
+                        "run of this command (and of --calibrate-copy) into the workload's "
+                        "entry of profiles/traffic.json; --steps gives the timed passes")
     return p.parse_args()
 
 
@@ -78,6 +83,82 @@ def measured_traffic(workload: str, stage: str):
     if not e or e.get("source_sha") != source_sha():
         return None
     return e["fetch_bytes"] + e["write_bytes"]
+
+
+def _read_counter_csv(path: str):
+    """(kernel name, value) per dispatch, in dispatch order, from a rocprofv3
+    counter_collection.csv holding one counter."""
+    import csv
+    rows = {}
+    with open(path, newline="") as f:
+        for r in csv.DictReader(f):
+            did = int(r.get("Dispatch_Id") or r.get("Dispatch_ID"))
+            name = r.get("Kernel_Name") or r.get("Kernel-Name")
+            rows.setdefault(did, [name, 0.0])[1] += float(r["Counter_Value"])
+    return [tuple(rows[k]) for k in sorted(rows)]
+
+
+def _short(name: str) -> str:
+    """Kernel name without namespaces and arguments: 'grouped_gemm_bf16_rs_kernel<1, 4, false, true>'."""
+    head = name.replace("(anonymous namespace)", "").replace("void ", "")
+    head = head.split("(")[0]
+    return head.split("::")[-1].strip()
+
+
+def _epi_of(short: str):
+    """The epilogue template argument of an expert-GEMM kernel (1: bias + SiLU,
+    the first Linear; 0: bias), or None for other kernels."""
+    base, _, args = short.partition("<")
+    args = [a.strip() for a in args.rstrip(">").split(",")] if args else []
+    pos = {"grouped_gemm_bf16_rs_kernel": 0, "rs_fixup_kernel": 0,
+           "grouped_gemm_bf16_stream_kernel": 4, "stream_finish_kernel": 3,
+           "grouped_gemm_bf16_rh_fp8_kernel": 0, "grouped_gemm_valu_kernel": 1}.get(base)
+    if pos is None or pos >= len(args):
+        return None
+    return 1 if args[pos] in ("1", "kEpiBiasSilu") else 0
+
+
+def stage_traffic(fetch_csv: str, write_csv: str, passes: int, fetch_scale: float,
+                  write_scale: float):
+    """HBM bytes of the two expert-GEMM stages per layer pass, averaged over the
+    last `passes` passes.  A pass starts at its router kernel; the first
+    Linear's stage runs from the kernel after the dispatch through the last
+    kernel with the SiLU epilogue (the FP8 quantisation pass included), the
+    second Linear's stage from there up to the combine."""
+    out = {}
+    for which, path, scale in (("fetch", fetch_csv, fetch_scale), ("write", write_csv, write_scale)):
+        disp = [(_short(n), v) for n, v in _read_counter_csv(path)]
+        starts = [i for i, (n, _) in enumerate(disp) if n.startswith("router_logits")]
+        if len(starts) < passes:
+            raise ValueError(f"{path}: {len(starts)} layer passes, {passes} asked for")
+        bounds = starts + [len(disp)]
+        acc = {"up": 0.0, "down": 0.0}
+        kern = {"up": [], "down": []}
+        for p in range(len(starts) - passes, len(starts)):
+            seq = disp[bounds[p]:bounds[p + 1]]
+            names = [n for n, _ in seq]
+            first = next(i for i, n in enumerate(names) if n.startswith("dispatch")) + 1
+            while first < len(names) and names[first].startswith("dispatch"):
+                first += 1
+            end = next(i for i, n in enumerate(names) if n.startswith("combine"))
+            last_up = max(i for i in range(first, end)
+                          if _epi_of(names[i]) == 1 or names[i].startswith("quantize"))
+            for i in range(first, end):
+                st = "up" if i <= last_up else "down"
+                acc[st] += seq[i][1] * 1024.0 * scale     # KiB per dispatch
+                if names[i] not in kern[st]:
+                    kern[st].append(names[i])
+        for st in acc:
+            out.setdefault(st, {"kernels": kern[st]})[f"{which}_bytes"] = acc[st] / passes
+    return out
+
+
+def copy_scales(fetch_csv: str, write_csv: str, copy_bytes: int = 1 << 30):
+    """Bytes per counter unit of FETCH_SIZE and WRITE_SIZE, from the device
+    copies of --calibrate-copy (the largest dispatches of those runs)."""
+    f = max(v for _, v in _read_counter_csv(fetch_csv)) * 1024.0
+    w = max(v for _, v in _read_counter_csv(write_csv)) * 1024.0
+    return copy_bytes / f, copy_bytes / w
 
 
 def stage_work(wl, kept_rows: int, touched: int):
@@ -154,7 +235,7 @@ def roofline(wl, work, stage_ms):
         roof = {"bound": "hbm", "achieved": nbytes / t_dom / 1e9, "peak": PEAK_HBM_GBS,
                 "unit": "GB/s"}
     roof["frac"] = roof["achieved"] / roof["peak"]
-    roof["traffic"] = measured_traffic(wl.name, dom)
+    roof["traffic"] = measured_traffic(wl.name + ("+fp8" if wl.dispatch_fp8 else ""), dom)
     roof["kernel"] = f"grouped_gemm_bf16 ({dom})" if wl.dtype == "bf16" else f"grouped_gemm_valu ({dom})"
     roof["work_per_launch"] = {"flops": flops, "bytes": nbytes}
     # the other expert GEMM, in the same units, for reference
@@ -240,8 +321,29 @@ def measure(wl, steps: int, warmup: int, keep_layer: bool = False):
     return res, None
 
 
+def record_traffic(args):
+    fetch_csv, write_csv, cf, cw = args.traffic_from
+    fs, ws = copy_scales(cf, cw)
+    st = stage_traffic(fetch_csv, write_csv, args.steps, fs, ws)
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        t = {}
+    t["_copy_calibration"] = {"fetch_scale": fs, "write_scale": ws,
+                              "note": "1 GiB device copy; counters in KiB per dispatch"}
+    key = args.workload + ("" if args.dispatch == "bf16" else "+fp8")
+    t[key] = {k: dict(v, source_sha=source_sha()) for k, v in st.items()}
+    with open(TRAFFIC_FILE, "w") as f:
+        json.dump(t, f, indent=1)
+    print(json.dumps({key: t[key]}, indent=1))
+
+
 def main():
     args = parse()
+    if args.traffic_from:
+        record_traffic(args)
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU only: the library has no multi-GPU path "
               "(run with --gpus 1)", file=sys.stderr)
