@@ -519,9 +519,43 @@ using T = Rh<128>;
 constexpr int BM = T::BM, TM = T::TM, TN = T::TN, WTM = T::WTM;
 }  // namespace rh
 
+// Store of ROWS staged output rows of 256 bf16 from LDS (row r at r * 256, its
+// 16-byte chunks swizzled by r & 31) by the 256 threads of a workgroup: thread
+// t owns chunk t % 32 of rows t / 32 + 8j.  All of a thread's LDS reads are
+// issued before its first store, so their latency is paid once and not per
+// row; the global addresses step by a fixed row stride.  row_of(j) is the
+// tile row (from v.row0) that staged row t / 32 + 8j holds, minus t / 32.
+template <int ROWS, typename RowOf>
+__device__ __forceinline__ void store_staged_rows(const uint16_t *s_tile, const GemmArgs &a,
+                                                  const TileView<uint16_t> &v, int n0,
+                                                  int etid, RowOf row_of) {
+  constexpr int BN = 256, CH = BN / 8, RPI = 256 / CH, NIT = ROWS / RPI;
+  static_assert(ROWS % RPI == 0, "whole sweeps");
+  const int c = etid % CH, r0 = etid / CH;
+  u32x4_t val[NIT];
+#pragma unroll
+  for (int j = 0; j < NIT; ++j) {
+    const int r = r0 + RPI * j;
+    val[j] = *reinterpret_cast<const u32x4_t *>(s_tile + r * BN + ((c ^ (r & 31)) << 3));
+  }
+  const int n = n0 + c * 8;
+  if (n >= a.Nout) return;
+  uint16_t *base = v.C + (v.out_base + v.row0 + r0) * a.Nout + n;
+  const int64_t lim = v.rows - v.row0 - r0;   // rows of the view from this thread's first
+#pragma unroll
+  for (int j = 0; j < NIT; ++j) {
+    const int lr = row_of(j);
+    if (lr < lim) store_nt(base + static_cast<int64_t>(lr) * a.Nout, val[j]);
+  }
+}
+
 // Epilogue of a 256x256 tile through LDS in two passes of 128 rows (the tile
 // buffer holds 128 x 256 bf16): in pass p every wave stores its row blocks
-// mi = 2p, 2p+1, so all four waves work in both passes.  The barriers only
+// mi = 2p, 2p+1, so all four waves work in both passes.  Without the SiLU,
+// pass 0's staged rows are read back into registers and their global stores
+// are issued one per column block of pass 1, under pass 1's arithmetic
+// (measured: with the SiLU the held rows spill and cost more than the overlap
+// gains, so there each pass stores its own rows).  The barriers only
 // order LDS accesses, so global loads issued before the epilogue (the next
 // tile's first K-steps) stay in flight across it.
 template <int EPI, bool BIAS>
@@ -532,14 +566,26 @@ __device__ __forceinline__ void rs_epilogue(const f32x16_t (&acc)[rs::TN][rs::TM
   using namespace rs;
   int el = lane, ewm = wm, ewn = wn, etid = tid;
   asm volatile("" : "+v"(el), "+v"(etid), "+s"(ewm), "+s"(ewn));
-  constexpr int CH = BN / 8;
   static_assert(TILE >= 128 * BN, "128 C-tile rows must fit");
+  static_assert(TN * 4 == 16, "one held row per column block of pass 1");
+  constexpr bool HOLD = EPI != kEpiBiasSilu;
+  // pass 0's rows, as store_staged_rows lays them out: thread t holds chunk
+  // t % 32 of staged rows t / 32 + 8j, tile rows (j / 8) * 128 + t / 32 + 8 (j % 8)
+  u32x4_t held[16];
+  uint16_t *hbase = nullptr;
+  int64_t hlim = 0;
+  bool hcol = false;
 #pragma unroll
   for (int pass = 0; pass < 2; ++pass) {
 #pragma unroll
     for (int ni = 0; ni < TN; ++ni) {
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
+        if (HOLD && pass == 1) {
+          const int j = ni * 4 + q;
+          const int lr = (j >> 3) * 128 + 8 * (j & 7);
+          if (hcol && lr < hlim) store_nt(hbase + static_cast<int64_t>(lr) * a.Nout, held[j]);
+        }
         const int nl = ewn * WTN + ni * 32 + q * 8 + (el >> 5) * 4;
         const int n = n0 + nl;
         float bv[4] = {0.0f, 0.0f, 0.0f, 0.0f};
@@ -570,15 +616,25 @@ __device__ __forceinline__ void rs_epilogue(const f32x16_t (&acc)[rs::TN][rs::TM
       }
     }
     rs::lds_barrier();
-    // LDS row ml of the pass is tile row (ml/64)*128 + pass*64 + ml%64
-    for (int i = etid; i < 128 * CH; i += NT) {
-      const int r = i / CH, c = i % CH;
-      const int64_t row = v.row0 + (r >> 6) * 128 + pass * 64 + (r & 63);
-      const int n = n0 + c * 8;
-      if (row < v.rows && n < a.Nout) {
-        const u32x4_t val = *reinterpret_cast<const u32x4_t *>(s_tile + r * BN + ((c ^ (r & 31)) << 3));
-        store_nt(v.C + (v.out_base + row) * a.Nout + n, val);
+    // LDS row ml of the pass is tile row (ml/64)*128 + pass*64 + ml%64; the
+    // thread's rows t/32 + 8j (t/32 < 8) cross from the first 64 at j = 8
+    if (!HOLD) {
+      store_staged_rows<128>(s_tile, a, v, n0, etid,
+                             [&](int j) { return (j >> 3) * 128 + pass * 64 + 8 * (j & 7); });
+    } else if (pass == 0) {
+      const int c = etid % 32, r0 = etid / 32;
+#pragma unroll
+      for (int j = 0; j < 16; ++j) {
+        const int r = r0 + 8 * j;
+        held[j] = *reinterpret_cast<const u32x4_t *>(s_tile + r * BN + ((c ^ (r & 31)) << 3));
       }
+      const int n = n0 + c * 8;
+      hcol = n < a.Nout;
+      hbase = v.C + (v.out_base + v.row0 + r0) * a.Nout + n;
+      hlim = v.rows - v.row0 - r0;
+    } else {
+      store_staged_rows<128>(s_tile, a, v, n0, etid,
+                             [&](int j) { return (j >> 3) * 128 + 64 + 8 * (j & 7); });
     }
     rs::lds_barrier();
   }
@@ -1036,15 +1092,7 @@ __device__ __forceinline__ void Rh<H>::epilogue(const f32x16_t (&acc)[TN][TM], c
     }
   }
   __syncthreads();
-  for (int i = etid; i < BM * CH; i += NT) {
-    const int r = i / CH, c = i % CH;
-    const int64_t row = v.row0 + r;
-    const int n = n0 + c * 8;
-    if (row < v.rows && n < a.Nout) {
-      const u32x4_t val = *reinterpret_cast<const u32x4_t *>(s_tile + r * BN + ((c ^ (r & 31)) << 3));
-      store_nt(v.C + (v.out_base + row) * a.Nout + n, val);
-    }
-  }
+  store_staged_rows<BM>(s_tile, a, v, n0, etid, [](int j) { return 8 * j; });
   __syncthreads();
 }
 
