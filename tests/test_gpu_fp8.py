@@ -67,6 +67,13 @@ SMALL = [
                       d_ff=320, dtype="bf16", expert_bias=True, dispatch_fp8=True),
     W.custom_workload("fp8_T1", T=1, d_model=128, n_routed=8, top_k=2, n_shared=0, d_ff=128,
                       dtype="bf16", dispatch_fp8=True),
+    # capacity drops and a selection-only bias: the codes of every token are
+    # produced, only kept slots are computed
+    W.custom_workload("fp8_sel_only_cap", T=256, d_model=256, n_routed=32, top_k=4, n_shared=1,
+                      d_ff=128, dtype="bf16", router_bias="gauss", router_bias_var=0.5,
+                      selection_only_bias=True, capacity_factor=1.0, dispatch_fp8=True),
+    W.custom_workload("fp8_N1024_K64", T=150, d_model=64, n_routed=1024, top_k=64, n_shared=1,
+                      d_ff=64, dtype="bf16", capacity_factor=1.5, dispatch_fp8=True),
 ]
 
 

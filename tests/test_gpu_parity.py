@@ -499,6 +499,13 @@ SMALL_LAYERS = [
                       dtype="f32", expert_bias=True),
     W.custom_workload("T1", T=1, d_model=128, n_routed=8, top_k=2, n_shared=1, d_ff=128,
                       dtype="bf16"),
+    # the interface's limits through the whole layer: 1,024 experts, 64 slots
+    # per token (combine's widest sum), groups of a few rows each, capacity drops
+    W.custom_workload("bf16_N1024_K64_cap", T=150, d_model=64, n_routed=1024, top_k=64,
+                      n_shared=1, d_ff=64, dtype="bf16", router_bias="gauss",
+                      router_bias_var=0.5, capacity_factor=1.5),
+    W.custom_workload("f32_N1024_K64", T=40, d_model=32, n_routed=1024, top_k=64, n_shared=0,
+                      d_ff=48, dtype="f32", expert_bias=True),
 ]
 
 
