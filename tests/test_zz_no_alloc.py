@@ -35,7 +35,8 @@ def rel_l2(a, b):
 def run_both(B, dl, wl, T):
     """The layer on the first T tokens, once per entry point."""
     cfg = B.config(T, wl.d_model, wl.n_routed, wl.top_k, wl.n_shared, wl.d_ff, wl.dtype,
-                   wl.capacity_factor, selection_only_bias=wl.selection_only_bias)
+                   wl.capacity_factor, selection_only_bias=wl.selection_only_bias,
+                   dispatch_fp8=wl.dispatch_fp8)
     x = dl.x[:T]
     out = {}
     for name in ("ws", "noalloc"):
@@ -84,7 +85,11 @@ def test_noalloc_small_layers_back_to_back():
     for wl, T2 in ((W.get_workload("tiny_fp32"), 33),
                    (W.custom_workload("noalloc_bf16", T=300, d_model=256, n_routed=16, top_k=4,
                                       n_shared=1, d_ff=320, dtype="bf16", router_bias="gauss",
-                                      router_bias_var=0.5, capacity_factor=1.25), 77)):
+                                      router_bias_var=0.5, capacity_factor=1.25), 77),
+                   # FP8 dispatch: the codes and row exponents in the array too
+                   (W.custom_workload("noalloc_fp8", T=200, d_model=256, n_routed=16, top_k=4,
+                                      n_shared=1, d_ff=256, dtype="bf16", capacity_factor=1.25,
+                                      dispatch_fp8=True), 50)):
         print(f"[noalloc] {wl.name}: T={wl.T} then {T2}", flush=True)
         dl = W.device.DeviceLayer(wl)
         compare(run_both(B, dl, wl, wl.T), wl.dtype, f"{wl.name} T={wl.T}")
