@@ -55,7 +55,14 @@ __global__ __launch_bounds__(256) void dispatch_masks_kernel(const int32_t *__re
   }
 }
 
-// Single workgroup of 1024 threads.
+// Single workgroup of 1024 threads.  Expert x's chunk counts are summed by a
+// segment of P adjacent lanes of one wave (P = 1024 / N rounded down to a
+// power of two, at most 64): lane j of the segment takes the contiguous
+// chunks j L .. (j+1) L - 1, L = ceil(n_chunks / P), and adds them with eight
+// loads in flight; the segment scans its P partial sums with shuffles, and
+// each lane then writes the base ranks of its own chunks.  The loop waits for
+// one memory latency per eight chunks of a lane instead of per eight chunks of
+// the expert.
 __global__ __launch_bounds__(1024) void dispatch_scan_kernel(
     const int32_t *__restrict__ hist, int64_t n_chunks, int N, int64_t capacity,
     int32_t *__restrict__ base, int32_t *__restrict__ counts, int32_t *__restrict__ offsets,
@@ -63,24 +70,51 @@ __global__ __launch_bounds__(1024) void dispatch_scan_kernel(
   __shared__ int32_t s_cnt[kMaxRouted];
   __shared__ int32_t s_drop[kMaxRouted];
   __shared__ int32_t s_wave[16];
-  for (int e = threadIdx.x; e < N; e += blockDim.x) {
-    int32_t run = 0;
-    // eight chunk counts are loaded before they are summed, so the loop waits
-    // for one memory latency per eight chunks rather than per chunk
-    for (int64_t c0 = 0; c0 < n_chunks; c0 += 8) {
-      int32_t hv[8];
+  int P = kWave;
+  while (P > 1 && P * N > static_cast<int>(blockDim.x)) P >>= 1;
+  {
+    const int j = threadIdx.x & (P - 1);
+    const int x = threadIdx.x / P;   // expert of this lane's segment (idle if >= N)
+    const int64_t L = (n_chunks + P - 1) / P;
+    const int64_t c_beg = min(n_chunks, j * L), c_end = min(n_chunks, c_beg + L);
+    int32_t part = 0;
+    if (x < N) {
+      for (int64_t c0 = c_beg; c0 < c_end; c0 += 8) {
+        int32_t hv[8];
 #pragma unroll
-      for (int j = 0; j < 8; ++j) hv[j] = c0 + j < n_chunks ? hist[(c0 + j) * N + e] : 0;
+        for (int i = 0; i < 8; ++i) hv[i] = c0 + i < c_end ? hist[(c0 + i) * N + x] : 0;
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        if (c0 + j < n_chunks) base[(c0 + j) * N + e] = run;
-        run += hv[j];
+        for (int i = 0; i < 8; ++i) part += hv[i];
       }
     }
-    const int32_t kept = (capacity >= 0 && run > capacity) ? static_cast<int32_t>(capacity) : run;
-    counts[e] = kept;
-    s_cnt[e] = kept;
-    s_drop[e] = run - kept;
+    // inclusive scan of the partial sums within the segment (segments are
+    // aligned, so lane - off stays inside it whenever j >= off)
+    int32_t incl = part;
+    for (int off = 1; off < P; off <<= 1) {
+      const int32_t o = __shfl_up(incl, off);
+      if (j >= off) incl += o;
+    }
+    const int32_t total = __shfl(incl, (threadIdx.x & (kWave - 1) & ~(P - 1)) + P - 1);
+    if (x < N) {
+      int32_t run = incl - part;   // base rank of chunk c_beg
+      for (int64_t c0 = c_beg; c0 < c_end; c0 += 8) {
+        int32_t hv[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) hv[i] = c0 + i < c_end ? hist[(c0 + i) * N + x] : 0;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          if (c0 + i < c_end) base[(c0 + i) * N + x] = run;
+          run += hv[i];
+        }
+      }
+      if (j == 0) {
+        const int32_t kept =
+            (capacity >= 0 && total > capacity) ? static_cast<int32_t>(capacity) : total;
+        counts[x] = kept;
+        s_cnt[x] = kept;
+        s_drop[x] = total - kept;
+      }
+    }
   }
   __syncthreads();
   // exclusive scan of s_cnt over N <= 1024 entries: one entry per thread
@@ -122,15 +156,34 @@ __global__ __launch_bounds__(256) void dispatch_scatter_kernel(
   const int64_t t = c * kChunk + lane;
   if (t >= T) return;
   const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-  for (int k = 0; k < K; ++k) {
-    const int e = idx[t * K + k];
-    const int64_t rank = base[c * N + e] + __popcll(masks[c * N + e] & below);
-    int32_t r = -1;
-    if (capacity < 0 || rank < capacity) {
-      r = offsets[e] + static_cast<int32_t>(rank);
-      row_token[r] = static_cast<int32_t>(t);
+  // eight slots at a time: their expert ids, then the loads that depend on
+  // them, then the stores, so a token waits for two memory latencies per eight
+  // slots rather than two per slot
+  for (int k0 = 0; k0 < K; k0 += 8) {
+    int ev[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) ev[i] = k0 + i < K ? idx[t * K + k0 + i] : 0;
+    int32_t bv[8], ov[8];
+    uint64_t mv[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      if (k0 + i < K) {
+        bv[i] = base[c * N + ev[i]];
+        mv[i] = masks[c * N + ev[i]];
+        ov[i] = offsets[ev[i]];
+      }
     }
-    slot_row[t * K + k] = r;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      if (k0 + i >= K) break;
+      const int64_t rank = bv[i] + __popcll(mv[i] & below);
+      int32_t r = -1;
+      if (capacity < 0 || rank < capacity) {
+        r = ov[i] + static_cast<int32_t>(rank);
+        row_token[r] = static_cast<int32_t>(t);
+      }
+      slot_row[t * K + k0 + i] = r;
+    }
   }
 }
 
