@@ -245,6 +245,16 @@ def roofline(wl, work, stage_ms):
                            "achieved": (work[other]["flops"] / t_o / 1e12 if roof["unit"] == "TFLOP/s"
                                         else work[other]["bytes"] / t_o / 1e9)}
     roof["other_stage"]["frac"] = roof["other_stage"]["achieved"] / roof["peak"]
+    # the same stage against the other roof (an HBM-bound stage's share of the
+    # matrix-core peak, an MFMA-bound stage's share of HBM bandwidth)
+    if roof["unit"] == "GB/s":
+        a = flops / t_dom / 1e12
+        roof["other_roof"] = {"unit": "TFLOP/s", "achieved": a, "peak": peak_flops,
+                              "frac": a / peak_flops}
+    else:
+        a = nbytes / t_dom / 1e9
+        roof["other_roof"] = {"unit": "GB/s", "achieved": a, "peak": PEAK_HBM_GBS,
+                              "frac": a / PEAK_HBM_GBS}
     return roof
 
 
