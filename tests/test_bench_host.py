@@ -72,3 +72,23 @@ def test_traffic_is_null_unless_taken_on_this_source(tmp_path, monkeypatch):
 @pytest.mark.parametrize("name", list(W.WORKLOADS))
 def test_every_workload_has_a_cpu_sample(name):
     assert bench.CPU_SAMPLE[name] >= 1
+
+
+def test_roofline_reports_both_roofs():
+    # an HBM-bound stage (prefill-shaped: 128 mean rows per expert, below the
+    # 312.5 flop/byte ridge) also gets its MFMA share, and an MFMA-bound one
+    # (Mixtral-shaped) its HBM share, from the same work and time
+    for name, kept, touched, bound in (("dsv3_prefill", 32768, 241, "hbm"),
+                                       ("mixtral_shape", 8192, 8, "mfma")):
+        wl = W.get_workload(name)
+        work = bench.stage_work(wl, kept, touched)
+        ms = {"up": 2.0, "down": 1.0}
+        roof = bench.roofline(wl, work, ms)
+        assert roof["bound"] == bound and roof["kernel"].endswith("(up)")
+        t = 2.0e-3
+        flops_frac = work["up"]["flops"] / t / 1e12 / bench.PEAK_BF16_TFLOPS
+        bytes_frac = work["up"]["bytes"] / t / 1e9 / bench.PEAK_HBM_GBS
+        main, other = (bytes_frac, flops_frac) if bound == "hbm" else (flops_frac, bytes_frac)
+        assert roof["frac"] == pytest.approx(main, rel=1e-12)
+        assert roof["other_roof"]["frac"] == pytest.approx(other, rel=1e-12)
+        assert roof["other_roof"]["unit"] == ("TFLOP/s" if bound == "hbm" else "GB/s")
