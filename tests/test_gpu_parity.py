@@ -415,6 +415,14 @@ FFN_CASES = [
     # (second), so the 256x256 kernel addresses its copies with 64-bit
     # pointers instead of 32-bit offsets from uniform bases
     ("bf16_wide_offsets", [700, 300, 520], 4096, 2048, "bf16", True, 1100000),
+    # widths of 1..128 mod 256 (a last 256x256 tile column at most half used,
+    # its missing columns clamped on load and skipped on store), with the last
+    # round split along K (first Linear 2176 = 8.5 x 256; second Linear
+    # 1088 = 4.25 x 256 over K = 4096), along M, and with 64-bit pointers
+    ("bf16_narrow_ksplit_up", [700, 300, 520], 4096, 2176, "bf16", True, 8192),
+    ("bf16_narrow_ksplit_down", [700, 300, 520], 1088, 4096, "bf16", True, 8192),
+    ("bf16_narrow_msplit", [700, 300, 520], 640, 1152, "bf16", True, 8192),
+    ("bf16_narrow_wide_offsets", [700, 300, 520], 4096, 2176, "bf16", True, 1100000),
 ]
 
 
