@@ -514,6 +514,11 @@ SMALL_LAYERS = [
                       router_bias_var=0.5, capacity_factor=1.5),
     W.custom_workload("f32_N1024_K64", T=40, d_model=32, n_routed=1024, top_k=64, n_shared=0,
                       d_ff=48, dtype="f32", expert_bias=True),
+    # dispatch at scale: 524,288 assignments in 1,024 chunks of 64 tokens (the
+    # scan's lanes each sum a run of 64 chunks), capacity drops on every expert
+    W.custom_workload("bf16_T65536_cap", T=65536, d_model=64, n_routed=64, top_k=8,
+                      n_shared=1, d_ff=64, dtype="bf16", router_bias="gauss",
+                      router_bias_var=0.5, capacity_factor=1.0),
 ]
 
 
