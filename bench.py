@@ -112,7 +112,7 @@ def _epi_of(short: str):
     args = [a.strip() for a in args.rstrip(">").split(",")] if args else []
     pos = {"grouped_gemm_bf16_rs_kernel": 0, "rs_fixup_kernel": 0,
            "grouped_gemm_bf16_stream_kernel": 4, "stream_finish_kernel": 3,
-           "grouped_gemm_bf16_rh_fp8_kernel": 0, "grouped_gemm_valu_kernel": 1}.get(base)
+           "grouped_gemm_valu_kernel": 1}.get(base)
     if pos is None or pos >= len(args):
         return None
     return 1 if args[pos] in ("1", "kEpiBiasSilu") else 0
@@ -178,12 +178,12 @@ def stage_work(wl, kept_rows: int, touched: int):
         "router": {"flops": 2 * T * d * N, "bytes": T * d * a + N * d * 4 + T * N * 4},
         "topk": {"flops": 0, "bytes": T * N * 4 + T * K * 8},
         "dispatch": {"flops": 0, "bytes": T * K * 4 * 3 + R * 4},
-        # with FP8 dispatch the routed rows arrive as one byte per element plus
-        # a 4-byte exponent, after a pass that reads x and writes the codes
+        # with FP8 dispatch one pass reads x and writes the codes (one byte per
+        # element), the per-row exponents and the rows widened back to bf16,
+        # which the first Linear then reads like x
         "up": {"flops": 2 * (R + Ks * T) * d * f,
-               "bytes": (w1_bytes + (R + Ks * T) * (d + f) * a + R * 4) if not fp8 else
-                        (w1_bytes + R * d + R * 4 + Ks * T * d * a + (R + Ks * T) * f * a
-                         + R * 4 + T * d * a + T * d + T * 4)},
+               "bytes": w1_bytes + (R + Ks * T) * (d + f) * a + R * 4
+                        + ((T * d * a + T * d + T * 4 + T * d * a) if fp8 else 0)},
         "down": {"flops": 2 * (R + Ks * T) * d * f,
                  "bytes": w2_bytes + (R + Ks * T) * (d + f) * a},
         "combine": {"flops": 0, "bytes": (R + Ks * T + T) * d * a + T * K * 8},

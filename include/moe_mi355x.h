@@ -108,10 +108,12 @@ typedef struct {
  *     OCP FP8 E4M3 codes (bias 7, 3 mantissa bits, largest value 448) with one
  *     power-of-two scale 2^E per row, E the smallest integer with
  *     max|x[t]| <= 448 * 2^E (0 for an all-zero row); codes are x / 2^E
- *     rounded to nearest, ties to even.  The routed experts' first Linear
- *     reads the codes through the dispatch permutation and widens them to
- *     bf16 (exactly 2^E * code value) on chip; the router and the shared
- *     experts use x; the combine is unchanged (bf16).  MOE_BF16 layers only
+ *     rounded to nearest, ties to even.  The pass that makes the codes (the
+ *     payload an exchange between GPUs would carry) also widens them back,
+ *     as the receiving side would, to bf16 rows of exactly 2^E * code value,
+ *     and the routed experts' first Linear reads those rows through the
+ *     dispatch permutation; the router and the shared experts use x; the
+ *     combine is unchanged (bf16).  MOE_BF16 layers only
  *     (MOE_ERR_UNSUPPORTED otherwise); honoured by moe_layer_forward and
  *     moe_layer_forward_noalloc, ignored by the other entry points. */
 enum { MOE_DISPATCH_BF16 = 0, MOE_DISPATCH_FP8 = 1 };

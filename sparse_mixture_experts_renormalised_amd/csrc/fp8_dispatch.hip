@@ -12,6 +12,12 @@
 // One wave per token row: the row's largest magnitude (bf16 magnitudes order
 // as their 15-bit patterns), E from its exponent and mantissa bits, then the
 // codes of 8 elements per lane per step (16-byte loads, 8-byte stores).
+//
+// The same pass also writes the row the receiving side gets back: each code
+// widened to its E4M3 value times 2^E and rounded to bf16 (exact, since an
+// E4M3 value has at most 4 significant bits, unless the product falls below
+// bf16's subnormal range), which the experts' first Linear then reads like
+// any bf16 row.
 #include "moe_common.h"
 
 namespace moe {
@@ -46,10 +52,28 @@ __device__ __forceinline__ uint32_t e4m3_code(float v) {
   return sign | (e << 3) | ((b >> 20) & 7u);
 }
 
+// Eight E4M3 codes (bytes of cw, element order) widened to bf16 times the
+// row's scale sc = 2^E: v_cvt_pk_f32_fp8 gives each code's value exactly in
+// float32, the product by 2^E is exact unless it leaves float32's normal
+// range, and the value (at most 4 significant bits) is exact in bf16.
+__device__ __forceinline__ uint4 widen_fp8x8(uint2 cw, float sc) {
+  const f32x2_t a = __builtin_amdgcn_cvt_pk_f32_fp8(static_cast<int>(cw.x), false);
+  const f32x2_t b = __builtin_amdgcn_cvt_pk_f32_fp8(static_cast<int>(cw.x), true);
+  const f32x2_t c = __builtin_amdgcn_cvt_pk_f32_fp8(static_cast<int>(cw.y), false);
+  const f32x2_t e = __builtin_amdgcn_cvt_pk_f32_fp8(static_cast<int>(cw.y), true);
+  uint4 o;
+  o.x = pack_bf16x2(a.x * sc, a.y * sc);
+  o.y = pack_bf16x2(b.x * sc, b.y * sc);
+  o.z = pack_bf16x2(c.x * sc, c.y * sc);
+  o.w = pack_bf16x2(e.x * sc, e.y * sc);
+  return o;
+}
+
 __global__ __launch_bounds__(256) void quantize_rows_fp8_kernel(const uint16_t *__restrict__ x,
                                                                 int64_t T, int d,
                                                                 uint8_t *__restrict__ q,
-                                                                int32_t *__restrict__ exps) {
+                                                                int32_t *__restrict__ exps,
+                                                                uint16_t *__restrict__ xw) {
   const int lane = threadIdx.x & 63;
   const int64_t t = static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6);
   if (t >= T) return;
@@ -68,6 +92,7 @@ __global__ __launch_bounds__(256) void quantize_rows_fp8_kernel(const uint16_t *
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) amax = max(amax, static_cast<uint32_t>(__shfl_xor(amax, off)));
   const int E = scale_exponent(amax << 16);
+  const float sc = __builtin_ldexpf(1.0f, E);
   if (lane == 0) exps[t] = E;
   uint8_t *qrow = q + t * d;
   for (int i = lane; i < nv; i += 64) {
@@ -83,17 +108,19 @@ __global__ __launch_bounds__(256) void quantize_rows_fp8_kernel(const uint16_t *
     out.x = c[0] | (c[1] << 8) | (c[2] << 16) | (c[3] << 24);
     out.y = c[4] | (c[5] << 8) | (c[6] << 16) | (c[7] << 24);
     *reinterpret_cast<uint2 *>(qrow + i * 8) = out;
+    if (xw) *reinterpret_cast<uint4 *>(xw + t * d + i * 8) = widen_fp8x8(out, sc);
   }
 }
 
 }  // namespace
 
 hipError_t launch_quantize_fp8(const void *x, int64_t T, int d, uint8_t *q, int32_t *exps,
-                               hipStream_t s) {
+                               void *xw, hipStream_t s) {
   if (T <= 0) return hipSuccess;
   const dim3 grid(static_cast<unsigned>((T + 3) / 4));
   hipLaunchKernelGGL(quantize_rows_fp8_kernel, grid, dim3(256), 0, s,
-                     static_cast<const uint16_t *>(x), T, d, q, exps);
+                     static_cast<const uint16_t *>(x), T, d, q, exps,
+                     static_cast<uint16_t *>(xw));
   return hipGetLastError();
 }
 

@@ -71,11 +71,6 @@ struct GemmArgs {
   // kernels can split one grouped product by group size.
   int64_t cls_lo;
   int64_t cls_hi;
-  // FP8-dispatched A rows of the routed groups (stream kernel's FP8 form):
-  // E4M3 codes [rows of A][K] gathered through a_index, and the power-of-two
-  // exponent of each A row; the rows are widened to bf16 x 2^E in LDS.
-  const uint8_t *A8;
-  const int32_t *a8_exp;
 };
 
 __device__ __forceinline__ int64_t group_rows(const GemmArgs &a, int g) {
@@ -204,23 +199,6 @@ __device__ __forceinline__ const T *a_row_ptr(const GemmArgs &a, const TileView<
   return static_cast<const T *>(a.A_sh) + static_cast<int64_t>(gs) * a.a_sh_stride + r * a.K;
 }
 
-// FP8 code row of local row r of a routed group (clamped into the group),
-// and that row's power-of-two exponent.
-__device__ __forceinline__ const uint8_t *a8_row_ptr(const GemmArgs &a,
-                                                     const TileView<uint16_t> &v, int64_t r) {
-  if (r >= v.rows) r = v.rows - 1;
-  const int64_t gr = v.out_base + r;
-  const int64_t src = a.a_index ? static_cast<int64_t>(a.a_index[gr]) : gr;
-  return a.A8 + src * a.K;
-}
-__device__ __forceinline__ int a8_row_exp(const GemmArgs &a, const TileView<uint16_t> &v,
-                                          int64_t r) {
-  if (r >= v.rows) r = v.rows - 1;
-  const int64_t gr = v.out_base + r;
-  const int64_t src = a.a_index ? static_cast<int64_t>(a.a_index[gr]) : gr;
-  return a.a8_exp[src];
-}
-
 // Decode a linear tile index into (m-tile, n-tile), banded by GM m-tiles.
 template <int GM>
 __device__ __forceinline__ void decode_tile(int L, int total_m, int n_nt, int *mt, int *nt) {
@@ -254,12 +232,6 @@ __device__ __forceinline__ void dma16(const uint16_t *src, uint32_t m0) {
 // raises the sustained read rate from about 6.1 to 7.2 TB/s on MI355X.
 __device__ __forceinline__ void dma16_nt(const uint16_t *src, uint32_t m0) {
   asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, off nt" : : "v"(src), "{m0}"(m0) : "memory");
-}
-
-// A four-byte-per-lane LDS DMA (64 lanes x 4 B into the 256 B at m0), for
-// rows of FP8 codes.
-__device__ __forceinline__ void dma4(const uint8_t *src, uint32_t m0) {
-  asm volatile("s_nop 0\n\tglobal_load_lds_dword %0, off" : : "v"(src), "{m0}"(m0) : "memory");
 }
 
 // The same copy addressed as a wave-uniform 64-bit base in SGPRs plus a 32-bit
@@ -366,23 +338,6 @@ __device__ __forceinline__ void lds_barrier() {
 // tile).  Such a tile is computed as H x 256 (H = 128 or 64) by all four
 // waves (2 x 2 waves of H/2 x 128) instead of leaving waves to multiply
 // padding rows: same operand path and swizzle, H/256 of the A rows and MFMAs.
-// Eight E4M3 codes (bytes of cw, element order) widened to bf16 times the
-// row's scale sc, a power of two: each code's value is exact in float32
-// (v_cvt_pk_f32_fp8 reads two codes), the product by 2^E is exact, and the
-// result, at most 4 significant bits, is exact in bf16.
-__device__ __forceinline__ u32x4_t widen_fp8x8(uint2 cw, float sc) {
-  u32x4_t o;
-  const uint32_t w2[2] = {cw.x, cw.y};
-#pragma unroll
-  for (int h = 0; h < 2; ++h) {
-    const f32x2_t lo = __builtin_amdgcn_cvt_pk_f32_fp8(static_cast<int>(w2[h]), false);
-    const f32x2_t hi = __builtin_amdgcn_cvt_pk_f32_fp8(static_cast<int>(w2[h]), true);
-    o[2 * h] = pack_bf16x2(lo.x * sc, lo.y * sc);
-    o[2 * h + 1] = pack_bf16x2(hi.x * sc, hi.y * sc);
-  }
-  return o;
-}
-
 template <int H>
 struct Rh {
 static constexpr int BM = H, BN = 256, BK = 64, NT = 256, WTM = H / 2, WTN = 128;
@@ -402,32 +357,6 @@ static __device__ __forceinline__ void gload(u32x4_t (&ra)[A_CH], u32x4_t (&rb)[
   for (int i = 0; i < A_CH; ++i) ra[i] = *reinterpret_cast<const u32x4_t *>(a_src[i] + kb * BK);
 #pragma unroll
   for (int i = 0; i < B_CH; ++i) rb[i] = *reinterpret_cast<const u32x4_t *>(b_src[i] + kb * BK);
-}
-
-// FP8 A rows: 8 codes (8 bytes) per 8-element piece, widened when stored.
-static __device__ __forceinline__ void gload8(uint2 (&ra)[A_CH], u32x4_t (&rb)[B_CH],
-                                       const uint8_t *const (&a_src)[A_CH],
-                                       const uint16_t *const (&b_src)[B_CH], int kb) {
-#pragma unroll
-  for (int i = 0; i < A_CH; ++i) ra[i] = *reinterpret_cast<const uint2 *>(a_src[i] + kb * BK);
-#pragma unroll
-  for (int i = 0; i < B_CH; ++i) rb[i] = *reinterpret_cast<const u32x4_t *>(b_src[i] + kb * BK);
-}
-
-static __device__ __forceinline__ void lstore8(uint16_t *tile, const uint2 (&ra)[A_CH],
-                                        const float (&sc)[A_CH], const u32x4_t (&rb)[B_CH],
-                                        int tid) {
-  const int kc = tid & 7;
-#pragma unroll
-  for (int i = 0; i < A_CH; ++i) {
-    const int row = (tid >> 3) + i * (NT / 8);
-    *reinterpret_cast<u32x4_t *>(tile + row * BK + (swz(row, kc) << 3)) = widen_fp8x8(ra[i], sc[i]);
-  }
-#pragma unroll
-  for (int i = 0; i < B_CH; ++i) {
-    const int row = (tid >> 3) + i * (NT / 8);
-    *reinterpret_cast<u32x4_t *>(tile + BM * BK + row * BK + (swz(row, kc) << 3)) = rb[i];
-  }
 }
 
 static __device__ __forceinline__ void lstore(uint16_t *tile, const u32x4_t (&ra)[A_CH],
@@ -502,11 +431,6 @@ static __device__ __forceinline__ void schedule_step() {
 static __device__ __forceinline__ void tile(const GemmArgs &a, const TileView<uint16_t> &v, int n0,
                                             int k0, int nk, uint16_t *s_tile, int tid, int lane,
                                             int wm, int wn, f32x16_t (&acc)[TN][TM]);
-// The same with the A rows read as FP8 codes (a.A8, a.a8_exp) and widened.
-static __device__ __forceinline__ void tile_fp8(const GemmArgs &a, const TileView<uint16_t> &v,
-                                                int n0, int nk, uint16_t *s_tile, int tid,
-                                                int lane, int wm, int wn,
-                                                f32x16_t (&acc)[TN][TM]);
 template <int EPI>
 static __device__ __forceinline__ void epilogue(const f32x16_t (&acc)[TN][TM], const GemmArgs &a,
                                                 const TileView<uint16_t> &v, int n0,
@@ -556,8 +480,7 @@ __device__ __forceinline__ void store_staged_rows(const uint16_t *s_tile, const 
 // are issued one per column block of pass 1, under pass 1's arithmetic
 // (measured: with the SiLU the held rows spill and cost more than the overlap
 // gains, so there each pass stores its own rows).  The barriers only
-// order LDS accesses, so global loads issued before the epilogue (the next
-// tile's first K-steps) stay in flight across it.
+// order LDS accesses; they wait for no global load or store.
 template <int EPI, bool BIAS>
 __device__ __forceinline__ void rs_epilogue(const f32x16_t (&acc)[rs::TN][rs::TM],
                                             const GemmArgs &a, const TileView<uint16_t> &v,
@@ -993,65 +916,6 @@ __device__ __forceinline__ void Rh<H>::tile(const GemmArgs &a, const TileView<ui
 }
 
 template <int H>
-__device__ __forceinline__ void Rh<H>::tile_fp8(const GemmArgs &a, const TileView<uint16_t> &v,
-                                                int n0, int nk, uint16_t *s_tile, int tid,
-                                                int lane, int wm, int wn,
-                                                f32x16_t (&acc)[TN][TM]) {
-  const int kc = tid & 7;
-  const uint8_t *a_src[A_CH];
-  float a_sc[A_CH];
-  const uint16_t *b_src[B_CH];
-#pragma unroll
-  for (int i = 0; i < A_CH; ++i) {
-    const int64_t r = v.row0 + (tid >> 3) + i * (NT / 8);
-    a_src[i] = a8_row_ptr(a, v, r) + kc * 8;
-    a_sc[i] = __builtin_ldexpf(1.0f, a8_row_exp(a, v, r));
-  }
-#pragma unroll
-  for (int i = 0; i < B_CH; ++i) {
-    int n = n0 + (tid >> 3) + i * (NT / 8);
-    if (n >= a.Nout) n = a.Nout - 1;
-    b_src[i] = v.W + static_cast<int64_t>(n) * a.K + kc * 8;
-  }
-#pragma unroll
-  for (int i = 0; i < TN; ++i)
-#pragma unroll
-    for (int j = 0; j < TM; ++j)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
-
-  uint2 ra[A_CH];
-  u32x4_t rb[B_CH];
-  Frags f;
-  gload8(ra, rb, a_src, b_src, 0);
-  lstore8(s_tile, ra, a_sc, rb, tid);
-  if (nk > 1) gload8(ra, rb, a_src, b_src, 1);
-  __syncthreads();
-  read_frags(s_tile, f, wm, wn, lane);
-  __builtin_amdgcn_sched_barrier(0);
-  int kb = 0;
-  for (; kb + 2 < nk; ++kb) {
-    rs::lds_barrier();
-    lstore8(s_tile, ra, a_sc, rb, tid);
-    gload8(ra, rb, a_src, b_src, kb + 2);
-    mfma_all(f, acc);
-    rs::lds_barrier();
-    read_frags(s_tile, f, wm, wn, lane);
-    schedule_step();
-    __builtin_amdgcn_sched_barrier(0);
-  }
-  if (kb + 1 < nk) {
-    rs::lds_barrier();
-    lstore8(s_tile, ra, a_sc, rb, tid);
-    mfma_all(f, acc);
-    rs::lds_barrier();
-    read_frags(s_tile, f, wm, wn, lane);
-  }
-  mfma_all(f, acc);
-  __syncthreads();
-}
-
-template <int H>
 template <int EPI>
 __device__ __forceinline__ void Rh<H>::epilogue(const f32x16_t (&acc)[TN][TM], const GemmArgs &a,
                                                 const TileView<uint16_t> &v, int n0,
@@ -1478,7 +1342,7 @@ __device__ __forceinline__ void stream_store(const f32x16_t (&acc)[MB][NTB], con
 // features nb*128*MB .., K part kp of kc_per chunks.  Ring stages are STRIDE
 // bf16 elements apart; `stage` is the ring position of the next chunk,
 // carried from unit to unit of one workgroup.
-template <int MB, int NTB, int S, int STRIDE, int EPI, bool FP8, int MR2>
+template <int MB, int NTB, int S, int STRIDE, int EPI>
 __device__ __forceinline__ void stream_unit(const GemmArgs &a, const StreamSplit &sp, int g,
                                             int mg, int nb, int rb, int kp, int ks, int kc_per,
                                             uint16_t *s_ring, uint32_t ring0, int &stage,
@@ -1487,15 +1351,9 @@ __device__ __forceinline__ void stream_unit(const GemmArgs &a, const StreamSplit
   constexpr int MR = 32 * NTB;                   // rows per unit
   constexpr int NB = 4 * 32 * MB;                // features per unit
   constexpr int W_INS = NB / 8 / NW;             // weight copies per wave per chunk
-  // activation copies per wave per chunk: 16-byte copies of bf16 rows, or
-  // 4-byte copies of FP8 rows (64 bytes a row) into the slot's staging area
-  constexpr int X_INS = FP8 ? MR / 16 : MR / 8 / NW;
+  constexpr int X_INS = MR / 8 / NW;             // activation copies per wave per chunk
   constexpr int LPS = W_INS + X_INS;
-  // slot layout: weights [NB][KCH], activations [MR2][KCH] (bf16, swizzled),
-  // then, for FP8 rows, their codes [MR2][64] bytes
-  constexpr int STAGE8 = (NB + MR2) * KCH * 2;   // byte offset of the FP8 staging area
-  static_assert((NB + MR) * KCH + (FP8 ? MR2 * KCH / 2 : 0) <= STRIDE, "stage fits its ring slot");
-  static_assert(MR <= MR2, "unit height");
+  static_assert((NB + MR) * KCH <= STRIDE, "stage fits its ring slot");
   static_assert((S - 2) * LPS <= 63, "vmcnt range");
   const int r32 = lane & 31, h = lane >> 5;
   const int nkc = a.K / KCH;
@@ -1508,33 +1366,17 @@ __device__ __forceinline__ void stream_unit(const GemmArgs &a, const StreamSplit
 
   // sources of this wave's copies (chunk 0 of the part)
   const uint16_t *w_src[W_INS];
-  const uint16_t *x_src[FP8 ? 1 : X_INS];
-  const uint8_t *x8_src[FP8 ? X_INS : 1];
+  const uint16_t *x_src[X_INS];
 #pragma unroll
   for (int i = 0; i < W_INS; ++i) {
     const int r = (i * NW + wave) * 8 + crow;
     const int n = min(n0 + r, a.Nout - 1);
     w_src[i] = v.W + static_cast<int64_t>(n) * a.K + kc0 * KCH + swz(r, cpos) * 8;
   }
-  // FP8 rows: copy i of wave w moves staging bytes (i NW + w) * 256 .. +255,
-  // rows 4 (i NW + w) + lane/16, bytes 4 (lane % 16) .. +3 of the row's chunk
-  float x8_scale[FP8 ? MR / 32 : 1];
-  if constexpr (FP8) {
 #pragma unroll
-    for (int i = 0; i < X_INS; ++i) {
-      const int r = (i * NW + wave) * 4 + (lane >> 4);
-      x8_src[i] = a8_row_ptr(a, v, v.row0 + r) + kc0 * KCH + (lane & 15) * 4;
-    }
-    // the rows this thread widens: (tid / 8) + 32 j
-#pragma unroll
-    for (int j = 0; j < MR / 32; ++j)
-      x8_scale[j] = __builtin_ldexpf(1.0f, a8_row_exp(a, v, v.row0 + (wave * 64 + lane) / 8 + 32 * j));
-  } else {
-#pragma unroll
-    for (int i = 0; i < X_INS; ++i) {
-      const int r = (i * NW + wave) * 8 + crow;
-      x_src[i] = a_row_ptr(a, v, v.row0 + r) + kc0 * KCH + swz(r, cpos) * 8;
-    }
+  for (int i = 0; i < X_INS; ++i) {
+    const int r = (i * NW + wave) * 8 + crow;
+    x_src[i] = a_row_ptr(a, v, v.row0 + r) + kc0 * KCH + swz(r, cpos) * 8;
   }
   // weights of a group with one row block are read once: stream them
   const bool w_once = mg == 1;
@@ -1547,15 +1389,9 @@ __device__ __forceinline__ void stream_unit(const GemmArgs &a, const StreamSplit
 #pragma unroll
       for (int i = 0; i < W_INS; ++i) dma16(w_src[i] + c * KCH, base + (i * NW + wave) * 1024);
     }
-    if constexpr (FP8) {
 #pragma unroll
-      for (int i = 0; i < X_INS; ++i)
-        dma::dma4(x8_src[i] + c * KCH, base + STAGE8 + (i * NW + wave) * 256);
-    } else {
-#pragma unroll
-      for (int i = 0; i < X_INS; ++i)
-        dma16(x_src[i] + c * KCH, base + NB * KCH * 2 + (i * NW + wave) * 1024);
-    }
+    for (int i = 0; i < X_INS; ++i)
+      dma16(x_src[i] + c * KCH, base + NB * KCH * 2 + (i * NW + wave) * 1024);
   };
 
   f32x16_t acc[MB][NTB];
@@ -1577,23 +1413,6 @@ __device__ __forceinline__ void stream_unit(const GemmArgs &a, const StreamSplit
     if (c + S - 1 < nch) issue(c + S - 1, (stage + c + S - 1) % S);
     const uint16_t *sw = s_ring + cur * STRIDE;
     const uint16_t *sx = sw + NB * KCH;
-    if constexpr (FP8) {
-      // widen the chunk's FP8 rows into the slot's bf16 activation rows:
-      // thread t takes 8 codes of row t/8 + 32 j (logical piece t % 8) and
-      // writes them, times the row's scale, where the swizzle puts that piece
-      const uint8_t *s8 = reinterpret_cast<const uint8_t *>(sw) + STAGE8;
-      uint16_t *sxw = const_cast<uint16_t *>(sx);
-      const int tid = wave * 64 + lane;
-#pragma unroll
-      for (int j = 0; j < MR / 32; ++j) {
-        const int r = tid / 8 + 32 * j, lc = tid & 7;
-        const uint2 cw = *reinterpret_cast<const uint2 *>(s8 + r * 64 + lc * 8);
-        *reinterpret_cast<u32x4_t *>(sxw + r * KCH + swz(r, lc) * 8) = widen_fp8x8(cw, x8_scale[j]);
-      }
-      // every wave's widened rows are in LDS (LDS only: the copies of later
-      // chunks stay in flight)
-      asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-    }
 #pragma unroll
     for (int kst = 0; kst < 4; ++kst) {
       const int p = 2 * kst + h;
@@ -1624,13 +1443,12 @@ __device__ __forceinline__ void stream_unit(const GemmArgs &a, const StreamSplit
 // 32*NTB rows take units of 32*NTB2 rows, so a group of up to 32*NTB2 rows
 // reads each weight block once.  Both shapes share the ring (slots sized
 // for the larger stage) and its position.
-template <int MB, int NTB, int NTB2, int S, int EPI, bool FP8 = false>
+template <int MB, int NTB, int NTB2, int S, int EPI>
 __global__ __launch_bounds__(256) void grouped_gemm_bf16_stream_kernel(GemmArgs a, StreamSplit sp) {
   using namespace st;
   constexpr int MR1 = 32 * NTB, MR2 = 32 * (NTB2 > NTB ? NTB2 : NTB);
   constexpr int NB = 4 * 32 * MB;
-  // slot: weights and bf16 activation rows, plus the FP8 staging rows
-  constexpr int STRIDE = (NB + MR2) * KCH + (FP8 ? MR2 * KCH / 2 : 0);
+  constexpr int STRIDE = (NB + MR2) * KCH;
   __shared__ __attribute__((aligned(16))) uint16_t s_ring[S * STRIDE];
   __shared__ int s_pref[kMaxGroups + 1];
   __shared__ int s_tmp[NT / 64];
@@ -1660,11 +1478,12 @@ __global__ __launch_bounds__(256) void grouped_gemm_bf16_stream_kernel(GemmArgs 
     const int uu = u - s_pref[g] * n_nb;
     const int nb = uu / mg, rb = uu % mg;
     if (NTB2 <= NTB || group_rows(a, g) <= MR1)
-      stream_unit<MB, NTB, S, STRIDE, EPI, FP8, MR2>(a, sp, g, mg, nb, rb, kp, ks_u, per, s_ring,
-                                                     ring0, stage, lane, wave, piece);
+      stream_unit<MB, NTB, S, STRIDE, EPI>(a, sp, g, mg, nb, rb, kp, ks_u, per, s_ring, ring0,
+                                           stage, lane, wave, piece);
     else
-      stream_unit<MB, (NTB2 > NTB ? NTB2 : NTB), S, STRIDE, EPI, FP8, MR2>(
-          a, sp, g, mg, nb, rb, kp, ks_u, per, s_ring, ring0, stage, lane, wave, piece);
+      stream_unit<MB, (NTB2 > NTB ? NTB2 : NTB), S, STRIDE, EPI>(a, sp, g, mg, nb, rb, kp, ks_u,
+                                                                 per, s_ring, ring0, stage, lane,
+                                                                 wave, piece);
   };
   // unit order: part fastest, then row block, then feature block, so the
   // workgroups running together share a weight block in L2
@@ -1823,46 +1642,6 @@ __global__ __launch_bounds__(256) void stream_finish_kernel(GemmArgs a, StreamSp
 }
 
 // ---------------------------------------------------------------------------
-// FP8-dispatched rows of groups above 128 rows: 128 x 256 tiles, registers
-// staging both operands (8-byte FP8 pieces for A, widened as they are stored
-// to LDS).  Persistent workgroups, the tile list split into eight contiguous
-// parts (one per XCD) and banded by eight m-tiles (1,024 rows), so the
-// workgroups of one XCD share a weight block across an expert's rows.
-// ---------------------------------------------------------------------------
-template <int EPI>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
-void grouped_gemm_bf16_rh_fp8_kernel(GemmArgs a) {
-  using R = Rh<128>;
-  constexpr int NT = 256;
-  // the tile (384 x 64 bf16) and, in the epilogue, 128 x 256 staged outputs
-  __shared__ __attribute__((aligned(16))) uint16_t s_tile[R::BM * R::BN];
-  static_assert((R::BM + R::BN) * R::BK <= R::BM * R::BN, "tile fits the epilogue staging");
-  __shared__ int s_pref[kMaxGroups + 1];
-  __shared__ int s_tmp[NT / 64];
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = uniform(tid >> 6);
-  const int wm = wave & 1, wn = wave >> 1;
-  const int n_groups = a.n_routed + a.n_shared;
-  const int total_m = build_tile_prefix<NT, R::BM>(a, s_pref, s_tmp);
-  const int n_nt = (a.Nout + R::BN - 1) / R::BN;
-  const int total = total_m * n_nt;
-  const int xcd = blockIdx.x % kXcds, slot = blockIdx.x / kXcds, nslots = gridDim.x / kXcds;
-  const int part = (total + kXcds - 1) / kXcds;
-  const int begin = xcd * part, end = min(total, begin + part);
-  const int nk = a.K / R::BK;
-  for (int L = begin + slot; L < end; L += nslots) {
-    int mt, nt;
-    decode_tile<8>(L, total_m, n_nt, &mt, &nt);
-    const int g = find_group(s_pref, n_groups, mt);
-    const TileView<uint16_t> v = tile_view<uint16_t>(a, g, mt - s_pref[g], R::BM);
-    f32x16_t acc[R::TN][R::TM];
-    R::tile_fp8(a, v, nt * R::BN, nk, s_tile, tid, lane, wm, wn, acc);
-    R::epilogue<EPI>(acc, a, v, nt * R::BN, s_tile, lane, wm, wn, tid);
-  }
-}
-
-// ---------------------------------------------------------------------------
 // fp32 VALU kernel: 64x64 tiles, 256 threads
 // ---------------------------------------------------------------------------
 template <typename TA, int EPI>
@@ -1974,8 +1753,6 @@ GemmArgs make_args(const GemmGroups &g) {
   a.K = g.K;
   a.cls_lo = 0;
   a.cls_hi = INT64_MAX;
-  a.A8 = g.A8;
-  a.a8_exp = g.a8_exp;
   return a;
 }
 
@@ -2002,7 +1779,7 @@ int64_t split_rows(const GemmGroups &g) {
   return g.max_routed_rows + static_cast<int64_t>(g.n_shared) * g.T_sh;
 }
 
-template <int MB, int NTB, int S, int NTB2 = 0, bool FP8 = false>
+template <int MB, int NTB, int S, int NTB2 = 0>
 hipError_t launch_bf16_stream(const GemmArgs &a, const GemmGroups &g, Epilogue epi, int per_cu,
                               hipStream_t s) {
   // scratch: [0, 256) the split the kernel chose; then the last-round piece
@@ -2028,11 +1805,11 @@ hipError_t launch_bf16_stream(const GemmArgs &a, const GemmGroups &g, Epilogue e
   const unsigned grid =
       persistent_grid(tiles_upper_bound(g, 32 * NTB, 128 * MB) * sp.ks_cap, per_cu);
   if (epi == kEpiBiasSilu)
-    hipLaunchKernelGGL((grouped_gemm_bf16_stream_kernel<MB, NTB, NTB2, S, kEpiBiasSilu, FP8>),
+    hipLaunchKernelGGL((grouped_gemm_bf16_stream_kernel<MB, NTB, NTB2, S, kEpiBiasSilu>),
                        dim3(grid), dim3(256), 0, s, a, sp);
   else
-    hipLaunchKernelGGL((grouped_gemm_bf16_stream_kernel<MB, NTB, NTB2, S, kEpiBias, FP8>),
-                       dim3(grid), dim3(256), 0, s, a, sp);
+    hipLaunchKernelGGL((grouped_gemm_bf16_stream_kernel<MB, NTB, NTB2, S, kEpiBias>), dim3(grid),
+                       dim3(256), 0, s, a, sp);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || !sp.ks_used) return e;
   // fpu workgroups per possible last-round unit (at most half of each XCD's
@@ -2122,31 +1899,6 @@ size_t grouped_gemm_split_bytes(const GemmGroups &g) {
 hipError_t launch_grouped_gemm(bool bf16, const GemmGroups &g, Epilogue epi, hipStream_t s) {
   GemmArgs a = make_args(g);
   if (g.n_routed + g.n_shared <= 0 || g.Nout <= 0) return hipSuccess;
-  if (g.A8) {
-    // FP8-dispatched rows of routed groups (no shared groups in this launch):
-    // the stream kernel at every group size, its activation rows widened in
-    // LDS; decode-sized groups take the deep 32-row ring, others 64- and
-    // 128-row units of 128 features (the staging rows leave no room for 256)
-    if (!bf16 || g.n_shared != 0 || g.K % 64 != 0 || g.Nout % 4 != 0 || !g.a8_exp)
-      return hipErrorInvalidValue;
-    constexpr int64_t kStreamRows = 128;
-    if (g.max_group_rows <= 32) return launch_bf16_stream<1, 1, 6, 0, true>(a, g, epi, 1, s);
-    if (g.max_group_rows <= kStreamRows) return launch_bf16_stream<1, 2, 3, 4, true>(a, g, epi, 1, s);
-    // groups above 128 rows on 128 x 256 tiles; the rest on the stream kernel
-    // when the mean leaves room for them
-    const int64_t mean_rows = g.max_routed_rows / (g.n_routed > 0 ? g.n_routed : 1);
-    GemmArgs ab = a, as = a;
-    ab.cls_lo = kStreamRows + 1;
-    as.cls_hi = kStreamRows;
-    const unsigned grid = persistent_grid(tiles_upper_bound(g, 128, 256), 1);
-    if (epi == kEpiBiasSilu)
-      hipLaunchKernelGGL((grouped_gemm_bf16_rh_fp8_kernel<kEpiBiasSilu>), dim3(grid), dim3(256), 0, s, ab);
-    else
-      hipLaunchKernelGGL((grouped_gemm_bf16_rh_fp8_kernel<kEpiBias>), dim3(grid), dim3(256), 0, s, ab);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess || mean_rows >= 384) return e;
-    return launch_bf16_stream<1, 2, 3, 4, true>(as, g, epi, 1, s);
-  }
   if (bf16 && g.K % 64 == 0 && g.Nout % 4 == 0) {
     // Groups of up to kStreamRows rows are bound by their weight stream and
     // go to the stream kernel (units of 64 rows up to 64 rows, else 128, so

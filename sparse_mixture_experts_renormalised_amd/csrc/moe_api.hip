@@ -87,6 +87,7 @@ struct LayerWs {
   size_t split_bytes;
   uint8_t *xq;     // FP8 dispatch: E4M3 codes [T][d] (else null)
   int32_t *xexp;   // FP8 dispatch: scale exponents [T] (else null)
+  void *xw;        // FP8 dispatch: the codes widened back to bf16 [T][d] (else null)
   size_t bytes;
 };
 
@@ -146,6 +147,7 @@ LayerWs layer_ws(const moe_config *c, void *base, size_t split_cap = SIZE_MAX) {
   const bool fp8 = c->dispatch == MOE_DISPATCH_FP8;
   w.xq = fp8 ? static_cast<uint8_t *>(take(static_cast<size_t>(T) * c->d_model)) : nullptr;
   w.xexp = fp8 ? static_cast<int32_t *>(take(sizeof(int32_t) * T)) : nullptr;
+  w.xw = fp8 ? take(ab * T * c->d_model) : nullptr;
   size_t sb = layer_split_bytes(c);
   if (sb > split_cap) sb = split_cap & ~(kAlign - 1);
   w.split = sb ? take(sb) : nullptr;
@@ -484,30 +486,16 @@ int run_layer(const moe_config *cfg, const moe_weights *w, const void *x, void *
   g.split_bytes = L.split ? L.split_bytes : 0;
   if ((st = mark(MOE_STAGE_UP)) != MOE_OK) return st;
   if (cfg->dispatch == MOE_DISPATCH_FP8) {
-    // FP8 dispatch: the routed rows go out as E4M3 codes with a per-row
-    // scale and are widened in the first Linear; the shared experts, which
-    // are not dispatched, take x in its own launch
-    st = hip_status(moe::launch_quantize_fp8(x, T, cfg->d_model, L.xq, L.xexp, s));
+    // FP8 dispatch: the token rows go out as E4M3 codes with a per-row scale
+    // (L.xq, L.xexp) and arrive widened back to bf16 (L.xw), in one pass; the
+    // routed groups read the arrived rows, the shared experts, which are not
+    // dispatched, read x, in the same launch
+    st = hip_status(moe::launch_quantize_fp8(x, T, cfg->d_model, L.xq, L.xexp, L.xw, s));
     if (st != MOE_OK) return st;
-    GemmGroups gr = g;
-    gr.n_shared = 0;
-    gr.A8 = L.xq;
-    gr.a8_exp = L.xexp;
-    st = hip_status(moe::launch_grouped_gemm(bf16, gr, moe::kEpiBiasSilu, s));
-    if (st != MOE_OK) return st;
-    if (Ks > 0) {
-      GemmGroups gs = g;
-      gs.n_routed = 0;
-      gs.a_index = nullptr;
-      gs.max_routed_rows = 0;
-      gs.max_group_rows = 0;
-      st = hip_status(moe::launch_grouped_gemm(bf16, gs, moe::kEpiBiasSilu, s));
-      if (st != MOE_OK) return st;
-    }
-  } else {
-    st = hip_status(moe::launch_grouped_gemm(bf16, g, moe::kEpiBiasSilu, s));
-    if (st != MOE_OK) return st;
+    g.A = L.xw;
   }
+  st = hip_status(moe::launch_grouped_gemm(bf16, g, moe::kEpiBiasSilu, s));
+  if (st != MOE_OK) return st;
 
   // Second Linear.
   g.A = L.h;

@@ -95,11 +95,6 @@ struct GemmGroups {
   // a product's work does not divide evenly over the chip; NULL: never split.
   void *split_ws;
   size_t split_bytes;
-  // FP8-dispatched A rows of the routed groups (instead of A): E4M3 codes
-  // [rows][K] read through a_index, and a power-of-two exponent per row; the
-  // launch then holds routed groups only (n_shared == 0).
-  const uint8_t *A8;
-  const int32_t *a8_exp;
 };
 
 // Scratch bytes with which launch_grouped_gemm splits this product (and
@@ -125,8 +120,10 @@ hipError_t launch_gather_rows(bool bf16, const void *x, const int32_t *row_token
                               const int32_t *total_rows, int64_t max_rows, int d, void *out,
                               hipStream_t s);
 hipError_t launch_grouped_gemm(bool bf16, const GemmGroups &g, Epilogue epi, hipStream_t s);
+// E4M3 codes q [T][d] and per-row scale exponents exps [T] of x (bf16), and,
+// when xw is not null, the codes widened back to bf16 rows xw [T][d].
 hipError_t launch_quantize_fp8(const void *x, int64_t T, int d, uint8_t *q, int32_t *exps,
-                               hipStream_t s);
+                               void *xw, hipStream_t s);
 hipError_t launch_combine(bool bf16, const void *y_rows, const int32_t *slot_row,
                           const float *gates, const void *shared_out, int n_shared, int64_t T,
                           int K, int d, void *y, hipStream_t s);

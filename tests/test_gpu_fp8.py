@@ -58,11 +58,11 @@ SMALL = [
     W.custom_workload("fp8_small", T=333, d_model=128, n_routed=16, top_k=4, n_shared=1,
                       d_ff=256, dtype="bf16", router_bias="gauss", router_bias_var=0.5,
                       dispatch_fp8=True),
-    # decode-sized groups: the 32-row ring, a K split of the few units
+    # decode-sized groups (the weight-streaming kernel, with capacity drops)
     W.custom_workload("fp8_decode_like", T=64, d_model=512, n_routed=64, top_k=6, n_shared=1,
                       d_ff=192, dtype="bf16", router_bias="zipf", zipf_s=1.1,
                       capacity_factor=1.25, dispatch_fp8=True),
-    # groups of more than 128 rows: several 128-row units per group, ragged
+    # groups of more than 128 rows (the 256x256 kernel), ragged, two shared experts
     W.custom_workload("fp8_big_groups", T=700, d_model=256, n_routed=4, top_k=2, n_shared=2,
                       d_ff=320, dtype="bf16", expert_bias=True, dispatch_fp8=True),
     W.custom_workload("fp8_T1", T=1, d_model=128, n_routed=8, top_k=2, n_shared=0, d_ff=128,
