@@ -289,6 +289,9 @@ typedef struct {
     size_t slot_row;    /* [T][K] int32 (-1 = dropped)                        */
     size_t x_fp8;       /* MOE_DISPATCH_FP8: [T][d] uint8 E4M3 codes, else 0  */
     size_t x_fp8_exp;   /* MOE_DISPATCH_FP8: [T] int32 scale exponents, else 0 */
+    size_t x_fp8_wide;  /* MOE_DISPATCH_FP8: [T][d] bf16, the codes widened back
+                           (2^E times each code's value: the rows the first
+                           Linear reads), else 0                             */
     size_t total;       /* moe_workspace_size(cfg)                            */
 } moe_ws_layout;
 

@@ -51,7 +51,7 @@ class WsLayout(ctypes.Structure):
     """Mirror of moe_ws_layout (byte offsets into the layer workspace)."""
     _fields_ = [(n, ctypes.c_size_t) for n in
                 ("logits", "topk_idx", "topk_gate", "counts", "offsets", "n_dropped", "row_token",
-                 "slot_row", "x_fp8", "x_fp8_exp", "total")]
+                 "slot_row", "x_fp8", "x_fp8_exp", "x_fp8_wide", "total")]
 
 
 class Weights(ctypes.Structure):

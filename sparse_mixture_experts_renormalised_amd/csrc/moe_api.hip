@@ -382,6 +382,7 @@ int moe_workspace_layout(const moe_config *cfg, moe_ws_layout *out) {
   out->slot_row = off(L.slot_row);
   out->x_fp8 = L.xq ? off(L.xq) : 0;
   out->x_fp8_exp = L.xexp ? off(L.xexp) : 0;
+  out->x_fp8_wide = L.xw ? off(L.xw) : 0;
   out->total = L.bytes;
   return MOE_OK;
 }

@@ -134,8 +134,23 @@ def test_workspace_layout(B):
     # 256-aligned, disjoint, inside the workspace
     for (o, n), (o2, _) in zip(regions, regions[1:] + [(lay.total, 0)]):
         assert o % 256 == 0 and o + n <= o2
+    assert lay.x_fp8 == lay.x_fp8_exp == lay.x_fp8_wide == 0   # bf16 dispatch
     with pytest.raises(B.MoeError):
         B.workspace_layout(B.config(64, 128, 4, 5, 0, 256, "bf16"))
+
+
+def test_workspace_layout_fp8_dispatch(B):
+    T, d, N, K = 333, 128, 16, 4
+    cfg = B.config(T, d, N, K, 1, 256, "bf16", dispatch_fp8=True)
+    lay = B.workspace_layout(cfg)
+    assert lay.total == B.workspace_size(cfg)
+    assert lay.total > B.workspace_size(B.config(T, d, N, K, 1, 256, "bf16"))
+    regions = sorted([(lay.logits, T * N * 4), (lay.topk_idx, T * K * 4), (lay.topk_gate, T * K * 4),
+                      (lay.counts, N * 4), (lay.offsets, (N + 1) * 4), (lay.n_dropped, 4),
+                      (lay.row_token, T * K * 4), (lay.slot_row, T * K * 4),
+                      (lay.x_fp8, T * d), (lay.x_fp8_exp, T * 4), (lay.x_fp8_wide, T * d * 2)])
+    for (o, n), (o2, _) in zip(regions, regions[1:] + [(lay.total, 0)]):
+        assert o % 256 == 0 and o + n <= o2
 
 
 def test_empty_batch_is_a_no_op(B):

@@ -1,7 +1,7 @@
 """FP8 dispatch (MOE_DISPATCH_FP8) of the HIP library against the oracle's
 reading of it (DeepEP page, section "DeepEP とは？" item 5, and section
-"DeepEP の性能": FP8 dispatch, BF16 combine): E4M3 codes and per-row
-exponents bit exact, routing bit exact, y within the bf16 tolerance of the
+"DeepEP の性能": FP8 dispatch, BF16 combine): E4M3 codes, per-row
+exponents and the rows widened back to bf16 bit exact, routing bit exact, y within the bf16 tolerance of the
 oracle's layer on the dispatched rows (all of [T, d] and every row), on small
 layers, on rows that use every code, and on the four large workloads at full
 size.  The FP8 layer's distance from the bf16 dispatch is bounded by the
@@ -44,6 +44,10 @@ def check_fp8_layer(dl, label):
     r = dl.routing_from_workspace()
     assert np.array_equal(r["fp8_exp"], ref["fp8_exp"]), label
     assert np.array_equal(r["fp8_codes"], ref["fp8_codes"]), label
+    # the rows the first Linear reads: every code widened to 2^E times its
+    # value, which bf16 holds exactly, so they compare bit for bit
+    wide = torch.from_numpy(oracle.dequantize_fp8_rows(ref["fp8_exp"], ref["fp8_codes"]))
+    assert np.array_equal(r["fp8_wide"], wide.to(torch.bfloat16).view(torch.int16).numpy()), label
     assert np.array_equal(dl.topk_idx.cpu().numpy(), ref["topk_idx"]), label
     assert np.array_equal(dl.counts.cpu().numpy(), ref["counts"]), label
     assert np.array_equal(r["slot_row"], ref["slot_row"]), label

@@ -70,6 +70,8 @@ class DeviceLayer:
         if lay.x_fp8:
             out["fp8_codes"] = region(lay.x_fp8, T * wl.d_model, torch.uint8).reshape(T, wl.d_model)
             out["fp8_exp"] = region(lay.x_fp8_exp, T, torch.int32)
+            out["fp8_wide"] = region(lay.x_fp8_wide, T * wl.d_model,
+                                     torch.int16).reshape(T, wl.d_model)
         return out | {
             "logits": region(lay.logits, T * N, torch.float32).reshape(T, N),
             "offsets": offsets,
