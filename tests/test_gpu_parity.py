@@ -452,6 +452,8 @@ def test_grouped_ffn_matches_oracle(case):
         torch.cuda.synchronize()
         assert rel_l2(host(h)[:R], H) <= TOL[dtype]
         assert rel_l2(host(y)[:R], Y) <= TOL[dtype]
+        assert row_rel_l2_max(host(h)[:R], H) <= ROW_TOL[dtype]
+        assert row_rel_l2_max(host(y)[:R], Y) <= ROW_TOL[dtype]
 
 
 # ---------------------------------------------------------------------------

@@ -1,4 +1,5 @@
-"""Seeded random small layers through moe_layer_forward against the oracle.
+"""Seeded random small layers through moe_layer_forward, and seeded random
+grouped FFN products through moe_grouped_ffn, against the oracle.
 
 Shapes, dtypes, capacity factors, router biases (in the logit or for the
 selection only), expert biases and the FP8 dispatch are drawn from a fixed
@@ -9,7 +10,12 @@ layer gets the checks of the hand-picked cases: routing outputs bit exact
 (ids, counts, and from the workspace the logits, offsets, row_token, slot_row
 and n_dropped; the FP8 codes, exponents and widened rows), gates within 1e-6,
 y within the global and the per-row tolerance of the oracle's layer
-(DeepSeekMoE explainer page, section 共有エキスパート機構, output equation)."""
+(DeepSeekMoE explainer page, section 共有エキスパート機構, output equation).
+The grouped products mix empty, one-row, small, tail-sized and large groups
+over widths up to 4096, with tight, loose (a wider grid, whose partial rounds
+split along K or M) and very large row bounds (64-bit copy addresses), each
+with and without the split scratch; H and Y within the global and per-row
+tolerance (the same page, section アルゴリズム: Linear - SiLU - Linear)."""
 import numpy as np
 import pytest
 import torch
@@ -18,8 +24,8 @@ import oracle
 import workloads as W
 import workloads.device  # noqa: F401
 
-from test_gpu_parity import (ROW_TOL, TOL, bias_np, check_layer, host, providers_host, rel_l2,
-                             row_rel_l2_max)
+from test_gpu_parity import (B, ROW_TOL, TOL, act_dtype, bias_np, cfg_of, check_layer, host,
+                             providers_host, rel_l2, row_rel_l2_max)
 from test_gpu_fp8 import check_fp8_layer
 
 pytestmark = pytest.mark.gpu
@@ -102,3 +108,71 @@ def test_random_layers_cover_the_options():
     assert any(w.capacity_factor > 0 for w in LAYERS)
     assert any(w.n_shared == 2 for w in LAYERS)
     assert any(w.T == 1 for w in LAYERS) and any(w.top_k > 32 for w in LAYERS)
+
+
+def random_ffns(n, seed):
+    rng = np.random.default_rng(seed)
+    kinds = [lambda: 0, lambda: 1, lambda: int(rng.integers(2, 65)),
+             lambda: int(rng.integers(65, 129)), lambda: int(rng.integers(129, 257)),
+             lambda: int(rng.integers(257, 513)), lambda: int(rng.integers(513, 1100))]
+    out = []
+    for i in range(n):
+        dtype = "bf16" if rng.random() < 0.85 else "f32"
+        q = 64 if dtype == "bf16" else 16
+        while True:
+            G = int(rng.integers(1, 41))
+            w = rng.dirichlet(np.ones(len(kinds)))
+            rows = [kinds[int(rng.choice(len(kinds), p=w))]() for _ in range(G)]
+            R = sum(rows)
+            d = q * int(rng.integers(1, 4096 // q + 1))
+            f = q * int(rng.integers(1, 4096 // q + 1))
+            if R <= 2500 and d * f <= 3_000_000 and R * d * f <= 2.5e9:
+                break
+        mode = str(rng.choice(["tight", "loose", "loose", "wide"])) if dtype == "bf16" else "tight"
+        max_rows = {"tight": max(R, 1), "loose": max(R, 1) * int(rng.choice([2, 4, 8])),
+                    "wide": 1100000}[mode]
+        out.append((f"ffn{i}", rows, d, f, dtype, bool(rng.random() < 0.5), max_rows,
+                    int(rng.integers(0, 1000))))
+    return out
+
+
+FFNS = random_ffns(20, 77)
+
+
+@pytest.mark.parametrize("case", FFNS, ids=lambda c: c[0])
+def test_random_grouped_ffn_matches_oracle(case):
+    b = B()
+    name, rows, d, f, dtype, eb, max_rows, seed = case
+    print(f"[random ffn] {case}", flush=True)
+    G, R = len(rows), int(sum(rows))
+    wl = W.custom_workload(name, T=max(R, 1), d_model=d, n_routed=G, top_k=1, n_shared=0,
+                           d_ff=f, dtype=dtype, expert_bias=eb, seed=seed)
+    cfg = cfg_of(wl)
+    x_rows = W.fill_normal((max(R, 1), d), 1.0, dtype, 3, 1, 0, "cuda")
+    w1, b1, w2, b2 = wl.stacked(False, "cuda")
+    offs = np.concatenate([[0], np.cumsum(rows)]).astype(np.int32)
+    offsets = torch.from_numpy(offs).cuda()
+    act = act_dtype(wl)
+    routed, _ = providers_host(wl)
+    H, Y = oracle.grouped_ffn(host(x_rows), offs, routed, G)
+    nws = b.grouped_ffn_workspace_size(cfg, G, max_rows)
+    for ws in (None, torch.empty(max(nws, 1), dtype=torch.uint8, device="cuda") if nws else None):
+        h = torch.zeros((max(R, 1), f), dtype=act, device="cuda")
+        y = torch.zeros((max(R, 1), d), dtype=act, device="cuda")
+        b.grouped_ffn(cfg, G, x_rows, offsets, max_rows, w1, b1, w2, b2, h, y, ws=ws)
+        torch.cuda.synchronize()
+        if R == 0:
+            continue
+        assert rel_l2(host(h)[:R], H) <= TOL[dtype] and rel_l2(host(y)[:R], Y) <= TOL[dtype]
+        assert row_rel_l2_max(host(h)[:R], H) <= ROW_TOL[dtype]
+        assert row_rel_l2_max(host(y)[:R], Y) <= ROW_TOL[dtype]
+
+
+def test_random_ffns_cover_the_paths():
+    modes = {("wide" if c[6] == 1100000 else "loose" if c[6] > max(sum(c[1]), 1) else "tight")
+             for c in FFNS}
+    assert modes == {"tight", "loose", "wide"}
+    assert any(c[4] == "f32" for c in FFNS)
+    sizes = [r for c in FFNS for r in c[1]]
+    assert 0 in sizes and 1 in sizes and any(129 <= r <= 256 for r in sizes)
+    assert any(r > 512 for r in sizes)
