@@ -1,5 +1,6 @@
-"""Seeded random small layers through moe_layer_forward, and seeded random
-grouped FFN products through moe_grouped_ffn, against the oracle.
+"""Seeded random small layers through moe_layer_forward, seeded random
+grouped FFN products through moe_grouped_ffn, and seeded random router and
+dispatch cases through moe_route and moe_permute, against the oracle.
 
 Shapes, dtypes, capacity factors, router biases (in the logit or for the
 selection only), expert biases and the FP8 dispatch are drawn from a fixed
@@ -15,7 +16,12 @@ The grouped products mix empty, one-row, small, tail-sized and large groups
 over widths up to 4096, with tight, loose (a wider grid, whose partial rounds
 split along K or M) and very large row bounds (64-bit copy addresses), each
 with and without the split scratch; H and Y within the global and per-row
-tolerance (the same page, section アルゴリズム: Linear - SiLU - Linear)."""
+tolerance (the same page, section アルゴリズム: Linear - SiLU - Linear).
+The router cases span one token to 9,000, 1 to 1,024 experts, any top-K up to
+min(N, 64), widths up to 2,048 in both dtypes and all three router biases;
+logits and ids bit exact, gates within 1e-6; the dispatch of that routing
+under a random capacity bit exact, gathered rows exact copies (Top-K routing
+page, section 解決策2: エキスパートキャパシティファクター)."""
 import numpy as np
 import pytest
 import torch
@@ -176,3 +182,64 @@ def test_random_ffns_cover_the_paths():
     sizes = [r for c in FFNS for r in c[1]]
     assert 0 in sizes and 1 in sizes and any(129 <= r <= 256 for r in sizes)
     assert any(r > 512 for r in sizes)
+
+
+def random_routes(n, seed):
+    rng = np.random.default_rng(seed)
+    out = []
+    for i in range(n):
+        dtype = "bf16" if rng.random() < 0.7 else "f32"
+        q = 64 if dtype == "bf16" else 16
+        while True:
+            T = int(rng.choice([1, 2, 15, 16, 17, 63, 64, 65, 128, 129, 500, 1500, 4096, 9000]))
+            N = int(rng.choice([1, 2, 3, 4, 7, 8, 9, 15, 16, 17, 31, 32, 33, 64, 100, 256, 257,
+                                300, 512, 1000, 1024]))
+            d = q * int(rng.integers(1, 2048 // q + 1))
+            K = int(rng.integers(1, min(N, 64) + 1))
+            if T * N * d <= 1.5e9 and T * K * d <= 3e8:   # oracle time, gathered bytes
+                break
+        rb = str(rng.choice(["none", "gauss", "zipf"]))
+        C = int(rng.choice([-1, -1, 0, 1, 2, 5, 17, 1000]))
+        out.append((f"rp{i}", dtype, T, d, N, K, rb, C, int(rng.integers(0, 1000))))
+    return out
+
+
+# seed 27 was chosen so that the set reaches every launch shape of the router
+# (one-logit-per-lane kernels for N = 1, 2 and more; the three matrix-core
+# shapes; the float32 register-tiled kernels at both chunk widths)
+ROUTES = random_routes(120, 27)
+
+
+@pytest.mark.parametrize("case", ROUTES, ids=lambda c: c[0])
+def test_random_route_and_permute_bit_exact(case):
+    b = B()
+    name, dtype, T, d, N, K, rb, C, seed = case
+    print(f"[random route] {case}", flush=True)
+    wl = W.custom_workload(name, T=T, d_model=d, n_routed=N, top_k=K, n_shared=0, d_ff=64,
+                           dtype=dtype, router_bias=rb, router_bias_var=0.5, zipf_s=1.1,
+                           seed=seed)
+    cfg = cfg_of(wl)
+    x, wr, rbv = wl.x("cuda"), wl.w_router("cuda"), wl.router_bias_values("cuda")
+    logits = torch.empty((T, N), dtype=torch.float32, device="cuda")
+    idx = torch.empty((T, K), dtype=torch.int32, device="cuda")
+    gates = torch.empty((T, K), dtype=torch.float32, device="cuda")
+    b.route(cfg, x, wr, rbv, logits, idx, gates)
+    torch.cuda.synchronize()
+    ref_l, ref_i, ref_g = oracle.route(host(x), host(wr), bias_np(wl), K)
+    assert np.array_equal(logits.cpu().numpy().view(np.uint32), ref_l.view(np.uint32))
+    assert np.array_equal(idx.cpu().numpy(), ref_i)
+    assert np.abs(gates.cpu().numpy() - ref_g).max() <= 1e-6
+    cfg_c = cfg_of(wl, capacity=C)
+    st = W.device.stage_tensors(wl)
+    ws = torch.empty((b.permute_workspace_size(cfg_c),), dtype=torch.uint8, device="cuda")
+    b.permute(cfg_c, idx, x, st["counts"], st["offsets"], st["row_token"], st["slot_row"],
+              st["n_dropped"], st["x_perm"], ws)
+    torch.cuda.synchronize()
+    ref = oracle.dispatch(ref_i, N, None if C < 0 else C)
+    R = int(ref["offsets"][-1])
+    assert np.array_equal(st["counts"].cpu().numpy(), ref["counts"])
+    assert np.array_equal(st["offsets"].cpu().numpy(), ref["offsets"])
+    assert np.array_equal(st["row_token"][:R].cpu().numpy(), ref["row_token"])
+    assert np.array_equal(st["slot_row"].cpu().numpy().reshape(T, K), ref["slot_row"])
+    assert int(st["n_dropped"].item()) == ref["n_dropped"]
+    assert torch.equal(st["x_perm"][:R].cpu(), x.cpu()[torch.from_numpy(ref["row_token"]).long()])
