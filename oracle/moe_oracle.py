@@ -372,7 +372,12 @@ def combine(y_rows, slot_row, gates, shared_out=None) -> np.ndarray:
     slot_row = np.asarray(slot_row)
     T, K = slot_row.shape
     y_rows = np.asarray(y_rows, dtype=np.float64)
-    d = y_rows.shape[1] if y_rows.size else (shared_out.shape[2] if shared_out is not None else 0)
+    # the width comes from the expert rows even when every slot was dropped
+    # (an empty [0, d] array); a bare empty array leaves it to the shared outputs
+    if y_rows.ndim == 2:
+        d = y_rows.shape[1]
+    else:
+        d = shared_out.shape[2] if shared_out is not None else 0
     out = np.zeros((T, d), dtype=np.float64)
     if shared_out is not None:
         for i in range(shared_out.shape[0]):

@@ -409,6 +409,18 @@ def test_zero_capacity_leaves_only_shared_experts():
     assert np.allclose(out["y"], ref, rtol=1e-12, atol=1e-12)
 
 
+def test_combine_with_every_slot_dropped_and_no_shared_expert_is_zero():
+    # a token whose K slots are all dropped gets only the shared sum, here
+    # empty: y = 0 at the rows' width, also when no routed row was kept
+    T, K, d = 5, 3, 7
+    slot_row = np.full((T, K), -1, dtype=np.int32)
+    y = oracle.combine(np.zeros((0, d)), slot_row, np.full((T, K), 1.0 / K))
+    assert y.shape == (T, d) and not y.any()
+    S = np.arange(2 * T * d, dtype=np.float64).reshape(2, T, d)
+    y = oracle.combine(np.zeros((0, d)), slot_row, np.full((T, K), 1.0 / K), S)
+    assert np.array_equal(y, S[0] + S[1])
+
+
 def test_capacity_that_drops_nothing_equals_unlimited():
     wl = SMALL[1]
     routed, shared = providers(wl)
