@@ -488,6 +488,7 @@ def test_combine_matches_oracle(dtype, Ks, C, T, N, K, d):
     torch.cuda.synchronize()
     ref = oracle.combine(host(y_rows)[:R], disp["slot_row"], g, None if shared is None else host(shared))
     assert rel_l2(host(y), ref) <= TOL[dtype]
+    assert row_rel_l2_max(host(y), ref) <= ROW_TOL[dtype]
 
 
 # ---------------------------------------------------------------------------

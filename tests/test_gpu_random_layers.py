@@ -1,6 +1,7 @@
-"""Seeded random small layers through moe_layer_forward, seeded random
-grouped FFN products through moe_grouped_ffn, and seeded random router and
-dispatch cases through moe_route and moe_permute, against the oracle.
+"""Seeded random cases of every entry point against the oracle: small layers
+through moe_layer_forward, grouped FFN products through moe_grouped_ffn,
+router and dispatch cases through moe_route and moe_permute, combines through
+moe_combine and balance statistics through moe_balance_stats.
 
 Shapes, dtypes, capacity factors, router biases (in the logit or for the
 selection only), expert biases and the FP8 dispatch are drawn from a fixed
@@ -21,7 +22,12 @@ The router cases span one token to 9,000, 1 to 1,024 experts, any top-K up to
 min(N, 64), widths up to 2,048 in both dtypes and all three router biases;
 logits and ids bit exact, gates within 1e-6; the dispatch of that routing
 under a random capacity bit exact, gathered rows exact copies (Top-K routing
-page, section 解決策2: エキスパートキャパシティファクター)."""
+page, section 解決策2: エキスパートキャパシティファクター).
+The combines draw T, N, K, the shared experts, the width and the capacity;
+y within the global and per-row tolerance (DeepSeekMoE explainer page,
+section 共有エキスパート機構, output equation).  The balance statistics draw T,
+N and K; f exact as counts, P and the loss within 1e-5 relative (the same
+page, section ルーティングとバランス損失)."""
 import numpy as np
 import pytest
 import torch
@@ -243,3 +249,92 @@ def test_random_route_and_permute_bit_exact(case):
     assert np.array_equal(st["slot_row"].cpu().numpy().reshape(T, K), ref["slot_row"])
     assert int(st["n_dropped"].item()) == ref["n_dropped"]
     assert torch.equal(st["x_perm"][:R].cpu(), x.cpu()[torch.from_numpy(ref["row_token"]).long()])
+
+
+def random_combines(n, seed):
+    rng = np.random.default_rng(seed)
+    out = []
+    for i in range(n):
+        dtype = "bf16" if rng.random() < 0.75 else "f32"
+        q = 64 if dtype == "bf16" else 16
+        T = int(rng.choice([1, 2, 63, 64, 65, 300, 1023, 1024, 1025, 3000]))
+        N = int(rng.choice([1, 2, 8, 33, 256, 1024]))
+        K = int(rng.integers(1, min(N, 64) + 1))
+        d = q * int(rng.integers(1, 4224 // q + 1))
+        while T * K * d > 4e7:
+            d = max(q, (d // 2) // q * q)
+            if d == q:
+                break
+        Ks = int(rng.integers(0, 4))
+        C = int(rng.choice([-1, -1, 0, 1, 3, 50]))
+        out.append((f"cb{i}", dtype, T, N, K, d, Ks, C, int(rng.integers(0, 1000))))
+    return out
+
+
+COMBINES = random_combines(40, 11)
+
+
+@pytest.mark.parametrize("case", COMBINES, ids=lambda c: c[0])
+def test_random_combine_matches_oracle(case):
+    b = B()
+    name, dtype, T, N, K, d, Ks, C, seed = case
+    print(f"[random combine] {case}", flush=True)
+    wl = W.custom_workload(name, T=T, d_model=d, n_routed=N, top_k=K, n_shared=Ks, d_ff=64,
+                           dtype=dtype)
+    rng = np.random.default_rng(seed)
+    idx_h = np.stack([rng.permutation(N)[:K] for _ in range(T)]).astype(np.int32)
+    disp = oracle.dispatch(idx_h, N, None if C < 0 else C)
+    R = int(disp["offsets"][-1])
+    g = rng.random((T, K)) + 0.1
+    g = (g / g.sum(1, keepdims=True)).astype(np.float32)
+    act = act_dtype(wl)
+    y_rows = W.fill_normal((max(R, 1), d), 1.0, dtype, seed, 20, 0, "cuda")
+    shared = W.fill_normal((max(Ks, 1), T, d), 1.0, dtype, seed, 21, 0, "cuda") if Ks else None
+    y = torch.zeros((T, d), dtype=act, device="cuda")
+    b.combine(cfg_of(wl, capacity=C), y_rows, torch.from_numpy(disp["slot_row"]).cuda(),
+              torch.from_numpy(g).cuda(), shared, y)
+    torch.cuda.synchronize()
+    ref = oracle.combine(host(y_rows)[:R], disp["slot_row"], g,
+                         None if shared is None else host(shared))
+    assert rel_l2(host(y), ref) <= TOL[dtype]
+    assert row_rel_l2_max(host(y), ref) <= ROW_TOL[dtype]
+
+
+def random_balances(n, seed):
+    rng = np.random.default_rng(seed)
+    out = []
+    for i in range(n):
+        T = int(rng.choice([1, 5, 64, 65, 500, 4096, 9000]))
+        N = int(rng.choice([1, 2, 3, 8, 64, 100, 256, 1000, 1024]))
+        K = int(rng.integers(1, min(N, 64) + 1))
+        out.append((f"bl{i}", T, N, K, int(rng.integers(0, 1000))))
+    return out
+
+
+BALANCES = random_balances(20, 5)
+
+
+@pytest.mark.parametrize("case", BALANCES, ids=lambda c: c[0])
+def test_random_balance_stats_match_oracle(case):
+    b = B()
+    name, T, N, K, seed = case
+    print(f"[random balance] {case}", flush=True)
+    wl = W.custom_workload(name, T=T, d_model=64, n_routed=N, top_k=K, n_shared=0, d_ff=64,
+                           dtype="bf16", router_bias="gauss", router_bias_var=0.5, seed=seed)
+    cfg = cfg_of(wl)
+    x, wr, rb = wl.x("cuda"), wl.w_router("cuda"), wl.router_bias_values("cuda")
+    logits = torch.empty((T, N), dtype=torch.float32, device="cuda")
+    idx = torch.empty((T, K), dtype=torch.int32, device="cuda")
+    gates = torch.empty((T, K), dtype=torch.float32, device="cuda")
+    b.route(cfg, x, wr, rb, logits, idx, gates)
+    ws = torch.empty(max(b.balance_stats_workspace_size(cfg), 1), dtype=torch.uint8, device="cuda")
+    f = torch.empty(N, dtype=torch.float32, device="cuda")
+    P = torch.empty(N, dtype=torch.float32, device="cuda")
+    loss = torch.empty(1, dtype=torch.float32, device="cuda")
+    b.balance_stats(cfg, logits, idx, 0.01, f, P, loss, ws)
+    torch.cuda.synchronize()
+    rf, rP, rL = oracle.balance_statistics(logits.cpu().numpy(), idx.cpu().numpy(), 0.01)
+    assert np.array_equal(np.rint(f.cpu().numpy().astype(np.float64) * T * K), np.rint(rf * T * K))
+    assert np.allclose(f.cpu().numpy(), rf, rtol=1e-6, atol=0)
+    assert np.abs(P.cpu().numpy() - rP).max() <= 1e-5 * max(rP.max(), 1e-30)
+    assert abs(float(loss.item()) - rL) <= 1e-5 * abs(rL)
