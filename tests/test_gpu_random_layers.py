@@ -1,7 +1,8 @@
 """Seeded random cases of every entry point against the oracle: small layers
 through moe_layer_forward, grouped FFN products through moe_grouped_ffn,
 router and dispatch cases through moe_route and moe_permute, combines through
-moe_combine and balance statistics through moe_balance_stats.
+moe_combine and balance statistics through moe_balance_stats, and large grouped
+products (thousands of rows, many tiles and rounds) on sampled rows.
 
 Shapes, dtypes, capacity factors, router biases (in the logit or for the
 selection only), expert biases and the FP8 dispatch are drawn from a fixed
@@ -338,3 +339,82 @@ def test_random_balance_stats_match_oracle(case):
     assert np.allclose(f.cpu().numpy(), rf, rtol=1e-6, atol=0)
     assert np.abs(P.cpu().numpy() - rP).max() <= 1e-5 * max(rP.max(), 1e-30)
     assert abs(float(loss.item()) - rL) <= 1e-5 * abs(rL)
+
+
+def random_large_ffns(n, seed):
+    rng = np.random.default_rng(seed)
+    kinds = [lambda: 0, lambda: 1, lambda: int(rng.integers(2, 129)),
+             lambda: int(rng.integers(129, 257)), lambda: int(rng.integers(257, 1100)),
+             lambda: int(rng.integers(1100, 5000))]
+    out = []
+    for i in range(n):
+        while True:
+            G = int(rng.integers(1, 33))
+            w = rng.dirichlet(np.ones(len(kinds)))
+            rows = [kinds[int(rng.choice(len(kinds), p=w))]() for _ in range(G)]
+            R = sum(rows)
+            d = 64 * int(rng.integers(1, 8192 // 64 + 1))
+            f = 64 * int(rng.integers(1, 8192 // 64 + 1))
+            if 2000 <= R <= 40000 and d * f <= 8_000_000:
+                break
+        max_rows = R if rng.random() < 0.6 else R * int(rng.choice([2, 4]))
+        out.append((f"big{i}", rows, d, f, bool(rng.random() < 0.5), max_rows,
+                    int(rng.integers(0, 1000))))
+    return out
+
+
+LARGE_FFNS = random_large_ffns(8, 5)
+
+
+def sample_rows(offs, G, R, rng):
+    """Rows of a grouped product to check: each group's first two and last two
+    rows, the rows either side of every 256-row tile boundary inside a group,
+    rows 63, 64, 127 and 128 of its last tile (where half- and quarter-height
+    tails end), and 100 random rows; all inside [0, R)."""
+    samp = set()
+    for g in range(G):
+        r0, r1 = int(offs[g]), int(offs[g + 1])
+        cand = [r0, r0 + 1, r1 - 1, r1 - 2]
+        for m in range(r0 + 256, r1, 256):
+            cand += [m - 1, m, m + 1]
+        last = r0 + ((r1 - r0 - 1) // 256) * 256
+        cand += [last + 63, last + 64, last + 127, last + 128]
+        samp |= {r for r in cand if r0 <= r < r1}
+    samp |= set(int(v) for v in rng.integers(0, R, 100))
+    samp = np.array(sorted(samp))
+    assert samp.min() >= 0 and samp.max() < R
+    return samp
+
+
+@pytest.mark.parametrize("case", LARGE_FFNS, ids=lambda c: c[0])
+def test_random_large_grouped_ffn_on_sampled_rows(case):
+    b = B()
+    name, rows, d, f, eb, max_rows, seed = case
+    print(f"[random large ffn] {name}: R={sum(rows)} groups={len(rows)} d={d} f={f} "
+          f"max_rows={max_rows}", flush=True)
+    G, R = len(rows), int(sum(rows))
+    wl = W.custom_workload(name, T=R, d_model=d, n_routed=G, top_k=1, n_shared=0, d_ff=f,
+                           dtype="bf16", expert_bias=eb, seed=seed)
+    cfg = cfg_of(wl)
+    x_rows = W.fill_normal((R, d), 1.0, "bf16", 3, 1, 0, "cuda")
+    w1, b1, w2, b2 = wl.stacked(False, "cuda")
+    offs = np.concatenate([[0], np.cumsum(rows)]).astype(np.int32)
+    nws = b.grouped_ffn_workspace_size(cfg, G, max_rows)
+    ws = torch.empty(max(nws, 1), dtype=torch.uint8, device="cuda") if nws else None
+    h = torch.zeros((R, f), dtype=torch.bfloat16, device="cuda")
+    y = torch.zeros((R, d), dtype=torch.bfloat16, device="cuda")
+    b.grouped_ffn(cfg, G, x_rows, torch.from_numpy(offs).cuda(), max_rows, w1, b1, w2, b2, h, y,
+                  ws=ws)
+    torch.cuda.synchronize()
+    samp = sample_rows(offs, G, R, np.random.default_rng(seed))
+    sel_d = torch.from_numpy(samp).long().cuda()
+    xs, hg, yg = host(x_rows[sel_d]), host(h[sel_d]), host(y[sel_d])
+    grp = np.searchsorted(offs, samp, side="right") - 1
+    Hs, Ys = np.zeros((len(samp), f)), np.zeros((len(samp), d))
+    for g in np.unique(grp):
+        sel = grp == g
+        e = tuple(None if t is None else t.float().numpy() for t in wl.routed_expert(int(g)))
+        Ys[sel], Hs[sel] = oracle.expert_ffn(xs[sel], *e, return_hidden=True)
+    assert rel_l2(hg, Hs) <= TOL["bf16"] and rel_l2(yg, Ys) <= TOL["bf16"]
+    assert row_rel_l2_max(hg, Hs) <= ROW_TOL["bf16"]
+    assert row_rel_l2_max(yg, Ys) <= ROW_TOL["bf16"]
