@@ -1,8 +1,9 @@
 """Seeded random cases of every entry point against the oracle: small layers
 through moe_layer_forward, grouped FFN products through moe_grouped_ffn,
 router and dispatch cases through moe_route and moe_permute, combines through
-moe_combine and balance statistics through moe_balance_stats, and large grouped
-products (thousands of rows, many tiles and rounds) on sampled rows.
+moe_combine and balance statistics through moe_balance_stats, large grouped
+products (thousands of rows, many tiles and rounds) on sampled rows, and
+mid-size layers (thousands of tokens, widths in the thousands) on every token.
 
 Shapes, dtypes, capacity factors, router biases (in the logit or for the
 selection only), expert biases and the FP8 dispatch are drawn from a fixed
@@ -418,3 +419,53 @@ def test_random_large_grouped_ffn_on_sampled_rows(case):
     assert rel_l2(hg, Hs) <= TOL["bf16"] and rel_l2(yg, Ys) <= TOL["bf16"]
     assert row_rel_l2_max(hg, Hs) <= ROW_TOL["bf16"]
     assert row_rel_l2_max(yg, Ys) <= ROW_TOL["bf16"]
+
+
+def random_mid_layers(n, seed):
+    rng = np.random.default_rng(seed)
+    out = []
+    for i in range(n):
+        while True:
+            T = int(rng.choice([1000, 2048, 3000, 4096, 6000, 8192, 12000]))
+            N = int(rng.choice([4, 8, 16, 32, 64, 128, 256]))
+            K = int(rng.integers(1, min(N, 16) + 1))
+            d = 64 * int(rng.integers(1, 4096 // 64 + 1))
+            f = 64 * int(rng.integers(1, 4096 // 64 + 1))
+            Ks = int(rng.integers(0, 3))
+            if T * N * d <= 2e9 and T * (K + Ks) * d * f <= 2.5e10:   # oracle time
+                break
+        cf = float(rng.choice([0.0, 0.0, 1.0, 1.25, 2.0]))
+        rb = str(rng.choice(["none", "gauss", "zipf"]))
+        fp8 = bool(rng.random() < 0.2)
+        eb = bool(rng.random() < 0.2)
+        out.append(W.custom_workload(f"mid{i}", T=T, d_model=d, n_routed=N, top_k=K, n_shared=Ks,
+                                     d_ff=f, dtype="bf16", capacity_factor=cf, router_bias=rb,
+                                     router_bias_var=0.5, zipf_s=1.1, dispatch_fp8=fp8,
+                                     expert_bias=eb, seed=int(rng.integers(0, 1000))))
+    return out
+
+
+MID_LAYERS = random_mid_layers(10, 9)
+
+
+@pytest.mark.parametrize("wl", MID_LAYERS, ids=lambda w: w.name)
+def test_random_mid_layer_matches_oracle_on_every_token(wl):
+    print(f"[random mid layer] {wl}", flush=True)
+    dl = W.device.DeviceLayer(wl)
+    dl.forward()
+    torch.cuda.synchronize()
+    if wl.dispatch_fp8:
+        check_fp8_layer(dl, wl.name)
+        return
+
+    # one expert at a time, widened on the device and copied over, no cache
+    def expert64(e, shared=False):
+        src = (dl.ws1, dl.bs1, dl.ws2, dl.bs2) if shared else (dl.w1, dl.b1, dl.w2, dl.b2)
+        return tuple(None if t is None else t[e].double().cpu().numpy() for t in src)
+
+    ref = oracle.layer_forward(host(dl.x), host(dl.w_router),
+                               None if dl.router_bias is None else host(dl.router_bias),
+                               lambda e: expert64(e), lambda j: expert64(j, True),
+                               top_k=wl.top_k, n_shared=wl.n_shared,
+                               capacity_factor=wl.capacity_factor)
+    check_layer(dl, ref, wl)
