@@ -347,7 +347,10 @@ int64_t moe_capacity(const moe_config *cfg);
 /* Static text for a moe_status value. */
 const char *moe_status_string(int status);
 
-/* Interface version: 0x00MMmmpp. */
+/* Interface version, 0x00MMmmpp: the library returns MOE_VERSION of the
+ * header it was built with; a caller built against another version should not
+ * use it (struct layouts may differ). */
+#define MOE_VERSION 0x000200
 int moe_version(void);
 
 #ifdef __cplusplus

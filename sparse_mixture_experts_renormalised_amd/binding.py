@@ -30,6 +30,9 @@ EXPORTS = ("moe_route", "moe_permute", "moe_permute_workspace_size", "moe_groupe
            "moe_layer_forward_noalloc", "moe_workspace_size", "moe_workspace_layout",
            "moe_capacity", "moe_status_string", "moe_version")
 STAGES = ("router", "topk", "dispatch", "up", "down", "combine")
+# moe_version() of the interface these ctypes declarations mirror (the structs
+# below must match the header's field for field)
+INTERFACE_VERSION = 0x000200
 
 
 class MoeError(RuntimeError):
@@ -95,6 +98,9 @@ def lib():
         for name, (res, args) in sig.items():
             f = getattr(L, name)
             f.restype, f.argtypes = res, args
+        if L.moe_version() != INTERFACE_VERSION:
+            raise RuntimeError(f"{LIB_PATH} implements interface {L.moe_version():#08x}, this "
+                               f"binding {INTERFACE_VERSION:#08x}: rebuild the library")
         _LIB = L
     return _LIB
 

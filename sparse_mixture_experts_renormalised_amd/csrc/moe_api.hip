@@ -206,7 +206,7 @@ int noalloc_scratch(void **out) {
 
 extern "C" {
 
-int moe_version(void) { return 0x000100; }
+int moe_version(void) { return MOE_VERSION; }
 
 const char *moe_status_string(int status) {
   switch (status) {

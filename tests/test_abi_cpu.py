@@ -35,7 +35,7 @@ def test_every_declared_symbol_is_exported(B):
 
 
 def test_version_and_status_strings(B):
-    assert B.lib().moe_version() == 0x000100
+    assert B.lib().moe_version() == B.INTERFACE_VERSION == 0x000200
     assert B.lib().moe_status_string(0) == b"ok"
     assert B.lib().moe_status_string(-3).startswith(b"workspace")
 
