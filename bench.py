@@ -11,8 +11,8 @@ workload.
 
     python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline] [--only]
 
-The headline value is the Mixtral-shaped layer (the configuration the
-matrix-core target is graded on); ``per_config`` carries the same figures
+The headline value is the Mixtral-shaped layer (the configuration whose
+expert GEMMs have the matrix-core target); ``per_config`` carries the same figures
 for every other workload of the metric, among them the DeepSeek-V3-shaped
 decode layer's HBM rate.
 """
