@@ -552,6 +552,24 @@ def test_layer_forward_is_deterministic():
     assert torch.equal(y1, dl.y)
 
 
+@pytest.mark.parametrize("fp8", [False, True], ids=["bf16", "fp8"])
+@pytest.mark.parametrize("name", ["mixtral_shape", "deepseekmoe_fine", "dsv3_prefill",
+                                  "dsv3_decode"])
+def test_full_size_layer_repeats_bit_exact(name, fp8):
+    # 200 back-to-back passes of a full-size layer (persistent schedules, LDS
+    # rings, K and M splits, tails): every 50th must equal the first bit for bit
+    wl = W.get_workload(name).with_(dispatch_fp8=fp8)
+    print(f"[repeat] {name} fp8={fp8}", flush=True)
+    dl = run_layer(wl)
+    ref = [t.clone() for t in (dl.y, dl.topk_idx, dl.topk_gate, dl.counts)]
+    for r in range(200):
+        dl.forward()
+        if r % 50 == 49:
+            torch.cuda.synchronize()
+            got = (dl.y, dl.topk_idx, dl.topk_gate, dl.counts)
+            assert all(torch.equal(a, b) for a, b in zip(got, ref)), f"pass {r}"
+
+
 def test_layer_zero_capacity_gives_shared_only():
     wl = SMALL_LAYERS[2]
     b = B()
