@@ -48,6 +48,10 @@ def parse():
                    help="precision of the routed experts' token rows (the FP8 dispatch mode)")
     p.add_argument("--only", action="store_true",
                    help="time only --workload (no per-config lines for the other workloads)")
+    p.add_argument("--vs-hipblaslt", action="store_true",
+                   help="also time torch.matmul (hipBLASLt) on the same expert products: one "
+                        "product per touched expert and shared expert, rows and weights of "
+                        "this layer, no gather, SiLU or bias (reported as vendor_gemm)")
     p.add_argument("--calibrate-copy", action="store_true",
                    help="only copy 1 GiB device-to-device three times (counter calibration)")
     p.add_argument("--traffic-from", nargs=4, metavar=("FETCH_CSV", "WRITE_CSV", "COPY_FETCH_CSV",
@@ -258,7 +262,65 @@ def roofline(wl, work, stage_ms):
     return roof
 
 
-def measure(wl, steps: int, warmup: int, keep_layer: bool = False):
+def vendor_gemms(dl, wl, steps: int, warmup: int):
+    """torch.matmul (hipBLASLt for bf16) on this layer's expert products: for
+    each expert with rows, its gathered token rows times W1_e^T, then the
+    hidden rows times W2_e^T; the shared experts on all T tokens.  Operands
+    are laid out contiguously beforehand (weights pre-transposed), so only the
+    products are timed; no gather, SiLU, bias or combine.  Stage times from
+    events over `steps` repetitions."""
+    import torch
+    r = dl.routing_from_workspace()
+    offs, row_token = r["offsets"], r["row_token"]
+    x = dl.x
+    ups, downs = [], []
+    for e in range(wl.n_routed):
+        lo, hi = int(offs[e]), int(offs[e + 1])
+        if hi <= lo:
+            continue
+        a = x[torch.from_numpy(row_token[lo:hi]).long().cuda()].contiguous()
+        w1t = dl.w1[e].t().contiguous()
+        w2t = dl.w2[e].t().contiguous()
+        h = torch.empty((hi - lo, wl.d_ff), dtype=x.dtype, device=x.device)
+        y = torch.empty((hi - lo, wl.d_model), dtype=x.dtype, device=x.device)
+        ups.append((a, w1t, h))
+        downs.append((h, w2t, y))
+    for i in range(wl.n_shared):
+        w1t = dl.ws1[i].t().contiguous()
+        w2t = dl.ws2[i].t().contiguous()
+        h = torch.empty((wl.T, wl.d_ff), dtype=x.dtype, device=x.device)
+        y = torch.empty((wl.T, wl.d_model), dtype=x.dtype, device=x.device)
+        ups.append((x, w1t, h))
+        downs.append((h, w2t, y))
+
+    def stage(prods):
+        for a, w, o in prods:
+            torch.matmul(a, w, out=o)
+
+    out = {"library": "torch.matmul (hipBLASLt), one product per expert with rows and per "
+                      "shared expert; no gather, SiLU, bias or combine"}
+    for name, prods in (("up", ups), ("down", downs)):
+        for _ in range(warmup):
+            stage(prods)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(steps):
+            stage(prods)
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / steps
+        flops = sum(2.0 * a.shape[0] * a.shape[1] * w.shape[1] for a, w, _ in prods)
+        out[f"{name}_ms"] = ms
+        out[f"{name}_tflops"] = flops / (ms * 1e-3) / 1e12
+        out[f"{name}_frac"] = out[f"{name}_tflops"] / PEAK_BF16_TFLOPS
+    del ups, downs
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    return out
+
+
+def measure(wl, steps: int, warmup: int, keep_layer: bool = False, vendor: bool = False):
     """Times one workload: warmup passes, a pass set with stage events, then
     the timed plain layer calls.  Returns the figures and (optionally) the
     device layer."""
@@ -323,6 +385,10 @@ def measure(wl, steps: int, warmup: int, keep_layer: bool = False):
         # algorithmic bytes of the whole layer over its wall time per step
         "layer_hbm_gbs": sum(w["bytes"] for w in work.values()) / (ms_per_step * 1e-3) / 1e9,
     }
+    if vendor and wl.dtype == "bf16":
+        print(f"[bench] {wl.name}: torch.matmul on the same expert products ...",
+              file=sys.stderr, flush=True)
+        res["vendor_gemm"] = vendor_gemms(dl, wl, steps, warmup)
     if keep_layer:
         return res, dl
     del dl
@@ -378,7 +444,8 @@ def main():
     wl = W.get_workload(args.workload)
     if args.dispatch == "fp8":
         wl = wl.with_(dispatch_fp8=True)
-    head, dl = measure(wl, args.steps, args.warmup, keep_layer=not args.no_cpu_baseline)
+    head, dl = measure(wl, args.steps, args.warmup, keep_layer=not args.no_cpu_baseline,
+                       vendor=args.vs_hipblaslt)
     cpu = None
     if dl is not None:
         print("[bench] cpu baseline (oracle) ...", file=sys.stderr, flush=True)
@@ -396,7 +463,7 @@ def main():
                 continue
             w = W.get_workload(name)
             r, _ = measure(w.with_(dispatch_fp8=True) if args.dispatch == "fp8" else w,
-                           args.steps, args.warmup)
+                           args.steps, args.warmup, vendor=args.vs_hipblaslt)
             per_config[name] = r
 
     out = {
@@ -419,6 +486,8 @@ def main():
         "cpu_baseline": cpu,
         "per_config": per_config,
     }
+    if "vendor_gemm" in head:
+        out["vendor_gemm"] = head["vendor_gemm"]
     print(json.dumps(out), flush=True)
 
 
